@@ -1,0 +1,258 @@
+"""ctypes binding of ``libbc.so`` (declared in ``include/bc.h``).
+
+Argument marshalling only: every function here turns torch tensors and host
+lists into the pointers and sizes of the C entry point of the same name and
+returns its status.  All computation happens in the HIP kernels behind those
+entry points; there is no fallback path.  Device tensors are checked for
+device, dtype, contiguity and minimum size before their pointers are handed
+over, because the C ABI cannot see tensor extents.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbc.so")
+
+BC_OK = 0
+BC_ERR_ARG = -1
+BC_ERR_UNSUPPORTED = -2
+BC_ERR_CAPACITY = -3
+BC_ERR_ORDER = -4
+BC_ERR_WORKSPACE = -5
+BC_ERR_HIP = -6
+
+BC_F32 = 0
+BC_BF16 = 1
+BC_MASK_BLOCK_BIDIR = 0
+BC_MASK_BLOCK_CAUSAL = 1
+BC_UNMASK_SEMI = 0
+BC_UNMASK_FULL = 1
+BC_MAX_SEQ = 64
+BC_MAX_BLOCKS = 64
+BC_MAX_BLOCK_ROWS = 1024
+
+EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
+            "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_status_str")
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class BcKvCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("n_seq", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+
+
+class BcActive(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("blk_off", _c_i32p), ("n_blk", ctypes.c_int32), ("n_seq", ctypes.c_int32),
+                ("n_rows", ctypes.c_int32), ("n_q_heads", ctypes.c_int32)]
+
+
+class BcError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s" % (what, bc_status_str(status)))
+
+
+_lib = None
+
+
+def lib():
+    """Load libbc.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libbc.so is not built (%s); run `python -m block_causal_attention_gqa_amd.build`"
+                           % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    cp, ap = ctypes.POINTER(BcKvCache), ctypes.POINTER(BcActive)
+    L.bc_status_str.argtypes = [ctypes.c_int]
+    L.bc_status_str.restype = ctypes.c_char_p
+    L.bc_kv_commit.argtypes = [cp, _c_i32p, i32, i32, i32, vp, vp, vp]
+    L.bc_kv_commit.restype = ctypes.c_int
+    L.bc_attn_workspace_bytes.argtypes = [cp, cp, ap, i32]
+    L.bc_attn_workspace_bytes.restype = sz
+    L.bc_attn_step.argtypes = [cp, _c_i32p, cp, _c_i32p, ap, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+    L.bc_attn_step.restype = ctypes.c_int
+    L.bc_unmask_workspace_bytes.argtypes = [i32, i32]
+    L.bc_unmask_workspace_bytes.restype = sz
+    L.bc_unmask_select.argtypes = [vp, i32, i32, _c_i32p, i32, _c_i32p, _c_i32p, ctypes.c_float,
+                                   vp, vp, vp, vp, vp, sz, vp]
+    L.bc_unmask_select.restype = ctypes.c_int
+    L.bc_verify_workspace_bytes.argtypes = [i32, i32, i32]
+    L.bc_verify_workspace_bytes.restype = sz
+    L.bc_spec_verify.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.bc_spec_verify.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def bc_status_str(status):
+    return lib().bc_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------- marshalling
+_DT = {torch.float32: BC_F32, torch.bfloat16: BC_BF16}
+
+
+def _dev(t, name, dtype=None, numel=None, allow_none=False):
+    """Device pointer of a contiguous CUDA tensor, after checks."""
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs %d" % (name, t.numel(), numel))
+    return t.data_ptr()
+
+
+def _host_i32(x):
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_c_i32p)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class KVCache:
+    """K and V tensors [n_seq][n_kv_heads][capacity][head_dim] of one dtype."""
+
+    def __init__(self, k, v):
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v must be [S][Hkv][cap][D] of one dtype")
+        if k.dtype not in _DT:
+            raise ValueError("cache dtype must be float32 or bfloat16")
+        self.k, self.v = k, v
+        self.n_seq, self.n_kv_heads, self.capacity, self.head_dim = (int(x) for x in k.shape)
+        self.dtype = _DT[k.dtype]
+
+    def struct(self):
+        return BcKvCache(_dev(self.k, "cache.k"), _dev(self.v, "cache.v"), self.dtype, self.n_seq,
+                         self.n_kv_heads, self.head_dim, self.capacity)
+
+    def shape_struct(self):
+        """Struct for workspace queries (no device pointers needed)."""
+        return BcKvCache(1, 1, self.dtype, self.n_seq, self.n_kv_heads, self.head_dim, self.capacity)
+
+
+def _active(q, k, v, blk_off, tdtype, Hkv, D, pointers=True):
+    S, R, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D:
+        raise ValueError("q head_dim %d != cache head_dim %d" % (Dq, D))
+    off_arr, off_p = _host_i32(blk_off)
+    if pointers:
+        qp = _dev(q, "q", tdtype, S * R * Hq * D)
+        kp = _dev(k, "k", tdtype, S * Hkv * R * D)
+        vp = _dev(v, "v", tdtype, S * Hkv * R * D)
+    else:
+        qp = kp = vp = 1
+    act = BcActive(qp, kp, vp, off_p, len(off_arr) - 1, S, R, Hq)
+    return act, off_arr
+
+
+def bc_attn_workspace_bytes(prefix, priv, q_shape, blk_off, n_prefix_splits=0):
+    """Workspace bytes for an attention call with these shapes (q_shape =
+    (S, R, Hq, D)) and the caches' capacities."""
+    S, R, Hq, D = q_shape
+    off_arr, off_p = _host_i32(blk_off)
+    act = BcActive(1, 1, 1, off_p, len(off_arr) - 1, S, R, Hq)
+    ps = prefix.shape_struct()
+    vs = priv.shape_struct() if priv is not None else None
+    return int(lib().bc_attn_workspace_bytes(ctypes.byref(ps), ctypes.byref(vs) if vs else None,
+                                             ctypes.byref(act), int(n_prefix_splits)))
+
+
+def bc_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                 n_prefix_splits=0, stream=None, check=True):
+    tdtype = prefix.k.dtype
+    act, off_arr = _active(q, k, v, blk_off, tdtype, prefix.n_kv_heads, prefix.head_dim)
+    pl_arr, pl_p = _host_i32(prefix_len)
+    if len(pl_arr) != prefix.n_seq:
+        raise ValueError("prefix_len needs one entry per prefix sequence")
+    ps = prefix.struct()
+    if priv is not None:
+        vs = priv.struct()
+        vl_arr, vl_p = _host_i32(priv_len)
+        if len(vl_arr) != act.n_seq:
+            raise ValueError("priv_len needs one entry per rollout")
+    else:
+        vs, vl_arr, vl_p = None, None, None
+    _dev(out, "out", tdtype, q.numel())
+    st = lib().bc_attn_step(ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p,
+                            ctypes.byref(act), int(mask), float(scale), int(n_prefix_splits),
+                            out.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_attn_step")
+    return st
+
+
+def bc_kv_commit(cache, length, seq, start, n_rows, blk_k, blk_v, stream=None, check=True):
+    """``length`` is a host int32 NumPy array [n_seq], updated in place."""
+    if not (isinstance(length, np.ndarray) and length.dtype == np.int32 and length.flags.c_contiguous):
+        raise ValueError("length must be a contiguous int32 NumPy array")
+    n = cache.n_kv_heads * int(n_rows) * cache.head_dim
+    kp = _dev(blk_k, "blk_k", cache.k.dtype, n)
+    vp = _dev(blk_v, "blk_v", cache.k.dtype, n)
+    cs = cache.struct()
+    st = lib().bc_kv_commit(ctypes.byref(cs), length.ctypes.data_as(_c_i32p), int(seq), int(start),
+                            int(n_rows), kp, vp, _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_kv_commit")
+    return st
+
+
+def bc_unmask_workspace_bytes(n_rows, vocab):
+    return int(lib().bc_unmask_workspace_bytes(int(n_rows), int(vocab)))
+
+
+def bc_unmask_select(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+                     stream=None, check=True):
+    R, V = (int(x) for x in logits.shape)
+    off_arr, off_p = _host_i32(blk_off)
+    n_blk = len(off_arr) - 1
+    mode_arr, mode_p = _host_i32(mode)
+    div_arr, div_p = _host_i32(n_div)
+    if len(mode_arr) != n_blk or len(div_arr) != n_blk:
+        raise ValueError("mode and n_div need one entry per block")
+    st = lib().bc_unmask_select(
+        _dev(logits, "logits", torch.float32, R * V), R, V, off_p, n_blk, mode_p, div_p,
+        float(threshold), _dev(masked, "masked", torch.uint8, R), _dev(tokens, "tokens", torch.int32, R),
+        _dev(conf, "conf", torch.float32, R, allow_none=True), _dev(n_commit, "n_commit", torch.int32, n_blk),
+        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_unmask_select")
+    return st
+
+
+def bc_verify_workspace_bytes(n_seq, n_lrows, vocab):
+    return int(lib().bc_verify_workspace_bytes(int(n_seq), int(n_lrows), int(vocab)))
+
+
+def bc_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=None, check=True):
+    S, L, V = (int(x) for x in logits.shape)
+    m = int(draft.shape[1])
+    st = lib().bc_spec_verify(
+        _dev(logits, "logits", torch.float32, S * L * V), S, L, V, _dev(draft, "draft", torch.int32, S * m), m,
+        _dev(fixed, "fixed", torch.uint8, S * m, allow_none=True), _dev(first, "first", torch.int32, S),
+        _dev(accept_len, "accept_len", torch.int32, S), _dev(bonus, "bonus", torch.int32, S),
+        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_spec_verify")
+    return st

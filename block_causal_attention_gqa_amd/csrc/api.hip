@@ -1,0 +1,301 @@
+// Host side of the C ABI declared in include/bc.h: argument validation,
+// workspace sizing, the split plan of the attention, and kernel launches.
+// Nothing here allocates device memory or keeps state between calls.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "bc_internal.h"
+
+namespace {
+
+using namespace bc;
+
+bool dtype_ok(int d) { return d == BC_F32 || d == BC_BF16; }
+int elem_bytes(int d) { return d == BC_BF16 ? 2 : 4; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_cache(const bc_kv_cache* c) {
+  if (!c || !c->k || !c->v) return BC_ERR_ARG;
+  if (!dtype_ok(c->dtype)) return BC_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return BC_ERR_UNSUPPORTED;
+  if (c->n_seq < 1 || c->n_kv_heads < 1 || c->capacity < 1) return BC_ERR_ARG;
+  return BC_OK;
+}
+
+int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_block) {
+  if (!off) return BC_ERR_ARG;
+  if (n_blk < 1) return BC_ERR_ARG;
+  if (n_blk > BC_MAX_BLOCKS) return BC_ERR_UNSUPPORTED;
+  if (off[0] != 0 || off[n_blk] != n_rows) return BC_ERR_ARG;
+  for (int b = 0; b < n_blk; ++b) {
+    if (off[b + 1] <= off[b]) return BC_ERR_ARG;
+    if (off[b + 1] - off[b] > max_rows_per_block) return BC_ERR_UNSUPPORTED;
+  }
+  return BC_OK;
+}
+
+// ------------------------------------------------------------ attention plan
+struct Plan {
+  int P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  size_t o_bytes, ml_bytes, total_bytes;
+};
+
+int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_active* a,
+                  int32_t n_splits) {
+  int st = check_cache(prefix);
+  if (st) return st;
+  if (!a || !a->q || !a->k || !a->v) return BC_ERR_ARG;
+  if (a->n_seq < 1 || a->n_rows < 1 || a->n_q_heads < 1) return BC_ERR_ARG;
+  if (a->n_seq > BC_MAX_SEQ) return BC_ERR_UNSUPPORTED;
+  if (a->n_q_heads % prefix->n_kv_heads) return BC_ERR_ARG;
+  if ((st = check_blk_off(a->blk_off, a->n_blk, a->n_rows, 1 << 30))) return st;
+  if (n_splits < 0 || n_splits > 256) return BC_ERR_ARG;
+  if (priv) {
+    if ((st = check_cache(priv))) return st;
+    if (prefix->n_seq != 1 || priv->n_seq != a->n_seq) return BC_ERR_ARG;
+    if (priv->dtype != prefix->dtype) return BC_ERR_UNSUPPORTED;
+    if (priv->n_kv_heads != prefix->n_kv_heads || priv->head_dim != prefix->head_dim) return BC_ERR_ARG;
+  } else if (prefix->n_seq != a->n_seq) {
+    return BC_ERR_ARG;
+  }
+  // all offsets of the kernels are 64-bit; keep the row/item counts in int range
+  const long long rows = (long long)a->n_seq * a->n_rows * a->n_q_heads;
+  if (rows > (1LL << 26)) return BC_ERR_UNSUPPORTED;
+  return BC_OK;
+}
+
+// lengths[s] are the prefix lengths the plan is made for (the capacities when
+// sizing the workspace: the plan is monotone in the lengths, so that bound
+// covers every call with the same shapes).
+void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_active* a,
+               const int* lengths, int32_t n_splits, Plan* p, int* chunk) {
+  const int S = a->n_seq, R = a->n_rows, Hq = a->n_q_heads, Hkv = prefix->n_kv_heads;
+  const int group = Hq / Hkv, D = prefix->head_dim;
+  const bool fork = priv != nullptr;
+  const int groups = fork ? Hkv : S * Hkv;
+  const int rows_group = fork ? S * R * group : R * group;
+  p->n_mt_prefix = (rows_group + kAttnTileRows - 1) / kAttnTileRows;
+  p->n_mt_active = (R * group + kAttnTileRows - 1) / kAttnTileRows;
+  int maxlen = 0;
+  for (int s = 0; s < prefix->n_seq; ++s) maxlen = std::max(maxlen, lengths[s]);
+  int P = n_splits;
+  if (P == 0) {
+    // enough workgroups to cover the 256 CUs about twice, but no chunk
+    // shorter than 128 keys (partial traffic grows with the chunk count)
+    const int base = groups * p->n_mt_prefix;
+    const int want = (512 + base - 1) / base;
+    const int most = std::max(1, (maxlen + 127) / 128);
+    P = std::max(1, std::min(want, most));
+  }
+  p->P = P;
+  for (int s = 0; s < prefix->n_seq; ++s) {
+    const int per = (lengths[s] + P - 1) / P;
+    chunk[s] = std::max(kAttnKeyTile, (per + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile);
+  }
+  p->n_slots = P + 1;
+  p->n_prefix_items = groups * P * p->n_mt_prefix;
+  p->n_items = p->n_prefix_items + S * Hkv * p->n_mt_active;
+  p->rows_total = S * R * Hq;
+  p->o_bytes = align256((size_t)p->n_slots * p->rows_total * D * sizeof(float));
+  p->ml_bytes = align256((size_t)p->n_slots * p->rows_total * 2 * sizeof(float));
+  p->total_bytes = p->o_bytes + p->ml_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bc_status_str(int status) {
+  switch (status) {
+    case BC_OK: return "BC_OK";
+    case BC_ERR_ARG: return "BC_ERR_ARG: malformed argument";
+    case BC_ERR_UNSUPPORTED: return "BC_ERR_UNSUPPORTED: outside what the kernels handle";
+    case BC_ERR_CAPACITY: return "BC_ERR_CAPACITY: commit past the cache capacity";
+    case BC_ERR_ORDER: return "BC_ERR_ORDER: commit does not start at the current length";
+    case BC_ERR_WORKSPACE: return "BC_ERR_WORKSPACE: workspace missing or too small";
+    case BC_ERR_HIP: return "BC_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown bc_status";
+  }
+}
+
+int bc_kv_commit(const bc_kv_cache* cache, int32_t* len, int32_t seq, int32_t start, int32_t n_rows,
+                 const void* blk_k, const void* blk_v, void* stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!len || !blk_k || !blk_v) return BC_ERR_ARG;
+  if (seq < 0 || seq >= cache->n_seq || n_rows < 1) return BC_ERR_ARG;
+  if (start != len[seq]) return BC_ERR_ORDER;
+  if ((long long)start + n_rows > cache->capacity) return BC_ERR_CAPACITY;
+  const int D = cache->head_dim, Hkv = cache->n_kv_heads, eb = elem_bytes(cache->dtype);
+  const long long head_stride = (long long)cache->capacity * D;
+  const long long seq_stride = head_stride * Hkv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  char* kdst = static_cast<char*>(cache->k) + seq * seq_stride * eb;
+  char* vdst = static_cast<char*>(cache->v) + seq * seq_stride * eb;
+  if (launch_commit(kdst, blk_k, cache->dtype, Hkv, D, seq_stride, head_stride, start, n_rows, s) != hipSuccess ||
+      launch_commit(vdst, blk_v, cache->dtype, Hkv, D, seq_stride, head_stride, start, n_rows, s) != hipSuccess)
+    return BC_ERR_HIP;
+  len[seq] = start + n_rows;
+  return BC_OK;
+}
+
+size_t bc_attn_workspace_bytes(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_active* a,
+                               int32_t n_prefix_splits) {
+  if (validate_attn(prefix, priv, a, n_prefix_splits) != BC_OK) return 0;
+  int caps[BC_MAX_SEQ];
+  for (int s = 0; s < prefix->n_seq; ++s) caps[s] = prefix->capacity;
+  Plan p;
+  int chunk[BC_MAX_SEQ];
+  make_plan(prefix, priv, a, caps, n_prefix_splits, &p, chunk);
+  return p.total_bytes;
+}
+
+int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale,
+                 int32_t n_prefix_splits, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_attn(prefix, priv, a, n_prefix_splits);
+  if (st) return st;
+  if (!prefix_len || !out || (priv && !priv_len)) return BC_ERR_ARG;
+  if (mask != BC_MASK_BLOCK_BIDIR && mask != BC_MASK_BLOCK_CAUSAL) return BC_ERR_ARG;
+  if (!std::isfinite(scale)) return BC_ERR_ARG;
+  for (int s = 0; s < prefix->n_seq; ++s)
+    if (prefix_len[s] < 0 || prefix_len[s] > prefix->capacity) return BC_ERR_ARG;
+  if (priv)
+    for (int s = 0; s < a->n_seq; ++s)
+      if (priv_len[s] < 0 || priv_len[s] > priv->capacity) return BC_ERR_ARG;
+
+  AttnArgs args;
+  std::memset(&args, 0, sizeof(args));
+  Plan p;
+  make_plan(prefix, priv, a, prefix_len, n_prefix_splits, &p, args.chunk);
+  if (!ws) return BC_ERR_WORKSPACE;
+  {
+    // the caller sized the workspace for the capacities; check against that bound
+    int caps[BC_MAX_SEQ];
+    for (int s = 0; s < prefix->n_seq; ++s) caps[s] = prefix->capacity;
+    Plan pmax;
+    int chunk_max[BC_MAX_SEQ];
+    make_plan(prefix, priv, a, caps, n_prefix_splits, &pmax, chunk_max);
+    if (ws_bytes < pmax.total_bytes || ws_bytes < p.total_bytes) return BC_ERR_WORKSPACE;
+  }
+  const int D = prefix->head_dim;
+  args.q = a->q;
+  args.out = out;
+  args.pk = prefix->k;
+  args.pv = prefix->v;
+  args.p_head_stride = (long long)prefix->capacity * D;
+  args.p_seq_stride = args.p_head_stride * prefix->n_kv_heads;
+  if (priv) {
+    args.vk = priv->k;
+    args.vv = priv->v;
+    args.v_head_stride = (long long)priv->capacity * D;
+    args.v_seq_stride = args.v_head_stride * priv->n_kv_heads;
+  }
+  args.ak = a->k;
+  args.av = a->v;
+  args.ws_o = static_cast<float*>(ws);
+  args.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.o_bytes);
+  args.scale_log2 = scale * 1.4426950408889634f;
+  args.S = a->n_seq;
+  args.R = a->n_rows;
+  args.Hq = a->n_q_heads;
+  args.Hkv = prefix->n_kv_heads;
+  args.group = a->n_q_heads / prefix->n_kv_heads;
+  args.D = D;
+  args.fork = priv ? 1 : 0;
+  args.causal = mask == BC_MASK_BLOCK_CAUSAL;
+  args.n_splits = p.P;
+  args.n_slots = p.n_slots;
+  args.n_mt_prefix = p.n_mt_prefix;
+  args.n_mt_active = p.n_mt_active;
+  args.n_prefix_items = p.n_prefix_items;
+  args.n_items = p.n_items;
+  args.rows_total = p.rows_total;
+  args.n_blk = a->n_blk;
+  for (int b = 0; b <= a->n_blk; ++b) args.blk_off[b] = a->blk_off[b];
+  for (int s = 0; s < prefix->n_seq; ++s) args.prefix_len[s] = prefix_len[s];
+  if (priv)
+    for (int s = 0; s < a->n_seq; ++s) args.priv_len[s] = priv_len[s];
+  (void)hipGetLastError();
+  if (launch_attn(args, prefix->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
+size_t bc_unmask_workspace_bytes(int32_t n_rows, int32_t vocab) {
+  if (n_rows < 1 || vocab < 1) return 0;
+  return align256((size_t)n_rows * scan_chunks(vocab) * sizeof(ScanPartial));
+}
+
+int bc_unmask_select(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off,
+                     int32_t n_blk, const int32_t* mode, const int32_t* n_div, float threshold,
+                     uint8_t* masked, int32_t* tokens, float* conf, int32_t* n_commit, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!logits || !mode || !n_div || !masked || !tokens || !n_commit) return BC_ERR_ARG;
+  if (n_rows < 1 || vocab < 1) return BC_ERR_ARG;
+  if (n_rows > 65535) return BC_ERR_UNSUPPORTED;
+  int st = check_blk_off(blk_off, n_blk, n_rows, BC_MAX_BLOCK_ROWS);
+  if (st) return st;
+  for (int b = 0; b < n_blk; ++b) {
+    if (mode[b] != BC_UNMASK_SEMI && mode[b] != BC_UNMASK_FULL) return BC_ERR_ARG;
+    if (n_div[b] < 1) return BC_ERR_ARG;
+  }
+  if (!std::isfinite(threshold)) return BC_ERR_ARG;
+  if (!ws || ws_bytes < bc_unmask_workspace_bytes(n_rows, vocab)) return BC_ERR_WORKSPACE;
+  UnmaskArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.logits = logits;
+  args.n_rows = n_rows;
+  args.vocab = vocab;
+  args.n_chunks = scan_chunks(vocab);
+  args.n_blk = n_blk;
+  args.masked = masked;
+  args.tokens = tokens;
+  args.conf = conf;
+  args.n_commit = n_commit;
+  args.part = static_cast<ScanPartial*>(ws);
+  args.threshold = threshold;
+  for (int b = 0; b <= n_blk; ++b) args.blk_off[b] = blk_off[b];
+  for (int b = 0; b < n_blk; ++b) {
+    args.mode[b] = mode[b];
+    args.n_div[b] = n_div[b];
+  }
+  (void)hipGetLastError();
+  if (launch_unmask(args, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
+size_t bc_verify_workspace_bytes(int32_t n_seq, int32_t n_lrows, int32_t vocab) {
+  if (n_seq < 1 || n_lrows < 1 || vocab < 1) return 0;
+  return align256((size_t)n_seq * n_lrows * scan_chunks(vocab) * sizeof(ScanPartial));
+}
+
+int bc_spec_verify(const float* logits, int32_t n_seq, int32_t n_lrows, int32_t vocab, const int32_t* draft,
+                   int32_t m, const uint8_t* fixed, const int32_t* first, int32_t* accept_len,
+                   int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !draft || !first || !accept_len || !bonus) return BC_ERR_ARG;
+  if (n_seq < 1 || n_lrows < 1 || vocab < 1 || m < 1 || m > n_lrows) return BC_ERR_ARG;
+  if ((long long)n_seq * n_lrows > 65535) return BC_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < bc_verify_workspace_bytes(n_seq, n_lrows, vocab)) return BC_ERR_WORKSPACE;
+  VerifyArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.logits = logits;
+  args.n_seq = n_seq;
+  args.n_lrows = n_lrows;
+  args.vocab = vocab;
+  args.n_chunks = scan_chunks(vocab);
+  args.m = m;
+  args.draft = draft;
+  args.fixed = fixed;
+  args.first = first;
+  args.accept_len = accept_len;
+  args.bonus = bonus;
+  args.part = static_cast<ScanPartial*>(ws);
+  (void)hipGetLastError();
+  if (launch_verify(args, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
+}  // extern "C"

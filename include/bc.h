@@ -1,0 +1,222 @@
+/*
+ * bc.h -- C ABI of the block-causal masked-diffusion denoising step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One denoising step of a block-diffusion decoder (the mechanism shared by
+ * Fast-dDrive, WAM-Diff2 and Fast-dVLA) is:
+ *
+ *   bc_attn_step      block-causal GQA attention of the active block(s) over
+ *                     the committed KV prefix plus the blocks' own K/V
+ *   (model layers and LM head: outside this library)
+ *   bc_unmask_select  per-row max / argmax / softmax confidence over the
+ *                     vocabulary, then threshold + ceil(remaining / n) reveal
+ *   bc_kv_commit      append a completed block's K/V to the cache
+ *   bc_spec_verify    scaffold speculative verification (accept length and
+ *                     bonus token) for the AR verify pass
+ *
+ * Conventions common to every entry point
+ *   - Every tensor argument is a caller-owned DEVICE pointer unless the
+ *     comment says HOST.  All device tensors are dense, row-major (C order)
+ *     with the layout given in brackets, and at least 16-byte aligned.
+ *   - The library allocates no memory and keeps no state between calls.
+ *     Scratch space is a caller-provided workspace whose minimum size is
+ *     returned by the matching *_workspace_bytes query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is only enqueued; results are valid once the stream has been
+ *     synchronised.  HOST arrays are read before the call returns and are
+ *     not retained.
+ *   - Arguments are validated on the host first.  On any failure a negative
+ *     bc_status is returned and nothing has been enqueued; BC_ERR_HIP means a
+ *     kernel launch was rejected by the runtime.
+ *   - Floating-point inputs must be finite.
+ *   - Calls on one stream that share a workspace run in stream order and may
+ *     reuse it; concurrent calls on different streams need their own.
+ */
+#ifndef BC_H
+#define BC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BC_MAX_SEQ 64      /* sequences (or rollouts) per bc_attn_step call */
+#define BC_MAX_BLOCKS 64   /* active blocks per call */
+#define BC_MAX_BLOCK_ROWS 1024 /* rows of one block in bc_unmask_select */
+
+typedef enum {
+  BC_OK = 0,
+  BC_ERR_ARG = -1,          /* malformed argument (null pointer, bad shape, ...) */
+  BC_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels handle */
+  BC_ERR_CAPACITY = -3,     /* a commit would grow a sequence past its capacity */
+  BC_ERR_ORDER = -4,        /* a commit that does not start at the current length */
+  BC_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the query says */
+  BC_ERR_HIP = -6           /* the HIP runtime rejected a launch */
+} bc_status;
+
+typedef enum { BC_F32 = 0, BC_BF16 = 1 } bc_dtype;
+
+/* Visibility among the active rows.  Across blocks both modes are causal
+ * (a block sees earlier blocks and never later ones); inside a block BIDIR is
+ * bidirectional (the MDM draft / denoise pass) and CAUSAL is causal (the AR
+ * verify pass).  Every committed (prefix / private) key is visible to every
+ * active row of its sequence. */
+typedef enum { BC_MASK_BLOCK_BIDIR = 0, BC_MASK_BLOCK_CAUSAL = 1 } bc_mask;
+
+/* Reveal rule of one block (Fast-dVLA notes, key design 4, pipelined
+ * parallel decoding): SEMI reveals only rows whose confidence exceeds the
+ * threshold; FULL also reveals at least ceil(|masked| / n) rows. */
+typedef enum { BC_UNMASK_SEMI = 0, BC_UNMASK_FULL = 1 } bc_unmask_mode;
+
+/* A KV cache: k and v are each [n_seq][n_kv_heads][capacity][head_dim] of
+ * `dtype`.  The number of valid rows per sequence is kept by the caller (a
+ * HOST int32 array) and advanced only by bc_kv_commit. */
+typedef struct {
+  void *k, *v;
+  int32_t dtype;        /* bc_dtype */
+  int32_t n_seq;
+  int32_t n_kv_heads;
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t capacity;     /* rows allocated per (sequence, kv head) */
+} bc_kv_cache;
+
+/* The active rows of one step: every sequence has the same n_rows rows cut
+ * into the same n_blk blocks.
+ *   q    [n_seq][n_rows][n_q_heads][head_dim]
+ *   k, v [n_seq][n_kv_heads][n_rows][head_dim]  (recomputed every step)
+ *   blk_off  HOST [n_blk + 1], blk_off[0] = 0 < blk_off[1] < ... <
+ *            blk_off[n_blk] = n_rows; row j is in block b when
+ *            blk_off[b] <= j < blk_off[b + 1].
+ * q, k and v have the dtype of the cache they are attended with. */
+typedef struct {
+  const void *q, *k, *v;
+  const int32_t *blk_off;
+  int32_t n_blk;
+  int32_t n_seq;
+  int32_t n_rows;
+  int32_t n_q_heads;    /* a multiple of the caches' n_kv_heads */
+} bc_active;
+
+/* ------------------------------------------------------------------------ */
+/* KV commit.
+ * Fast-dVLA notes, key design 1, and Fast-dDrive method summary sec. 3.1:
+ * a completed block's K/V never change again and are cached; only a prefix
+ * whose predecessors are all complete may be cached, so commits are
+ * append-only and in order.
+ *
+ * Copies blk_k / blk_v [n_kv_heads][n_rows][head_dim] (device, cache dtype)
+ * into rows [start, start + n_rows) of sequence `seq` and sets
+ * len[seq] = start + n_rows.  `len` is HOST [cache->n_seq], in/out.
+ * Errors: BC_ERR_ORDER if start != len[seq]; BC_ERR_CAPACITY if
+ * start + n_rows > capacity; BC_ERR_ARG for a bad seq, n_rows < 1 or null
+ * pointers.  The copy is bit-exact. */
+int bc_kv_commit(const bc_kv_cache *cache, int32_t *len, int32_t seq, int32_t start,
+                 int32_t n_rows, const void *blk_k, const void *blk_v, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Block-causal GQA attention of the active rows.
+ * WAM-Diff2 article sec. 2.1 and Fast-dVLA notes, key design 1: blocks are
+ * bidirectional inside and causal across, so a block sees the prefix,
+ * earlier blocks and itself; Fast-dDrive method summary sec. 3.2 step 3: the
+ * AR verify pass is causal over the block; sec. 3.3 and the Fast-dDrive
+ * abstract: N rollouts fork from one shared prefix KV cache.
+ *
+ * For query head h of row i (kv head h / (n_q_heads / n_kv_heads)):
+ *   out[s][i][h] = sum_j softmax_j(scale * q.k_j) v_j
+ * over the visible keys j of sequence s: every prefix row < prefix_len,
+ * every private row < priv_len[s] (fork), and active rows by `mask`.
+ *
+ *   prefix      committed cache.  Without a fork, prefix->n_seq == a->n_seq.
+ *               With a fork (priv != NULL), prefix->n_seq == 1 and all
+ *               a->n_seq rollouts read it.
+ *   prefix_len  HOST [prefix->n_seq], 0 <= len <= capacity.
+ *   priv        NULL, or each rollout's private cache (n_seq == a->n_seq).
+ *   priv_len    HOST [a->n_seq] when priv != NULL.
+ *   mask        bc_mask.
+ *   scale       softmax scale, normally 1 / sqrt(head_dim).
+ *   n_prefix_splits  0 = automatic; otherwise the number of key chunks the
+ *               prefix is cut into (1 .. 256), for tuning and tests.
+ *   out         [n_seq][n_rows][n_q_heads][head_dim] in the q dtype.
+ *   ws          workspace of at least bc_attn_workspace_bytes(...) bytes
+ *               for the same shapes, capacities and n_prefix_splits.
+ * Errors: BC_ERR_ARG (shapes / pointers / blk_off / lengths);
+ * BC_ERR_UNSUPPORTED (head_dim not 64 or 128, n_seq > BC_MAX_SEQ,
+ * n_blk > BC_MAX_BLOCKS, mixed dtypes); BC_ERR_WORKSPACE. */
+size_t bc_attn_workspace_bytes(const bc_kv_cache *prefix, const bc_kv_cache *priv,
+                               const bc_active *a, int32_t n_prefix_splits);
+int bc_attn_step(const bc_kv_cache *prefix, const int32_t *prefix_len,
+                 const bc_kv_cache *priv, const int32_t *priv_len,
+                 const bc_active *a, int32_t mask, float scale, int32_t n_prefix_splits,
+                 void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Confidence unmask.
+ * Fast-dVLA notes, key design 4: a semi-active block reveals only positions
+ * whose prediction confidence exceeds the threshold; a fully-active block
+ * also ranks the remaining positions by confidence and reveals at least a
+ * 1/n fraction of them.  Revealed tokens never change (key design 2).
+ *
+ * For every row r with masked[r] != 0:
+ *   conf_r = 1 / sum_v exp(l_rv - max_v l_rv)   (max softmax probability)
+ *   tok_r  = argmax_v l_rv (lowest index on ties)
+ * Then per block b with masked set E and A = {r in E : conf_r > threshold}:
+ *   k = |A|                                     (mode[b] == SEMI)
+ *   k = min(|E|, max(|A|, ceil(|E| / n_div[b]))) (mode[b] == FULL)
+ * and the first k rows of E in (conf descending, row ascending) order get
+ * tokens[r] = tok_r, masked[r] = 0.  n_commit[b] = k.
+ * Decisions are exact with respect to float64 confidences: rows whose float32
+ * confidence lies too close to the threshold or to the ranking cut for the
+ * float32 error bound are recomputed in float64 before deciding.
+ *
+ *   logits  [n_rows][vocab] float32
+ *   blk_off HOST [n_blk + 1] as in bc_active; each block <= BC_MAX_BLOCK_ROWS
+ *   mode    HOST [n_blk] bc_unmask_mode;  n_div HOST [n_blk], >= 1
+ *   masked  [n_rows] uint8, in/out (1 = still masked)
+ *   tokens  [n_rows] int32, in/out (rows revealed now are written)
+ *   conf    [n_rows] float32 or NULL: confidence of every row masked on
+ *           entry (other rows are left untouched)
+ *   n_commit [n_blk] int32
+ *   ws      at least bc_unmask_workspace_bytes(n_rows, vocab) bytes */
+size_t bc_unmask_workspace_bytes(int32_t n_rows, int32_t vocab);
+int bc_unmask_select(const float *logits, int32_t n_rows, int32_t vocab,
+                     const int32_t *blk_off, int32_t n_blk,
+                     const int32_t *mode, const int32_t *n_div, float threshold,
+                     uint8_t *masked, int32_t *tokens, float *conf, int32_t *n_commit,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Scaffold speculative verify.
+ * Fast-dDrive method summary sec. 3.2, Scaffold Speculative decoding:
+ * scaffold positions are accepted without a check; the AR pass gives
+ * p_AR(. | x_<i) for every position; walking left to right a draft equal to
+ * the AR argmax is accepted, and at the first mismatch the AR prediction is
+ * taken as a bonus token and later drafts are dropped.
+ *
+ * Per sequence s, with t_i = argmax logits[s][i] (lowest index on ties):
+ *   k = the first i in [first[s], m) with fixed[s][i] == 0 and
+ *       t_i != draft[s][i], or m if there is none;
+ *   accept_len[s] = k - first[s];  bonus[s] = t_k if k < n_lrows else -1.
+ *
+ *   logits   [n_seq][n_lrows][vocab] float32, row i already aligned with
+ *            draft position i (row i = p_AR(. | x_<i))
+ *   draft    [n_seq][m] int32, 1 <= m <= n_lrows
+ *   fixed    [n_seq][m] uint8 or NULL (scaffold rows, auto-accepted)
+ *   first    [n_seq] int32 device, each in [0, m] (clamped to it)
+ *   accept_len, bonus  [n_seq] int32
+ *   ws       at least bc_verify_workspace_bytes(n_seq, n_lrows, vocab) */
+size_t bc_verify_workspace_bytes(int32_t n_seq, int32_t n_lrows, int32_t vocab);
+int bc_spec_verify(const float *logits, int32_t n_seq, int32_t n_lrows, int32_t vocab,
+                   const int32_t *draft, int32_t m, const uint8_t *fixed,
+                   const int32_t *first, int32_t *accept_len, int32_t *bonus,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a bc_status value (never NULL). */
+const char *bc_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BC_H */

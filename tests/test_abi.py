@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every entry point include/bc.h declares,
+and rejects malformed arguments on the host before any launch.
+
+Every call here fails host-side validation by construction, so no kernel is
+launched and no pointer is dereferenced: the tests run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_causal_attention_gqa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "bc.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(bc_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch
+    if torch.cuda.is_available():
+        # host-only checks; on a GPU machine the parity tests cover the library
+        pytest.skip("host-side ABI checks run where no GPU is present")
+    return B.lib()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for st in range(-6, 1):
+        assert B.bc_status_str(st).startswith("BC_")
+    assert B.bc_status_str(-99) == "unknown bc_status"
+
+
+def _cache(dtype=B.BC_BF16, S=1, Hkv=2, D=128, cap=64, k=1, v=1):
+    return B.BcKvCache(k, v, dtype, S, Hkv, D, cap)
+
+
+def _active(S=1, R=8, Hq=16, off=(0, 8)):
+    arr = (ctypes.c_int32 * len(off))(*off)
+    return B.BcActive(1, 1, 1, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), len(off) - 1, S, R, Hq), arr
+
+
+def _lens(*xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def attn(L, cache, lens, act, mask=0, splits=0, ws=1, ws_bytes=1 << 40, priv=None, priv_len=None, out=1):
+    return L.bc_attn_step(ctypes.byref(cache), lens, ctypes.byref(priv) if priv else None, priv_len,
+                          ctypes.byref(act), mask, 0.1, splits, out, ws, ws_bytes, None)
+
+
+def test_attention_validation(L):
+    act, keep = _active()
+    assert attn(L, _cache(D=96), _lens(8), act) == B.BC_ERR_UNSUPPORTED
+    assert attn(L, _cache(dtype=7), _lens(8), act) == B.BC_ERR_UNSUPPORTED
+    assert attn(L, _cache(k=0), _lens(8), act) == B.BC_ERR_ARG
+    assert attn(L, _cache(Hkv=3), _lens(8), act) == B.BC_ERR_ARG          # 16 % 3
+    assert attn(L, _cache(), _lens(65), act) == B.BC_ERR_ARG              # > capacity
+    assert attn(L, _cache(), _lens(-1), act) == B.BC_ERR_ARG
+    assert attn(L, _cache(), _lens(8), act, mask=2) == B.BC_ERR_ARG
+    assert attn(L, _cache(), _lens(8), act, splits=257) == B.BC_ERR_ARG
+    assert attn(L, _cache(), _lens(8), act, ws=0) == B.BC_ERR_WORKSPACE
+    assert attn(L, _cache(), _lens(8), act, ws_bytes=16) == B.BC_ERR_WORKSPACE
+    assert attn(L, _cache(), _lens(8), act, out=0) == B.BC_ERR_ARG
+    assert attn(L, _cache(S=2), _lens(8, 8), act) == B.BC_ERR_ARG        # n_seq mismatch
+    bad, k1 = _active(off=(0, 4, 4, 8))
+    assert attn(L, _cache(), _lens(8), bad) == B.BC_ERR_ARG
+    bad, k2 = _active(off=(1, 8))
+    assert attn(L, _cache(), _lens(8), bad) == B.BC_ERR_ARG
+    bad, k3 = _active(off=(0, 7))
+    assert attn(L, _cache(), _lens(8), bad) == B.BC_ERR_ARG
+    many, k4 = _active(S=B.BC_MAX_SEQ + 1)
+    assert attn(L, _cache(S=B.BC_MAX_SEQ + 1), _lens(*([8] * (B.BC_MAX_SEQ + 1))), many) == B.BC_ERR_UNSUPPORTED
+    blocks, k5 = _active(R=70, off=tuple(range(71)))
+    assert attn(L, _cache(), _lens(8), blocks) == B.BC_ERR_UNSUPPORTED  # > BC_MAX_BLOCKS
+    # fork: shared prefix must hold one sequence, priv one per rollout
+    f_act, k6 = _active(S=2)
+    assert attn(L, _cache(S=2), _lens(8, 8), f_act, priv=_cache(S=2), priv_len=_lens(0, 0)) == B.BC_ERR_ARG
+    assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=3), priv_len=_lens(0, 0)) == B.BC_ERR_ARG
+    assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=2), priv_len=None) == B.BC_ERR_ARG
+    assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=2), priv_len=_lens(0, 65)) == B.BC_ERR_ARG
+    assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=2, dtype=B.BC_F32),
+                priv_len=_lens(0, 0)) == B.BC_ERR_UNSUPPORTED
+
+
+def test_workspace_queries(L):
+    act, keep = _active()
+    c = _cache(cap=3352)
+    n0 = L.bc_attn_workspace_bytes(ctypes.byref(c), None, ctypes.byref(act), 0)
+    n1 = L.bc_attn_workspace_bytes(ctypes.byref(c), None, ctypes.byref(act), 1)
+    assert n0 > n1 > 0 and n0 % 256 == 0
+    assert L.bc_attn_workspace_bytes(ctypes.byref(_cache(D=96)), None, ctypes.byref(act), 0) == 0
+    assert L.bc_unmask_workspace_bytes(32, 151936) >= 32 * 19 * 16
+    assert L.bc_unmask_workspace_bytes(0, 10) == 0
+    assert L.bc_verify_workspace_bytes(64, 24, 151936) >= 64 * 24 * 19 * 16
+
+
+def test_commit_validation(L):
+    c = _cache(cap=64)
+    ln = _lens(60)
+    assert L.bc_kv_commit(ctypes.byref(c), ln, 0, 59, 4, 1, 1, None) == B.BC_ERR_ORDER
+    assert L.bc_kv_commit(ctypes.byref(c), ln, 0, 60, 5, 1, 1, None) == B.BC_ERR_CAPACITY
+    assert L.bc_kv_commit(ctypes.byref(c), ln, 1, 60, 1, 1, 1, None) == B.BC_ERR_ARG
+    assert L.bc_kv_commit(ctypes.byref(c), ln, 0, 60, 0, 1, 1, None) == B.BC_ERR_ARG
+    assert L.bc_kv_commit(ctypes.byref(c), ln, 0, 60, 1, 0, 1, None) == B.BC_ERR_ARG
+    assert L.bc_kv_commit(ctypes.byref(_cache(D=80)), ln, 0, 60, 1, 1, 1, None) == B.BC_ERR_UNSUPPORTED
+    assert ln[0] == 60
+
+
+def test_unmask_validation(L):
+    off, mode, div = _lens(0, 4), _lens(1), _lens(2)
+
+    def call(logits=1, R=4, V=10, off=off, nb=1, mode=mode, div=div, tau=0.9, masked=1, ws=1, wsb=1 << 30):
+        return L.bc_unmask_select(logits, R, V, off, nb, mode, div, tau, masked, 1, None, 1, ws, wsb, None)
+    assert call(logits=0) == B.BC_ERR_ARG
+    assert call(V=0) == B.BC_ERR_ARG
+    assert call(off=_lens(0, 3)) == B.BC_ERR_ARG
+    assert call(mode=_lens(5)) == B.BC_ERR_ARG
+    assert call(div=_lens(0)) == B.BC_ERR_ARG
+    assert call(tau=float("nan")) == B.BC_ERR_ARG
+    assert call(masked=0) == B.BC_ERR_ARG
+    assert call(ws=0) == B.BC_ERR_WORKSPACE
+    assert call(wsb=15) == B.BC_ERR_WORKSPACE
+    assert call(R=2000, off=_lens(0, 2000)) == B.BC_ERR_UNSUPPORTED   # block > 1024 rows
+    assert call(R=70000, off=_lens(0, 70000)) == B.BC_ERR_UNSUPPORTED
+
+
+def test_verify_validation(L):
+    def call(logits=1, S=1, Lr=4, V=10, draft=1, m=4, first=1, acc=1, bonus=1, ws=1, wsb=1 << 30):
+        return L.bc_spec_verify(logits, S, Lr, V, draft, m, None, first, acc, bonus, ws, wsb, None)
+    assert call(m=5) == B.BC_ERR_ARG
+    assert call(m=0) == B.BC_ERR_ARG
+    assert call(draft=0) == B.BC_ERR_ARG
+    assert call(first=0) == B.BC_ERR_ARG
+    assert call(V=0) == B.BC_ERR_ARG
+    assert call(ws=0) == B.BC_ERR_WORKSPACE
+    assert call(wsb=100) == B.BC_ERR_WORKSPACE
+    assert call(S=5000, Lr=24, m=24) == B.BC_ERR_UNSUPPORTED

@@ -1,0 +1,162 @@
+"""GPU parity of bc_attn_step against the float64 oracle.
+
+Tolerances: max-abs 1e-5 for float32 inputs, 1e-2 for bf16 inputs (float32
+accumulation, bf16 probabilities into the PV product, bf16 output)."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA
+from tests import gpu_util as G
+from block_causal_attention_gqa_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+BIDIR, CAUSAL = B.BC_MASK_BLOCK_BIDIR, B.BC_MASK_BLOCK_CAUSAL
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.require_lib()
+
+
+def _check(seed, S, R, Hq, Hkv, D, dtype, prefix_len, blk_off, mode, **kw):
+    print("attn case seed=%d S=%d R=%d Hq=%d Hkv=%d D=%d %s prefix=%s blk=%s mode=%d %s"
+          % (seed, S, R, Hq, Hkv, D, dtype, list(prefix_len)[:4], list(blk_off)[:6], mode, kw), flush=True)
+    got, h = G.attn_case(seed, S, R, Hq, Hkv, D, dtype, prefix_len, blk_off, mode, **kw)
+    fork = kw.get("fork", False)
+    want = OA.attention_step(h["q"], h["pk"], h["pv"], prefix_len, h["k"], h["v"], blk_off, mode,
+                             scale=h["scale"], priv_k=h["vk"] if fork else None,
+                             priv_v=h["vv"] if fork else None,
+                             priv_len=kw.get("priv_len") if fork else None)
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], "max-abs %.3g > %.3g" % (err, TOL[dtype])
+    return got
+
+
+def test_tiny_fp32_single_step():
+    # 1 sequence, 4 query heads / 1 KV head, head_dim 64, fp32, prefix 256 + one block of 8
+    _check(0, 1, 8, 4, 1, 64, "f32", [256], [0, 8], BIDIR)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 7, 40])
+def test_tiny_fp32_split_counts(splits):
+    _check(1, 1, 8, 4, 1, 64, "f32", [256], [0, 8], BIDIR, n_splits=splits)
+
+
+@pytest.mark.parametrize("bs", [32, 12, 6])
+def test_section_decode_shape(bs):
+    # Fast-dDrive section decode: bs1, 16q/2kv, D 128, bf16, prefix 3072 + a block
+    _check(2, 1, bs, 16, 2, 128, "bf16", [3072], [0, bs], BIDIR, cap=3352)
+
+
+def test_section_decode_grown_prefix():
+    _check(3, 1, 32, 16, 2, 128, "bf16", [3072 + 236], [0, 32], BIDIR, cap=3352)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_ragged_multiblock(D, group, mode):
+    Hkv = 2
+    _check(10 + group, 1, 23, Hkv * group, Hkv, D, "bf16", [333], [0, 5, 17, 23], mode, cap=400)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+def test_forced_splits_with_empty_chunks(splits):
+    _check(20, 1, 17, 8, 2, 128, "bf16", [97], [0, 9, 17], CAUSAL, cap=200, n_splits=splits)
+
+
+def test_empty_prefix():
+    _check(21, 1, 9, 4, 2, 128, "bf16", [0], [0, 4, 9], BIDIR, cap=64)
+
+
+def test_fp32_multiblock_causal():
+    _check(22, 2, 13, 6, 3, 128, "f32", [70, 141], [0, 7, 13], CAUSAL, cap=160)
+
+
+def test_large_block_batch_independent_prefixes():
+    # WAM-Diff2 shape: 32q/8kv, D 128, bf16, prefix 2048, block of 32, batch 4
+    _check(30, 4, 32, 32, 8, 128, "bf16", [2048, 2080, 2112, 2304], [0, 32], BIDIR, cap=2304)
+
+
+def test_pipelined_three_active_blocks():
+    # Fast-dVLA: 3 active 7-token blocks over a 512-token prefix
+    _check(40, 1, 21, 16, 2, 128, "bf16", [512], [0, 7, 14, 21], BIDIR)
+
+
+def test_pipelined_625_window():
+    # 625-token output in blocks of 32, window of 3 active blocks (96 rows)
+    _check(41, 1, 96, 16, 2, 128, "bf16", [512 + 32 * 9], [0, 32, 64, 96], BIDIR, cap=1137)
+    _check(42, 1, 81, 16, 2, 128, "bf16", [512 + 32 * 17], [0, 32, 64, 81], BIDIR, cap=1137)
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("N", [1, 4])
+def test_fork_shared_prefix(mode, N):
+    # shared prefix 3072 + 210, 16q/2kv, trajectory block of 24 rows, private
+    # blocks of earlier trajectory blocks per rollout
+    priv = [0, 24, 47, 23][:N]
+    _check(50 + N, N, 24, 16, 2, 128, "bf16", [3282], [0, 24], mode, fork=True,
+           priv_len=priv, priv_cap=48)
+
+
+def test_fork_sixteen_rollouts_ragged_rows():
+    priv = [(7 * s) % 48 for s in range(16)]
+    _check(60, 16, 23, 16, 2, 128, "bf16", [3282], [0, 23], CAUSAL, fork=True, priv_len=priv, priv_cap=48)
+
+
+def test_block_size_one_equals_causal():
+    # WAM-Diff2 sec. 2.1: B = 1 is causal decoding -- bitwise equal on the GPU
+    a, _ = G.attn_case(70, 1, 16, 8, 2, 128, "bf16", [300], list(range(17)), BIDIR)
+    b, _ = G.attn_case(70, 1, 16, 8, 2, 128, "bf16", [300], [0, 16], CAUSAL)
+    assert np.array_equal(a, b)
+
+
+def test_completed_block_rows_do_not_move():
+    # rows of earlier blocks are bit-identical when a later block's inputs
+    # change (Fast-dVLA notes, key design 1)
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    seed, R, Hq, Hkv, D = 71, 20, 8, 2, 128
+    (pk_t, pv_t), _ = synth.kv_cache(seed, 1, Hkv, 256, D, [256], "bf16")
+    (q_t, _), (k_t, _), (v_t, _) = synth.active_qkv(seed, 1, R, Hq, Hkv, D, "bf16", 0)
+    prefix = B.KVCache(pk_t.to(G.DEV), pv_t.to(G.DEV))
+    blk = [0, 8, 20]
+    nb = B.bc_attn_workspace_bytes(prefix, None, (1, R, Hq, D), blk)
+    ws = torch.empty(nb, dtype=torch.uint8, device=G.DEV)
+    outs = []
+    for variant in range(2):
+        q, k, v = q_t.clone(), k_t.clone(), v_t.clone()
+        if variant:
+            q[0, 8:] = -q[0, 8:]
+            k[0, :, 8:] = k[0, :, 8:] * 2
+            v[0, :, 8:] = v[0, :, 8:] + 1
+        out = torch.empty((1, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+        B.bc_attn_step(prefix, [256], None, None, q.to(G.DEV), k.to(G.DEV), v.to(G.DEV), blk, BIDIR,
+                       D ** -0.5, out, ws)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0][0, :8], outs[1][0, :8])
+    assert not torch.equal(outs[0][0, 8:], outs[1][0, 8:])
+
+
+def test_workspace_and_argument_errors_before_launch():
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    (pk_t, pv_t), _ = synth.kv_cache(1, 1, 2, 128, 128, [100], "bf16")
+    (q_t, _), (k_t, _), (v_t, _) = synth.active_qkv(1, 1, 8, 16, 2, 128, "bf16", 0)
+    prefix = B.KVCache(pk_t.to(G.DEV), pv_t.to(G.DEV))
+    out = torch.empty((1, 8, 16, 128), dtype=torch.bfloat16, device=G.DEV)
+    nb = B.bc_attn_workspace_bytes(prefix, None, (1, 8, 16, 128), [0, 8])
+    small = torch.empty(nb - 256, dtype=torch.uint8, device=G.DEV)
+    q, k, v = q_t.to(G.DEV), k_t.to(G.DEV), v_t.to(G.DEV)
+    st = B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, small, check=False)
+    assert st == B.BC_ERR_WORKSPACE
+    ws = torch.empty(nb, dtype=torch.uint8, device=G.DEV)
+    assert B.bc_attn_step(prefix, [129], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, ws,
+                          check=False) == B.BC_ERR_ARG
+    assert B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 5, 5, 8], BIDIR, 0.1, out, ws,
+                          check=False) == B.BC_ERR_ARG
+    assert B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], 7, 0.1, out, ws,
+                          check=False) == B.BC_ERR_ARG

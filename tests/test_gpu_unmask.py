@@ -1,0 +1,162 @@
+"""GPU parity of bc_unmask_select against the float64 oracle: the revealed
+set, tokens and per-block counts must match bit for bit; the float32
+confidence output is compared with a relative tolerance."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import unmask as OU
+from tests import gpu_util as G
+from block_causal_attention_gqa_amd import binding as B
+from block_causal_attention_gqa_amd import synth
+
+pytestmark = pytest.mark.gpu
+SEMI, FULL = B.BC_UNMASK_SEMI, B.BC_UNMASK_FULL
+NEG = np.float32(-1e30)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.require_lib()
+
+
+def run_gpu(logits, blk_off, mode, n_div, tau, masked, tokens):
+    R, V = logits.shape
+    lg = G.to_dev(logits)
+    m = G.to_dev(masked.astype(np.uint8))
+    t = G.to_dev(tokens.astype(np.int32))
+    conf = torch.full((R,), float("nan"), dtype=torch.float32, device=G.DEV)
+    nc = torch.zeros(len(blk_off) - 1, dtype=torch.int32, device=G.DEV)
+    ws = torch.empty(B.bc_unmask_workspace_bytes(R, V), dtype=torch.uint8, device=G.DEV)
+    B.bc_unmask_select(lg, blk_off, mode, n_div, tau, m, t, conf, nc, ws)
+    torch.cuda.synchronize()
+    return m.cpu().numpy(), t.cpu().numpy(), nc.cpu().numpy(), conf.cpu().numpy()
+
+
+def compare(logits, blk_off, mode, n_div, tau, masked, tokens):
+    print("unmask case R=%d V=%d blk=%s mode=%s n_div=%s" % (logits.shape[0], logits.shape[1],
+          list(blk_off)[:5], list(mode)[:4], list(n_div)[:4]), flush=True)
+    gm, gt, gn, gc = run_gpu(logits, blk_off, mode, n_div, tau, masked, tokens)
+    om, ot, on, oc = OU.unmask_select(logits, blk_off, mode, n_div, np.float32(tau), masked, tokens)
+    assert np.array_equal(gm, om), "revealed set differs"
+    assert np.array_equal(gt, ot), "tokens differ"
+    assert np.array_equal(gn, on), "commit counts differ"
+    sel = masked.astype(bool)
+    np.testing.assert_allclose(gc[sel], oc[sel], rtol=2e-5, atol=0)
+    return gm, gt
+
+
+def test_tiny_config():
+    # [8 x 1024] ~ N(0, 3^2), threshold 0.9, at least one reveal per step
+    x = synth.logits(0, 8, 1024, 3.0, 0)
+    compare(x, [0, 8], [FULL], [1 << 30], 0.9, np.ones(8, np.uint8), np.full(8, -1, np.int32))
+
+
+def test_tiny_config_runs_until_complete():
+    masked = np.ones(8, np.uint8)
+    tokens = np.full(8, -1, np.int32)
+    for step in range(8):
+        x = synth.logits(0, 8, 1024, 3.0, step)
+        synth.plant_peaks(x, 0, 0.2, 9.0, step)
+        masked, tokens = compare(x, [0, 8], [FULL], [1 << 30], 0.9, masked, tokens)
+        if masked.sum() == 0:
+            break
+    assert masked.sum() == 0
+
+
+@pytest.mark.parametrize("bs", [32, 12, 6])
+def test_section_block_schedule(bs):
+    # full vocabulary 151936, sigma 4, 8 steps with n = steps left
+    masked = np.ones(bs, np.uint8)
+    tokens = np.full(bs, -1, np.int32)
+    for step in range(8):
+        x = synth.logits(3, bs, 151936, 4.0, bs, step)
+        synth.plant_peaks(x, 3, 0.1, 12.0, bs, step)
+        masked, tokens = compare(x, [0, bs], [FULL], [8 - step], 0.9, masked, tokens)
+    assert masked.sum() == 0
+
+
+def test_pipelined_semi_and_full_blocks():
+    rng = np.random.default_rng(4)
+    x = synth.logits(4, 21, 2048, 4.0, 0)
+    synth.plant_peaks(x, 4, 0.3, 10.0, 0)
+    masked = np.ones(21, np.uint8)
+    # completion ratios -> committed rows, seeded
+    for b in range(3):
+        r = rng.random()
+        done = rng.choice(7, size=int(r * 7), replace=False)
+        masked[7 * b + done] = 0
+    compare(x, [0, 7, 14, 21], [FULL, SEMI, SEMI], [1 << 30, 1, 1], 0.9, masked, np.full(21, -1, np.int32))
+
+
+def _two_value(a, V):
+    row = np.full(V, NEG, np.float32)
+    row[0] = np.float32(a)
+    row[1] = 0.0
+    return row
+
+
+def test_threshold_band_rows_are_decided_in_float64():
+    # confidences within 1e-9 of the threshold: inside the float32 error band,
+    # so the kernel must recompute them in float64 to agree with the oracle
+    V = 4096
+    t = float(np.float32(0.9))
+    rows = []
+    for c in [t + 1e-9, t - 1e-9, t + 3e-9, t - 3e-9, t + 2e-8, t - 2e-8, 0.3, 0.95]:
+        a = math.log(c / (1 - c))
+        rows.append(_two_value(a, V))
+    x = np.stack(rows)
+    for mode in (SEMI, FULL):
+        compare(x, [0, 8], [mode], [4], 0.9, np.ones(8, np.uint8), np.zeros(8, np.int32))
+
+
+def test_rank_cut_near_ties_and_exact_ties():
+    V = 4096
+    gaps = [0.5, 0.5 + 1e-7, 0.5 - 1e-7, 0.5, 0.1, 0.7, 0.5 + 2e-7, 0.3]
+    x = np.stack([_two_value(a, V) for a in gaps])
+    x[3] = x[0]                       # exact duplicate rows: lower index wins
+    for n in (1, 2, 3, 4, 8):
+        compare(x, [0, 8], [FULL], [n], 0.9, np.ones(8, np.uint8), np.zeros(8, np.int32))
+
+
+def test_argmax_ties_and_uniform_rows():
+    V = 1000
+    x = np.zeros((4, V), np.float32)
+    x[1, [5, 900]] = 3.0
+    x[2, [999, 998]] = 1.0
+    x[3] = synth.logits(5, 1, V, 1.0, 0)[0]
+    compare(x, [0, 4], [FULL], [1], 0.9, np.ones(4, np.uint8), np.zeros(4, np.int32))
+
+
+@pytest.mark.parametrize("V", [1, 3, 1023, 8193, 70001])
+def test_odd_vocab_sizes(V):
+    x = synth.logits(6, 5, V, 4.0, V)
+    compare(x, [0, 2, 5], [FULL, FULL], [2, 1], 0.9, np.ones(5, np.uint8), np.zeros(5, np.int32))
+
+
+def test_many_blocks_batch():
+    # 16 sequences' blocks of 32 in one call (large-block decode at batch 16)
+    R, V = 16 * 32, 151936
+    x = synth.logits(7, R, V, 4.0, 0)
+    synth.plant_peaks(x, 7, 0.05, 12.0, 0)
+    masked = (np.random.default_rng(7).random(R) < 0.7).astype(np.uint8)
+    compare(x, list(range(0, R + 1, 32)), [FULL] * 16, [3] * 16, 0.9, masked, np.zeros(R, np.int32))
+
+
+def test_nothing_masked_and_errors():
+    x = synth.logits(8, 4, 64, 4.0, 0)
+    gm, gt, gn, _ = run_gpu(x, [0, 4], [FULL], [1], 0.9, np.zeros(4, np.uint8), np.arange(4, dtype=np.int32))
+    assert gm.sum() == 0 and list(gt) == [0, 1, 2, 3] and gn[0] == 0
+    lg = G.to_dev(x)
+    m = G.to_dev(np.ones(4, np.uint8))
+    t = G.to_dev(np.zeros(4, np.int32))
+    nc = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    ws = torch.empty(B.bc_unmask_workspace_bytes(4, 64), dtype=torch.uint8, device=G.DEV)
+    assert B.bc_unmask_select(lg, [0, 4], [FULL], [0], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
+    assert B.bc_unmask_select(lg, [0, 3], [FULL], [1], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
+    assert B.bc_unmask_select(lg, [0, 4], [2], [1], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
+    assert B.bc_unmask_select(lg, [0, 4], [FULL], [1], 0.9, m, t, None, nc, ws[:8], check=False) \
+        == B.BC_ERR_WORKSPACE

@@ -1,0 +1,91 @@
+"""GPU parity of bc_spec_verify against the oracle: accept lengths and bonus
+tokens bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import verify as OV
+from tests import gpu_util as G
+from block_causal_attention_gqa_amd import binding as B
+from block_causal_attention_gqa_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.require_lib()
+
+
+def run(logits, draft, fixed, first):
+    S, L, V = logits.shape
+    acc = torch.zeros(S, dtype=torch.int32, device=G.DEV)
+    bon = torch.zeros(S, dtype=torch.int32, device=G.DEV)
+    ws = torch.empty(B.bc_verify_workspace_bytes(S, L, V), dtype=torch.uint8, device=G.DEV)
+    B.bc_spec_verify(G.to_dev(logits), G.to_dev(draft.astype(np.int32)),
+                     None if fixed is None else G.to_dev(fixed.astype(np.uint8)),
+                     G.to_dev(np.asarray(first, np.int32)), acc, bon, ws)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), bon.cpu().numpy()
+
+
+def compare(logits, draft, fixed, first):
+    print("verify case S=%d L=%d V=%d m=%d" % (logits.shape + (draft.shape[1],)), flush=True)
+    ga, gb = run(logits, draft, fixed, first)
+    oa, ob = OV.spec_verify(logits, draft, fixed, first)
+    assert np.array_equal(ga, oa) and np.array_equal(gb, ob)
+    return ga, gb
+
+
+@pytest.mark.parametrize("p_agree", [0.5, 0.8, 1.0])
+@pytest.mark.parametrize("N", [1, 4])
+def test_trajectory_block_agreement(p_agree, N):
+    # [24 x 151936] per rollout; drafts agree with the AR argmax at rate p
+    L, V = 24, 151936
+    lg = np.empty((N, L, V), np.float32)
+    draft = np.empty((N, L), np.int32)
+    for s in range(N):
+        lg[s], t = synth.argmax_planted_logits(9, L, V, 4.0, 0.5, s)
+        draft[s] = synth.drafts_with_agreement(9, t, p_agree, V, s, int(p_agree * 10))
+    fixed = (np.random.default_rng(N).random((N, L)) < 0.15).astype(np.uint8)
+    first = np.random.default_rng(N + 1).integers(0, 5, N)
+    compare(lg, draft, None, np.zeros(N, np.int32))
+    compare(lg, draft, fixed, first)
+
+
+def test_partial_block_and_bonus_row():
+    # block of 23 drafts verified against 24 logit rows: full agreement gives
+    # the bonus from row 23; m == n_lrows gives none
+    V = 5000
+    lg, t = synth.argmax_planted_logits(10, 24, V, 4.0, 1.0, 0)
+    compare(lg[None], t[None, :23].copy(), None, [0])
+    compare(lg[None], t[None].copy(), None, [0])
+    compare(lg[None], t[None].copy(), None, [24])
+    compare(lg[None], t[None, :23].copy(), None, [23])
+
+
+def test_ties_take_lowest_index():
+    lg = np.zeros((1, 3, 300), np.float32)
+    lg[0, 0, [7, 200]] = 1.0
+    lg[0, 1, [250, 13]] = 2.0
+    lg[0, 2, :] = -1.0
+    compare(lg, np.array([[7, 13, 0]], np.int32), None, [0])
+    compare(lg, np.array([[200, 13, 0]], np.int32), None, [0])
+
+
+@pytest.mark.parametrize("V", [1, 7, 8191, 8193])
+def test_odd_vocab(V):
+    rng = np.random.default_rng(V)
+    lg = rng.standard_normal((3, 6, V)).astype(np.float32)
+    draft = rng.integers(0, V, (3, 5)).astype(np.int32)
+    compare(lg, draft, None, [0, 2, 5])
+
+
+def test_argument_errors():
+    lg = G.to_dev(np.zeros((1, 4, 10), np.float32))
+    d = G.to_dev(np.zeros((1, 5), np.int32))
+    f = G.to_dev(np.zeros(1, np.int32))
+    a = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    ws = torch.empty(4096, dtype=torch.uint8, device=G.DEV)
+    assert B.bc_spec_verify(lg, d, None, f, a, a.clone(), ws, check=False) == B.BC_ERR_ARG  # m > n_lrows
