@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the block-causal denoising step on one MI355X.
+
+Workload: the Fast-dDrive-shaped section decode at batch 1 -- 16 query / 2
+KV heads, head_dim 128, bf16 K/V, a 3072-token committed prefix, editable
+sections of 12 / 192 / 6 / 70 tokens cut into blocks of 32 (11 blocks, 280
+tokens), 8 denoise steps per block, each step = block-causal attention over
+the cache + confidence unmask over fp32 logits [b x 151936] ~ N(0, 4^2) with
+threshold 0.9 and n = steps left; the block's K/V are committed when it
+completes.  All inputs are seeded synthetic tensors resident in HBM before
+timing starts.
+
+One bench step = one whole section decode (88 denoise steps, 11 commits),
+replayed as a captured HIP graph.  value = decoded tokens / s.
+
+Prints ONE JSON line.  Options: --steps K --warmup W (timed decodes /
+untimed decodes), --mode graph|eager, --no-cpu-baseline.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "denoise-step ms + decoded tok/s at bs1 B=32; attn HBM TB/s vs roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle decode until this much CPU time is spent")
+    return ap.parse_args()
+
+
+def attn_bytes_flops(prefix_len, R, Hq, Hkv, D, elem=2):
+    """Algorithmic bytes / flops of one BIDIR single-block attention call."""
+    L = prefix_len + R
+    kv = 2 * Hkv * L * D * elem
+    qo = 2 * R * Hq * D * elem
+    flops = 4 * D * Hq * R * L
+    return kv + qo, flops
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md, "
+              "'How the path would shard').", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    from block_causal_attention_gqa_amd import decode, synth
+
+    B.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    preset = synth.PRESETS["section"]
+    t0 = time.time()
+    dec = decode.SectionDecode(preset, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.Stream()
+    graph = None
+    with torch.cuda.stream(stream):
+        dec.run()            # eager once before capture (library + torch warm)
+    torch.cuda.synchronize()
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            dec.run()
+        torch.cuda.synchronize()
+
+    def one():
+        # graph replays and eager calls both go to `stream`, where the events are
+        with torch.cuda.stream(stream):
+            if graph is not None:
+                graph.replay()
+            else:
+                dec.run()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+
+    # sanity: the decode finished every block
+    assert int(dec.masked.sum().item()) == 0, "decode left masked rows"
+    assert int((dec.tokens < 0).sum().item()) == 0
+
+    # ---- per-kernel device time: the same decode issued through the
+    # sub-step entry points, each bracketed by HIP events on its stream
+    kinds = ("attn_partial", "attn_combine", "vocab_scan", "unmask_decide", "commit")
+    events = {k: [] for k in kinds}
+    masked_counts = []
+
+    def timed(kind, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        events[kind].append((e0, e1))
+
+    def traced_run():
+        length = dec.len0.copy()
+        off = 0
+        for b, bs in enumerate(dec.blocks):
+            masked = dec.masked[off: off + bs]
+            tokens = dec.tokens[off: off + bs]
+            masked.fill_(1)
+            for st in range(dec.steps):
+                q, k, v = dec.qkv[b][st]
+                args = (dec.cache, length, None, None, q, k, v, [0, bs], B.BC_MASK_BLOCK_BIDIR, dec.scale,
+                        dec.out[bs], dec.ws_attn)
+                timed("attn_partial", lambda: B.bc_attn_partial(*args, stream=stream))
+                timed("attn_combine", lambda: B.bc_attn_combine(*args, stream=stream))
+                masked_counts.append(masked.sum())
+                lg = dec.logits[b][st]
+                timed("vocab_scan", lambda: B.bc_vocab_scan(lg, masked, True, dec.ws_unmask, stream=stream))
+                timed("unmask_decide", lambda: B.bc_unmask_decide(
+                    lg, [0, bs], [B.BC_UNMASK_FULL], [dec.steps - st], dec.tau, masked, tokens, dec.conf[:bs],
+                    dec.n_commit[:1], dec.ws_unmask, stream=stream))
+            q, k, v = dec.qkv[b][dec.steps - 1]
+            timed("commit", lambda: B.bc_kv_commit(dec.cache, length, 0, int(length[0]), bs, k[0], v[0],
+                                                   stream=stream))
+            off += bs
+
+    # Queue ~0.1 s of unrelated GPU work first, so that every traced call is
+    # already enqueued when the GPU reaches it: the event pairs then bracket
+    # device time only, not the host's launch overhead.
+    gate_a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gate_b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gate_c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(120):
+            torch.matmul(gate_a, gate_b, out=gate_c)
+        gate_end = torch.cuda.Event(enable_timing=True)
+        gate_end.record(stream)
+        traced_run()
+        trace_end = torch.cuda.Event(enable_timing=True)
+        trace_end.record(stream)
+    torch.cuda.synchronize()
+    dur = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in events.items()}   # microseconds
+    first_pre = events["attn_partial"][0][0]
+    gate_slack_us = gate_end.elapsed_time(first_pre) * 1e3
+    trace_span_us = first_pre.elapsed_time(trace_end) * 1e3
+    del gate_a, gate_b, gate_c
+    masked_rows = [int(x.item()) for x in masked_counts]
+    assert int(dec.masked.sum().item()) == 0, "traced decode left masked rows"
+
+    # algorithmic work
+    Hq, Hkv, D, V = dec.Hq, dec.Hkv, dec.D, dec.V
+    attn_bytes, attn_flops, partial_bytes = 0, 0, 0
+    length = dec.prefix
+    for bs in dec.blocks:
+        for _ in range(dec.steps):
+            b_, f_ = attn_bytes_flops(length, bs, Hq, Hkv, D)
+            attn_bytes += b_
+            attn_flops += f_
+            partial_bytes += b_ - bs * Hq * D * 2       # K/V and Q; the output is the combine's
+        length += bs
+    avg = {k: float(np.mean(v)) for k, v in dur.items()}
+    n_attn = len(dur["attn_partial"])
+    attn_us = avg["attn_partial"] + avg["attn_combine"]
+    attn_gbs = attn_bytes / n_attn / (attn_us * 1e-6) / 1e9
+    attn_tflops = attn_flops / n_attn / (attn_us * 1e-6) / 1e12
+    scan_bytes = sum(4 * V * r for r in masked_rows)
+    n_scan = len(dur["vocab_scan"])
+    scan_gbs = scan_bytes / n_scan / (avg["vocab_scan"] * 1e-6) / 1e9
+    unmask_us = avg["vocab_scan"] + avg["unmask_decide"]
+    tot = {k: float(np.sum(v)) for k, v in dur.items()}
+    dominant = max(("attn_partial", "vocab_scan"), key=tot.get)
+    if dominant == "vocab_scan":
+        roof = {"kernel": "scan_kernel (bc_vocab_scan: per-row max/argmax/exp-sum over the vocabulary)",
+                "bound": "hbm", "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": scan_bytes / n_scan, "avg_launch_us": round(avg["vocab_scan"], 3)}
+    else:
+        pgbs = partial_bytes / n_attn / (avg["attn_partial"] * 1e-6) / 1e9
+        roof = {"kernel": "attn_partial_kernel (bc_attn_partial: block-causal GQA attention, split-KV)",
+                "bound": "hbm", "achieved": round(pgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": partial_bytes / n_attn, "avg_launch_us": round(avg["attn_partial"], 3)}
+    kernel_us = {k: round(v, 3) for k, v in avg.items()}
+
+    tokens = dec.tokens_per_decode
+    value = tokens * args.steps / (ms_total * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, N(0,4^2) fp32 logits; no model weights)",
+        "config": {"workload": "section_decode bs1 B=32: 16q/2kv heads, head_dim 128, prefix 3072, "
+                               "blocks 12/32x6/6/32/32/6, 8 denoise steps/block, vocab 151936",
+                   "global_batch": 1, "seq_len": dec.prefix + sum(dec.blocks), "parallelism": "none (1 GPU)",
+                   "mode": args.mode},
+        "denoise_step_ms": round(ms_per_step / dec.denoise_steps, 5),
+        "attn": {"avg_us": round(attn_us, 3), "TB_s": round(attn_gbs / 1e3, 4),
+                 "TFLOP_s": round(attn_tflops, 3), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 5),
+                 "bytes_per_call": attn_bytes / n_attn, "flops_per_call": attn_flops / n_attn},
+        "unmask": {"avg_us": round(unmask_us, 3), "scan_GB_s": round(scan_gbs, 1),
+                   "avg_masked_rows": float(np.mean(masked_rows))},
+        "kernel_avg_us": kernel_us,
+        "trace": {"span_us": round(trace_span_us, 1), "kernels_us": round(sum(tot.values()), 1),
+                  "gate_to_first_call_us": round(gate_slack_us, 2)},
+        "roofline": roof,
+        "wall_s_timed": round(wall, 4),
+        "setup_s": round(setup_s, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dec, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(dec, args):
+    """The float64 oracle on the host cores: the whole section decode (same
+    seeded inputs, 88 denoise steps: attention + unmask each, commit per
+    block), repeated until about --cpu-seconds have passed, in decoded tokens
+    per second."""
+    import threadpoolctl
+    from oracle import attention as OA, kvcache as OK, unmask as OU
+    from block_causal_attention_gqa_amd import synth
+
+    seed = args.seed
+    (_, _), (k32, v32) = synth.kv_cache(seed, 1, dec.Hkv, dec.cap, dec.D, [dec.prefix], dec.dtype)
+    # inputs first (not timed): the same seeded tensors the GPU decode uses
+    inputs = []
+    for b, bs in enumerate(dec.blocks):
+        row = []
+        for st in range(dec.steps):
+            (_, q), (_, k), (_, v) = synth.active_qkv(seed, 1, bs, dec.Hq, dec.Hkv, dec.D, dec.dtype, b, st)
+            row.append((q, k, v, synth.logits(seed, bs, dec.V, dec.sigma, b, st)))
+        inputs.append(row)
+    tokens, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        cache = OK.new_cache(k32, v32, [dec.prefix])
+        for b, bs in enumerate(dec.blocks):
+            masked = np.ones(bs, np.uint8)
+            toks = np.full(bs, -1, np.int32)
+            for st in range(dec.steps):
+                q, k, v, lg = inputs[b][st]
+                ck, cv = cache[0]
+                OA.attention_step(q, ck[None], cv[None], [ck.shape[1]], k, v, [0, bs], OA.MASK_BIDIR,
+                                  scale=dec.scale)
+                masked, toks, _, _ = OU.unmask_select(lg, [0, bs], [OU.MODE_FULL], [dec.steps - st],
+                                                      np.float32(dec.tau), masked, toks)
+            OK.commit(cache, 0, cache[0][0].shape[1], k[0], v[0])
+            tokens += bs
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
+            break
+    secs = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": round(tokens / secs, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": "%d repetitions of the whole section decode (%d tokens, %d denoise steps each) on "
+                      "the same inputs; BLAS threads %d, os.cpu_count()=%s"
+                      % (reps, sum(dec.blocks), dec.denoise_steps, threads, os.cpu_count()),
+            "seconds": round(secs, 2)}
+
+
+if __name__ == "__main__":
+    main()

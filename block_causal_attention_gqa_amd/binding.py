@@ -33,9 +33,11 @@ BC_UNMASK_FULL = 1
 BC_MAX_SEQ = 64
 BC_MAX_BLOCKS = 64
 BC_MAX_BLOCK_ROWS = 1024
+BC_MAX_SCAN_ROWS = 4096
 
 EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
-            "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_status_str")
+            "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_status_str",
+            "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -78,13 +80,18 @@ def lib():
     L.bc_kv_commit.restype = ctypes.c_int
     L.bc_attn_workspace_bytes.argtypes = [cp, cp, ap, i32]
     L.bc_attn_workspace_bytes.restype = sz
-    L.bc_attn_step.argtypes = [cp, _c_i32p, cp, _c_i32p, ap, i32, ctypes.c_float, i32, vp, vp, sz, vp]
-    L.bc_attn_step.restype = ctypes.c_int
+    for name in ("bc_attn_step", "bc_attn_partial", "bc_attn_combine"):
+        f = getattr(L, name)
+        f.argtypes = [cp, _c_i32p, cp, _c_i32p, ap, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
     L.bc_unmask_workspace_bytes.argtypes = [i32, i32]
     L.bc_unmask_workspace_bytes.restype = sz
-    L.bc_unmask_select.argtypes = [vp, i32, i32, _c_i32p, i32, _c_i32p, _c_i32p, ctypes.c_float,
-                                   vp, vp, vp, vp, vp, sz, vp]
-    L.bc_unmask_select.restype = ctypes.c_int
+    for name in ("bc_unmask_select", "bc_unmask_decide"):
+        f = getattr(L, name)
+        f.argtypes = [vp, i32, i32, _c_i32p, i32, _c_i32p, _c_i32p, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    L.bc_vocab_scan.argtypes = [vp, i32, i32, vp, i32, vp, sz, vp]
+    L.bc_vocab_scan.restype = ctypes.c_int
     L.bc_verify_workspace_bytes.argtypes = [i32, i32, i32]
     L.bc_verify_workspace_bytes.restype = sz
     L.bc_spec_verify.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -179,8 +186,8 @@ def bc_attn_workspace_bytes(prefix, priv, q_shape, blk_off, n_prefix_splits=0):
                                              ctypes.byref(act), int(n_prefix_splits)))
 
 
-def bc_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
-                 n_prefix_splits=0, stream=None, check=True):
+def _attn_call(name, prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+               n_prefix_splits, stream, check):
     tdtype = prefix.k.dtype
     act, off_arr = _active(q, k, v, blk_off, tdtype, prefix.n_kv_heads, prefix.head_dim)
     pl_arr, pl_p = _host_i32(prefix_len)
@@ -195,12 +202,30 @@ def bc_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, sca
     else:
         vs, vl_arr, vl_p = None, None, None
     _dev(out, "out", tdtype, q.numel())
-    st = lib().bc_attn_step(ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p,
-                            ctypes.byref(act), int(mask), float(scale), int(n_prefix_splits),
-                            out.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    st = getattr(lib(), name)(ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p,
+                              ctypes.byref(act), int(mask), float(scale), int(n_prefix_splits),
+                              out.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     if check and st != BC_OK:
-        raise BcError(st, "bc_attn_step")
+        raise BcError(st, name)
     return st
+
+
+def bc_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                 n_prefix_splits=0, stream=None, check=True):
+    return _attn_call("bc_attn_step", prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out,
+                      ws, n_prefix_splits, stream, check)
+
+
+def bc_attn_partial(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                    n_prefix_splits=0, stream=None, check=True):
+    return _attn_call("bc_attn_partial", prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale,
+                      out, ws, n_prefix_splits, stream, check)
+
+
+def bc_attn_combine(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                    n_prefix_splits=0, stream=None, check=True):
+    return _attn_call("bc_attn_combine", prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale,
+                      out, ws, n_prefix_splits, stream, check)
 
 
 def bc_kv_commit(cache, length, seq, start, n_rows, blk_k, blk_v, stream=None, check=True):
@@ -222,8 +247,30 @@ def bc_unmask_workspace_bytes(n_rows, vocab):
     return int(lib().bc_unmask_workspace_bytes(int(n_rows), int(vocab)))
 
 
+def bc_vocab_scan(logits, row_mask, with_sum, ws, stream=None, check=True):
+    R, V = (int(x) for x in logits.shape)
+    st = lib().bc_vocab_scan(_dev(logits, "logits", torch.float32, R * V), R, V,
+                             _dev(row_mask, "row_mask", torch.uint8, R, allow_none=True), int(bool(with_sum)),
+                             _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_vocab_scan")
+    return st
+
+
 def bc_unmask_select(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
                      stream=None, check=True):
+    return _unmask_call("bc_unmask_select", logits, blk_off, mode, n_div, threshold, masked, tokens, conf,
+                        n_commit, ws, stream, check)
+
+
+def bc_unmask_decide(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+                     stream=None, check=True):
+    return _unmask_call("bc_unmask_decide", logits, blk_off, mode, n_div, threshold, masked, tokens, conf,
+                        n_commit, ws, stream, check)
+
+
+def _unmask_call(name, logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+                 stream, check):
     R, V = (int(x) for x in logits.shape)
     off_arr, off_p = _host_i32(blk_off)
     n_blk = len(off_arr) - 1
@@ -231,13 +278,13 @@ def bc_unmask_select(logits, blk_off, mode, n_div, threshold, masked, tokens, co
     div_arr, div_p = _host_i32(n_div)
     if len(mode_arr) != n_blk or len(div_arr) != n_blk:
         raise ValueError("mode and n_div need one entry per block")
-    st = lib().bc_unmask_select(
+    st = getattr(lib(), name)(
         _dev(logits, "logits", torch.float32, R * V), R, V, off_p, n_blk, mode_p, div_p,
         float(threshold), _dev(masked, "masked", torch.uint8, R), _dev(tokens, "tokens", torch.int32, R),
         _dev(conf, "conf", torch.float32, R, allow_none=True), _dev(n_commit, "n_commit", torch.int32, n_blk),
         _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
     if check and st != BC_OK:
-        raise BcError(st, "bc_unmask_select")
+        raise BcError(st, name)
     return st
 
 

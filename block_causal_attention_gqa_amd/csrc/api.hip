@@ -38,7 +38,7 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 
 // ------------------------------------------------------------ attention plan
 struct Plan {
-  int P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  int waves, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
   size_t o_bytes, ml_bytes, total_bytes;
 };
 
@@ -76,8 +76,12 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   const bool fork = priv != nullptr;
   const int groups = fork ? Hkv : S * Hkv;
   const int rows_group = fork ? S * R * group : R * group;
-  p->n_mt_prefix = (rows_group + kAttnTileRows - 1) / kAttnTileRows;
-  p->n_mt_active = (R * group + kAttnTileRows - 1) / kAttnTileRows;
+  // Few row tiles (small batch): 2-wave workgroups double the tiles, so the
+  // key range needs half as many splits for the same parallelism.
+  p->waves = groups * ((rows_group + 127) / 128) < 32 ? 2 : 4;
+  const int tile_rows = p->waves * kAttnRowsPerWave;
+  p->n_mt_prefix = (rows_group + tile_rows - 1) / tile_rows;
+  p->n_mt_active = (R * group + tile_rows - 1) / tile_rows;
   int maxlen = 0;
   for (int s = 0; s < prefix->n_seq; ++s) maxlen = std::max(maxlen, lengths[s]);
   int P = n_splits;
@@ -135,8 +139,7 @@ int bc_kv_commit(const bc_kv_cache* cache, int32_t* len, int32_t seq, int32_t st
   (void)hipGetLastError();
   char* kdst = static_cast<char*>(cache->k) + seq * seq_stride * eb;
   char* vdst = static_cast<char*>(cache->v) + seq * seq_stride * eb;
-  if (launch_commit(kdst, blk_k, cache->dtype, Hkv, D, seq_stride, head_stride, start, n_rows, s) != hipSuccess ||
-      launch_commit(vdst, blk_v, cache->dtype, Hkv, D, seq_stride, head_stride, start, n_rows, s) != hipSuccess)
+  if (launch_commit(kdst, vdst, blk_k, blk_v, cache->dtype, Hkv, D, head_stride, start, n_rows, s) != hipSuccess)
     return BC_ERR_HIP;
   len[seq] = start + n_rows;
   return BC_OK;
@@ -153,9 +156,14 @@ size_t bc_attn_workspace_bytes(const bc_kv_cache* prefix, const bc_kv_cache* pri
   return p.total_bytes;
 }
 
-int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
-                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale,
-                 int32_t n_prefix_splits, void* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate an attention call and fill the kernel arguments; BC_OK or an error.
+int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale, int32_t n_prefix_splits,
+                 void* out, void* ws, size_t ws_bytes, AttnArgs* args) {
   int st = validate_attn(prefix, priv, a, n_prefix_splits);
   if (st) return st;
   if (!prefix_len || !out || (priv && !priv_len)) return BC_ERR_ARG;
@@ -167,10 +175,9 @@ int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
     for (int s = 0; s < a->n_seq; ++s)
       if (priv_len[s] < 0 || priv_len[s] > priv->capacity) return BC_ERR_ARG;
 
-  AttnArgs args;
-  std::memset(&args, 0, sizeof(args));
+  std::memset(args, 0, sizeof(*args));
   Plan p;
-  make_plan(prefix, priv, a, prefix_len, n_prefix_splits, &p, args.chunk);
+  make_plan(prefix, priv, a, prefix_len, n_prefix_splits, &p, args->chunk);
   if (!ws) return BC_ERR_WORKSPACE;
   {
     // the caller sized the workspace for the capacities; check against that bound
@@ -182,60 +189,53 @@ int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
     if (ws_bytes < pmax.total_bytes || ws_bytes < p.total_bytes) return BC_ERR_WORKSPACE;
   }
   const int D = prefix->head_dim;
-  args.q = a->q;
-  args.out = out;
-  args.pk = prefix->k;
-  args.pv = prefix->v;
-  args.p_head_stride = (long long)prefix->capacity * D;
-  args.p_seq_stride = args.p_head_stride * prefix->n_kv_heads;
+  args->q = a->q;
+  args->out = out;
+  args->pk = prefix->k;
+  args->pv = prefix->v;
+  args->p_head_stride = (long long)prefix->capacity * D;
+  args->p_seq_stride = args->p_head_stride * prefix->n_kv_heads;
   if (priv) {
-    args.vk = priv->k;
-    args.vv = priv->v;
-    args.v_head_stride = (long long)priv->capacity * D;
-    args.v_seq_stride = args.v_head_stride * priv->n_kv_heads;
+    args->vk = priv->k;
+    args->vv = priv->v;
+    args->v_head_stride = (long long)priv->capacity * D;
+    args->v_seq_stride = args->v_head_stride * priv->n_kv_heads;
   }
-  args.ak = a->k;
-  args.av = a->v;
-  args.ws_o = static_cast<float*>(ws);
-  args.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.o_bytes);
-  args.scale_log2 = scale * 1.4426950408889634f;
-  args.S = a->n_seq;
-  args.R = a->n_rows;
-  args.Hq = a->n_q_heads;
-  args.Hkv = prefix->n_kv_heads;
-  args.group = a->n_q_heads / prefix->n_kv_heads;
-  args.D = D;
-  args.fork = priv ? 1 : 0;
-  args.causal = mask == BC_MASK_BLOCK_CAUSAL;
-  args.n_splits = p.P;
-  args.n_slots = p.n_slots;
-  args.n_mt_prefix = p.n_mt_prefix;
-  args.n_mt_active = p.n_mt_active;
-  args.n_prefix_items = p.n_prefix_items;
-  args.n_items = p.n_items;
-  args.rows_total = p.rows_total;
-  args.n_blk = a->n_blk;
-  for (int b = 0; b <= a->n_blk; ++b) args.blk_off[b] = a->blk_off[b];
-  for (int s = 0; s < prefix->n_seq; ++s) args.prefix_len[s] = prefix_len[s];
+  args->ak = a->k;
+  args->av = a->v;
+  args->ws_o = static_cast<float*>(ws);
+  args->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.o_bytes);
+  args->scale_log2 = scale * 1.4426950408889634f;
+  args->S = a->n_seq;
+  args->R = a->n_rows;
+  args->Hq = a->n_q_heads;
+  args->Hkv = prefix->n_kv_heads;
+  args->group = a->n_q_heads / prefix->n_kv_heads;
+  args->D = D;
+  args->waves = p.waves;
+  args->fork = priv ? 1 : 0;
+  args->causal = mask == BC_MASK_BLOCK_CAUSAL;
+  args->n_splits = p.P;
+  args->n_slots = p.n_slots;
+  args->n_mt_prefix = p.n_mt_prefix;
+  args->n_mt_active = p.n_mt_active;
+  args->n_prefix_items = p.n_prefix_items;
+  args->n_items = p.n_items;
+  args->rows_total = p.rows_total;
+  args->n_blk = a->n_blk;
+  for (int b = 0; b <= a->n_blk; ++b) args->blk_off[b] = a->blk_off[b];
+  for (int s = 0; s < prefix->n_seq; ++s) args->prefix_len[s] = prefix_len[s];
   if (priv)
-    for (int s = 0; s < a->n_seq; ++s) args.priv_len[s] = priv_len[s];
-  (void)hipGetLastError();
-  if (launch_attn(args, prefix->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
+    for (int s = 0; s < a->n_seq; ++s) args->priv_len[s] = priv_len[s];
   return BC_OK;
 }
 
-size_t bc_unmask_workspace_bytes(int32_t n_rows, int32_t vocab) {
-  if (n_rows < 1 || vocab < 1) return 0;
-  return align256((size_t)n_rows * scan_chunks(vocab) * sizeof(ScanPartial));
-}
-
-int bc_unmask_select(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off,
-                     int32_t n_blk, const int32_t* mode, const int32_t* n_div, float threshold,
-                     uint8_t* masked, int32_t* tokens, float* conf, int32_t* n_commit, void* ws,
-                     size_t ws_bytes, void* stream) {
+int validate_unmask(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                    const int32_t* mode, const int32_t* n_div, float threshold, const uint8_t* masked,
+                    const int32_t* tokens, const int32_t* n_commit, const void* ws, size_t ws_bytes) {
   if (!logits || !mode || !n_div || !masked || !tokens || !n_commit) return BC_ERR_ARG;
   if (n_rows < 1 || vocab < 1) return BC_ERR_ARG;
-  if (n_rows > 65535) return BC_ERR_UNSUPPORTED;
+  if (n_rows > BC_MAX_SCAN_ROWS) return BC_ERR_UNSUPPORTED;
   int st = check_blk_off(blk_off, n_blk, n_rows, BC_MAX_BLOCK_ROWS);
   if (st) return st;
   for (int b = 0; b < n_blk; ++b) {
@@ -244,31 +244,120 @@ int bc_unmask_select(const float* logits, int32_t n_rows, int32_t vocab, const i
   }
   if (!std::isfinite(threshold)) return BC_ERR_ARG;
   if (!ws || ws_bytes < bc_unmask_workspace_bytes(n_rows, vocab)) return BC_ERR_WORKSPACE;
-  UnmaskArgs args;
-  std::memset(&args, 0, sizeof(args));
-  args.logits = logits;
-  args.n_rows = n_rows;
-  args.vocab = vocab;
-  args.n_chunks = scan_chunks(vocab);
-  args.n_blk = n_blk;
-  args.masked = masked;
-  args.tokens = tokens;
-  args.conf = conf;
-  args.n_commit = n_commit;
-  args.part = static_cast<ScanPartial*>(ws);
-  args.threshold = threshold;
-  for (int b = 0; b <= n_blk; ++b) args.blk_off[b] = blk_off[b];
-  for (int b = 0; b < n_blk; ++b) {
-    args.mode[b] = mode[b];
-    args.n_div[b] = n_div[b];
-  }
-  (void)hipGetLastError();
-  if (launch_unmask(args, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
   return BC_OK;
 }
 
+void fill_unmask(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                 const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
+                 float* conf, int32_t* n_commit, void* ws, UnmaskArgs* args) {
+  std::memset(args, 0, sizeof(*args));
+  args->logits = logits;
+  args->n_rows = n_rows;
+  args->vocab = vocab;
+  args->n_chunks = scan_chunks(vocab);
+  args->n_blk = n_blk;
+  args->masked = masked;
+  args->tokens = tokens;
+  args->conf = conf;
+  args->n_commit = n_commit;
+  args->part = static_cast<const ScanPartial*>(ws);
+  args->threshold = threshold;
+  for (int b = 0; b <= n_blk; ++b) args->blk_off[b] = blk_off[b];
+  for (int b = 0; b < n_blk; ++b) {
+    args->mode[b] = mode[b];
+    args->n_div[b] = n_div[b];
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int bc_attn_partial(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                    const int32_t* priv_len, const bc_active* a, int32_t mask, float scale, int32_t n_prefix_splits,
+                    void* out, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs args;
+  const int st = prepare_attn(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out, ws,
+                              ws_bytes, &args);
+  if (st) return st;
+  (void)hipGetLastError();
+  return launch_attn_partial(args, prefix->dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? BC_OK
+                                                                                                   : BC_ERR_HIP;
+}
+
+int bc_attn_combine(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                    const int32_t* priv_len, const bc_active* a, int32_t mask, float scale, int32_t n_prefix_splits,
+                    void* out, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs args;
+  const int st = prepare_attn(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out, ws,
+                              ws_bytes, &args);
+  if (st) return st;
+  (void)hipGetLastError();
+  return launch_attn_combine(args, prefix->dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? BC_OK
+                                                                                                   : BC_ERR_HIP;
+}
+
+int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale,
+                 int32_t n_prefix_splits, void* out, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs args;
+  const int st = prepare_attn(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out, ws,
+                              ws_bytes, &args);
+  if (st) return st;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_attn_partial(args, prefix->dtype, s) != hipSuccess) return BC_ERR_HIP;
+  if (launch_attn_combine(args, prefix->dtype, s) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
+// unmask / verify workspaces hold the per-(row, chunk) scan partials.
+size_t bc_unmask_workspace_bytes(int32_t n_rows, int32_t vocab) {
+  if (n_rows < 1 || vocab < 1 || n_rows > BC_MAX_SCAN_ROWS) return 0;
+  return align256((size_t)n_rows * scan_chunks(vocab) * sizeof(ScanPartial));
+}
+
+int bc_vocab_scan(const float* logits, int32_t n_rows, int32_t vocab, const uint8_t* row_mask, int32_t with_sum,
+                  void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || n_rows < 1 || vocab < 1) return BC_ERR_ARG;
+  if (n_rows > BC_MAX_SCAN_ROWS) return BC_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < bc_unmask_workspace_bytes(n_rows, vocab)) return BC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return launch_scan(logits, n_rows, vocab, row_mask, with_sum != 0, static_cast<ScanPartial*>(ws),
+                     static_cast<hipStream_t>(stream)) == hipSuccess ? BC_OK : BC_ERR_HIP;
+}
+
+int bc_unmask_decide(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                     const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
+                     float* conf, int32_t* n_commit, void* ws, size_t ws_bytes, void* stream) {
+  const int st = validate_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens,
+                                 n_commit, ws, ws_bytes);
+  if (st) return st;
+  UnmaskArgs args;
+  fill_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+              &args);
+  (void)hipGetLastError();
+  return launch_unmask_decide(args, static_cast<hipStream_t>(stream)) == hipSuccess ? BC_OK : BC_ERR_HIP;
+}
+
+int bc_unmask_select(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                     const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
+                     float* conf, int32_t* n_commit, void* ws, size_t ws_bytes, void* stream) {
+  const int st = validate_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens,
+                                 n_commit, ws, ws_bytes);
+  if (st) return st;
+  UnmaskArgs args;
+  fill_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+              &args);
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_scan(logits, n_rows, vocab, masked, true, static_cast<ScanPartial*>(ws), s) != hipSuccess)
+    return BC_ERR_HIP;
+  return launch_unmask_decide(args, s) == hipSuccess ? BC_OK : BC_ERR_HIP;
+}
+
 size_t bc_verify_workspace_bytes(int32_t n_seq, int32_t n_lrows, int32_t vocab) {
-  if (n_seq < 1 || n_lrows < 1 || vocab < 1) return 0;
+  if (n_seq < 1 || n_lrows < 1 || vocab < 1 || (long long)n_seq * n_lrows > BC_MAX_SCAN_ROWS) return 0;
   return align256((size_t)n_seq * n_lrows * scan_chunks(vocab) * sizeof(ScanPartial));
 }
 
@@ -277,7 +366,7 @@ int bc_spec_verify(const float* logits, int32_t n_seq, int32_t n_lrows, int32_t 
                    int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !draft || !first || !accept_len || !bonus) return BC_ERR_ARG;
   if (n_seq < 1 || n_lrows < 1 || vocab < 1 || m < 1 || m > n_lrows) return BC_ERR_ARG;
-  if ((long long)n_seq * n_lrows > 65535) return BC_ERR_UNSUPPORTED;
+  if ((long long)n_seq * n_lrows > BC_MAX_SCAN_ROWS) return BC_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < bc_verify_workspace_bytes(n_seq, n_lrows, vocab)) return BC_ERR_WORKSPACE;
   VerifyArgs args;
   std::memset(&args, 0, sizeof(args));

@@ -10,8 +10,8 @@
 //
 // Work decomposition.  Query rows are grouped per KV head: row m of a group
 // is (sequence, active row, query head within the GQA group), so one K/V
-// stream serves all `group` query heads.  A workgroup (4 waves x 32 rows)
-// takes one 128-row tile against one key range and writes an unnormalised
+// stream serves all `group` query heads.  A workgroup (2 or 4 waves x 32
+// rows) takes one row tile against one key range and writes an unnormalised
 // partial (running max, sum, output) to its slot:
 //   * prefix items: slot p < P covers chunk p of the committed prefix; under
 //     a fork the tile runs over the rows of ALL rollouts, so the shared prefix
@@ -62,6 +62,11 @@ template <int D> struct Cfg<float, D> {
 
 __device__ inline float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
+// every outstanding global load of the wave, which would stall on the next
+// key tile's prefetch; here only LDS traffic is drained before the barrier.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map
 // hardware id -> logical id so that consecutive logical ids (the row tiles
 // sharing one key chunk) land on the same XCD and share its L2.
@@ -78,9 +83,11 @@ __device__ inline int key_pos(int t, int jj, int i) {
   else return 16 * t + 4 * jj + i;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a) {
   using C = Cfg<T, D>;
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int kTileRows = NW * kAttnRowsPerWave;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int KT = kAttnKeyTile;
   __shared__ __attribute__((aligned(16))) T k_lds[C::K_ELEMS];
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
   int orow[2], lim[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int m = mt * kAttnTileRows + wave * kAttnRowsPerWave + c * 16 + n;
+    const int m = mt * kTileRows + wave * kAttnRowsPerWave + c * 16 + n;
     valid[c] = m < rows_in_group;
     int s = s_item, rem = m;
     if (s_item < 0) { s = m / (a.R * a.group); rem = m - s * (a.R * a.group); }
@@ -179,28 +186,65 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
     return base + ((long long)(s_act * a.Hkv + g) * a.R + (key - lv)) * D;
   };
 
-  for (int kb = key_begin; kb < key_end; kb += KT) {
-    __syncthreads();
-    // ---- stage K (and V) of keys kb .. kb + 63 in LDS; keys past the range are zero
-    if constexpr (kBf16) {
-      constexpr int CPR = D / 8;   // 16-byte chunks per row
-      for (int idx = tid; idx < KT * CPR; idx += 256) {
-        const int kr = idx / CPR, cc = idx - kr * CPR;
-        const int key = kb + kr;
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (key < key_end) val = *reinterpret_cast<const uint4*>(key_row(key, false) + 8 * cc);
-        *reinterpret_cast<uint4*>(&k_lds[kr * C::KP + 8 * cc]) = val;
+  // ---- register staging of one key tile: the next tile's global loads are
+  // issued before the current tile is computed, so HBM latency is paid once.
+  constexpr int CPR = kBf16 ? D / 8 : D / 4;           // 16-byte units per key row
+  constexpr int NK = (KT * CPR + NT - 1) / NT;         // K units per thread
+  constexpr int NVQ = ((KT / 4) * CPR + NT - 1) / NT;  // bf16: 4-key quads per thread
+  constexpr int NV = kBf16 ? 4 * NVQ : NK;             // V units per thread
+  uint4 kreg[NK], vreg[NV];
+
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int idx = tid + NT * u;
+      const int kr = idx / CPR, cc = idx - kr * CPR;
+      const int key = kb + kr;
+      kreg[u] = uint4{0u, 0u, 0u, 0u};
+      if (idx < KT * CPR && key < key_end)
+        kreg[u] = *reinterpret_cast<const uint4*>(key_row(key, false) + (kBf16 ? 8 : 4) * cc);
+      if constexpr (!kBf16) {
+        vreg[u] = uint4{0u, 0u, 0u, 0u};
+        if (idx < KT * CPR && key < key_end)
+          vreg[u] = *reinterpret_cast<const uint4*>(key_row(key, true) + 4 * cc);
       }
-      // V transposed: each thread takes 4 consecutive keys x 8 dims
-      for (int idx = tid; idx < (KT / 4) * CPR; idx += 256) {
+    }
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int u = 0; u < NVQ; ++u) {
+        const int idx = tid + NT * u;
         const int qd = idx % (KT / 4), cc = idx / (KT / 4);
-        uint4 v4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb + 4 * qd + i;
-          v4[i] = uint4{0u, 0u, 0u, 0u};
-          if (key < key_end) v4[i] = *reinterpret_cast<const uint4*>(key_row(key, true) + 8 * cc);
+          vreg[4 * u + i] = uint4{0u, 0u, 0u, 0u};
+          if (idx < (KT / 4) * CPR && key < key_end)
+            vreg[4 * u + i] = *reinterpret_cast<const uint4*>(key_row(key, true) + 8 * cc);
         }
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int idx = tid + NT * u;
+      if (idx >= KT * CPR) continue;
+      const int kr = idx / CPR, cc = idx - kr * CPR;
+      if constexpr (kBf16) {
+        *reinterpret_cast<uint4*>(&k_lds[kr * C::KP + 8 * cc]) = kreg[u];
+      } else {
+        *reinterpret_cast<uint4*>(&k_lds[kr * C::KP + 4 * cc]) = kreg[u];
+        *reinterpret_cast<uint4*>(&v_lds[kr * C::VP + 4 * cc]) = vreg[u];
+      }
+    }
+    if constexpr (kBf16) {
+      // V transposed: 4 consecutive keys x 8 dims -> 8 rows of V^T, 4 keys each
+#pragma unroll
+      for (int u = 0; u < NVQ; ++u) {
+        const int idx = tid + NT * u;
+        if (idx >= (KT / 4) * CPR) continue;
+        const int qd = idx % (KT / 4), cc = idx / (KT / 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t sh = (e & 1) * 16;
@@ -210,26 +254,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
             return (word >> sh) & 0xffffu;
           };
           uint2 packed;
-          packed.x = pick(v4[0]) | (pick(v4[1]) << 16);
-          packed.y = pick(v4[2]) | (pick(v4[3]) << 16);
+          packed.x = pick(vreg[4 * u]) | (pick(vreg[4 * u + 1]) << 16);
+          packed.y = pick(vreg[4 * u + 2]) | (pick(vreg[4 * u + 3]) << 16);
           *reinterpret_cast<uint2*>(&v_lds[(8 * cc + e) * C::VP + 4 * qd]) = packed;
         }
       }
-    } else {
-      constexpr int CPR = D / 4;
-      for (int idx = tid; idx < KT * CPR; idx += 256) {
-        const int kr = idx / CPR, cc = idx - kr * CPR;
-        const int key = kb + kr;
-        float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-        if (key < key_end) {
-          kv = *reinterpret_cast<const float4*>(key_row(key, false) + 4 * cc);
-          vv = *reinterpret_cast<const float4*>(key_row(key, true) + 4 * cc);
-        }
-        *reinterpret_cast<float4*>(&k_lds[kr * C::KP + 4 * cc]) = kv;
-        *reinterpret_cast<float4*>(&v_lds[kr * C::VP + 4 * cc]) = vv;
-      }
     }
-    __syncthreads();
+  };
+
+  if (key_begin < key_end) load_tile(key_begin);
+  for (int kb = key_begin; kb < key_end; kb += KT) {
+    lds_barrier();             // the previous tile's LDS reads are complete
+    store_tile();
+    if (kb + KT < key_end) load_tile(kb + KT);
+    lds_barrier();
 
     // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
     f32x4 st[2][4];
@@ -260,19 +298,32 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
     }
 
     // ---- online softmax, one query column per lane and column tile
+    // a prefix tile inside its key range is fully visible: no predicate
+    const bool full_tile = is_prefix && kb + KT <= key_end;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float tmax = kNegInf;
+      if (full_tile) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + key_pos<T>(t, jj, i);
-          const bool vis = key < key_end && (is_prefix || key < lv || key - lv < lim[c]);
-          const float x = vis ? st[c][t][i] * a.scale_log2 : kNegInf;
-          st[c][t][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float x = st[c][t][i] * a.scale_log2;
+            st[c][t][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + key_pos<T>(t, jj, i);
+            const bool vis = key < key_end && (is_prefix || key < lv || key - lv < lim[c]);
+            const float x = vis ? st[c][t][i] * a.scale_log2 : kNegInf;
+            st[c][t][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      }
       tmax = fmaxf(tmax, wave_xor(tmax, 16));
       tmax = fmaxf(tmax, wave_xor(tmax, 32));
       const float mnew = fmaxf(m_run[c], tmax);
@@ -289,8 +340,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
         }
       l_run[c] = l_run[c] * alpha + psum;
       m_run[c] = mnew;
+      if (__any(alpha != 1.f)) {   // wave-uniform: skip when no column's max moved
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha;
+        for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha;
+      }
     }
 
     // ---- O^T += V^T P^T
@@ -345,33 +398,78 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
-// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.
+// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  One row per
+// workgroup; wave w takes slots w, w + 4, ... eight at a time with every load
+// of the batch issued before any is used, rescaling online when a batch
+// raises the running max; the four waves then merge through LDS.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows_total) return;
-  float mx = kNegInf;
-  for (int s = 0; s < a.n_slots; ++s) mx = fmaxf(mx, a.ws_ml[(long long)s * a.rows_total + row].x);
   constexpr int E = D / 64;
-  float acc[E];
+  constexpr int B = 8;
+  __shared__ float red_o[4][D];
+  __shared__ float red_m[4], red_l[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+  float wm = kNegInf, wl = 0.f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  for (int s = 0; s < a.n_slots; ++s) {
-    const long long prow = (long long)s * a.rows_total + row;
-    const float2 ml = a.ws_ml[prow];
-    if (ml.x == kNegInf) continue;
-    const float w = __builtin_amdgcn_exp2f(ml.x - mx);
-    L += w * ml.y;
+  for (int s0 = wave; s0 < a.n_slots; s0 += 4 * B) {
+    float2 ml[B];
+    float ov[B][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += w * a.ws_o[prow * D + lane + 64 * e];
+    for (int u = 0; u < B; ++u) {
+      const int s = s0 + 4 * u;
+      const long long prow = (long long)s * a.rows_total + row;
+      ml[u] = float2{kNegInf, 0.f};
+#pragma unroll
+      for (int e = 0; e < E; ++e) ov[u][e] = 0.f;
+      if (s < a.n_slots) {
+        ml[u] = a.ws_ml[prow];
+#pragma unroll
+        for (int e = 0; e < E; ++e) ov[u][e] = a.ws_o[prow * D + lane + 64 * e];
+      }
+    }
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < B; ++u) bm = fmaxf(bm, ml[u].x);
+    const float nm = fmaxf(wm, bm);
+    if (nm == kNegInf) continue;
+    const float sc = __builtin_amdgcn_exp2f(wm - nm);
+    wl *= sc;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float w = ml[u].x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - nm);
+      wl += w * ml[u].y;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * ov[u][e];
+    }
+    wm = nm;
+  }
+  if (lane == 0) { red_m[wave] = wm; red_l[wave] = wl; }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red_o[wave][lane + 64 * e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w]);
+  float L = 0.f, o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float f = red_m[w] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(red_m[w] - M);
+    L += f * red_l[w];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += f * red_o[w][lane + 64 * e];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   T* out = static_cast<T*>(a.out) + (long long)row * D;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float v = acc[e] * inv;
+    const float v = o[e] * inv;
     if constexpr (sizeof(T) == 2) {
       const __bf16 b = (__bf16)v;
       out[lane + 64 * e] = *reinterpret_cast<const uint16_t*>(&b);
@@ -382,19 +480,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial_kernel<T, D>), dim3(a.n_items), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((a.rows_total + 3) / 4), dim3(256), 0, stream, a);
+hipError_t launch_partial_typed(const AttnArgs& a, hipStream_t stream) {
+  if (a.waves == 2)
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<T, D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_combine_typed(const AttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(a.rows_total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t stream) {
-  if (dtype == BC_BF16) return a.D == 128 ? launch_typed<bf16_t, 128>(a, stream) : launch_typed<bf16_t, 64>(a, stream);
-  return a.D == 128 ? launch_typed<float, 128>(a, stream) : launch_typed<float, 64>(a, stream);
+hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == BC_BF16)
+    return a.D == 128 ? launch_partial_typed<bf16_t, 128>(a, stream) : launch_partial_typed<bf16_t, 64>(a, stream);
+  return a.D == 128 ? launch_partial_typed<float, 128>(a, stream) : launch_partial_typed<float, 64>(a, stream);
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == BC_BF16)
+    return a.D == 128 ? launch_combine_typed<bf16_t, 128>(a, stream) : launch_combine_typed<bf16_t, 64>(a, stream);
+  return a.D == 128 ? launch_combine_typed<float, 128>(a, stream) : launch_combine_typed<float, 64>(a, stream);
 }
 
 }  // namespace bc

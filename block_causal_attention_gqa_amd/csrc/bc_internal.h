@@ -5,14 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/bc.h"
+#include "bc.h"   // include/bc.h (the build passes -I include)
 
 namespace bc {
 
 // ---------------------------------------------------------------- attention
-constexpr int kAttnWaves = 4;             // waves per workgroup
 constexpr int kAttnRowsPerWave = 32;      // query rows per wave (2 MFMA column tiles)
-constexpr int kAttnTileRows = kAttnWaves * kAttnRowsPerWave;
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 
 struct AttnArgs {
@@ -30,6 +28,7 @@ struct AttnArgs {
   float2* ws_ml;       // [n_slots][rows_total] (running max in log2 units, sum)
   float scale_log2;    // softmax scale * log2(e)
   int S, R, Hq, Hkv, group, D;
+  int waves;           // waves per workgroup (2 or 4); a row tile is waves * 32 rows
   int fork;            // 1: one shared prefix for all S rollouts + private caches
   int causal;          // bc_mask
   int n_splits;        // prefix chunks P; slot P holds private + active keys
@@ -46,17 +45,17 @@ struct AttnArgs {
   int priv_len[BC_MAX_SEQ];
 };
 
-hipError_t launch_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream);
 
 // -------------------------------------------------------------- commit
-hipError_t launch_commit(void* cache, const void* blk, int dtype, int Hkv, int D,
-                         long long seq_stride, long long head_stride, int start, int n_rows,
-                         hipStream_t stream);
+hipError_t launch_commit(void* k_cache, void* v_cache, const void* blk_k, const void* blk_v, int dtype,
+                         int Hkv, int D, long long head_stride, int start, int n_rows, hipStream_t stream);
 
 // -------------------------------------------------------------- vocab scans
 constexpr int kScanThreads = 256;
-constexpr int kScanVecPerThread = 8;                                // float4 per thread
-constexpr int kScanChunk = kScanThreads * kScanVecPerThread * 4;    // 8192 logits
+constexpr int kScanVecPerThread = 16;                               // float4 per thread
+constexpr int kScanChunk = kScanThreads * kScanVecPerThread * 4;    // 16384 logits
 
 struct ScanPartial { float m; int a; float s; int pad; };
 
@@ -69,14 +68,18 @@ struct UnmaskArgs {
   int* tokens;
   float* conf;
   int* n_commit;
-  ScanPartial* part;   // [n_rows][n_chunks]
+  const ScanPartial* part;   // [n_rows][n_chunks], left by the scan
   float threshold;
   int blk_off[BC_MAX_BLOCKS + 1];
   int mode[BC_MAX_BLOCKS];
   int n_div[BC_MAX_BLOCKS];
 };
 
-hipError_t launch_unmask(const UnmaskArgs& a, hipStream_t stream);
+// row_mask: scan rows with row_mask[r] != 0 (all rows when null);
+// with_sum: also the exp-sum (unmask) besides max / argmax.
+hipError_t launch_scan(const float* logits, int n_rows, int vocab, const uint8_t* row_mask, bool with_sum,
+                       ScanPartial* part, hipStream_t stream);
+hipError_t launch_unmask_decide(const UnmaskArgs& a, hipStream_t stream);
 
 struct VerifyArgs {
   const float* logits;

@@ -9,18 +9,21 @@
 //     per row the lowest argmax, then the first row from `first` whose draft
 //     disagrees (scaffold rows pass) -> accept length and bonus token.
 //
-// The scan is one pass over HBM: a (chunk, row) grid where each workgroup
-// reads 8192 logits with 16-byte loads (8 per lane, all in flight before any
-// arithmetic), reduces max / argmax / exp-sum inside the wave and across the
-// 4 waves, and leaves one 16-byte partial.  Rows that need no scan (already
-// revealed, or before `first`) exit before touching HBM.
+// Two kernels per call.  The scan is one pass over HBM: a (chunk, row) grid
+// where each workgroup reads 16384 logits with 16-byte loads (16 per lane,
+// all in flight before any arithmetic), reduces max / argmax / exp-sum inside
+// the wave and across the 4 waves, and leaves one 16-byte partial.  Rows that
+// need no scan (already revealed, or outside the verified range) skip the
+// reads.  The decision kernel runs one workgroup per block (or sequence): it
+// merges each row's chunk partials with 8 lanes per row, one round of loads,
+// and decides.  The kernel boundary is the only synchronisation: no atomics,
+// no counters, and the workspace needs no initialisation.
 //
 // Exact decisions.  Float32 confidences carry a relative error far below
-// 2^-12 (the error analysis is in the design notes); a decision whose float32
-// margin -- to the threshold, or between the rows on both sides of the
-// ranking cut -- is inside that band is retaken on confidences recomputed in
-// float64 by re-reading the row.  Decisions therefore follow the float64
-// confidences.
+// 2^-12.  A decision whose float32 margin -- to the threshold, or between the
+// two sides of the ranking cut -- is inside that band is retaken on
+// confidences recomputed in float64 by re-reading the row, so decisions
+// follow the float64 confidences.
 
 #include <climits>
 
@@ -45,9 +48,10 @@ __device__ inline Acc merge(Acc x, Acc y) {
   return r;
 }
 
-__device__ inline Acc wave_merge(Acc x) {
+template <int kWidth>
+__device__ inline Acc lanes_merge(Acc x) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
+  for (int off = kWidth / 2; off > 0; off >>= 1) {
     Acc y;
     y.m = __shfl_xor(x.m, off, 64);
     y.a = __shfl_xor(x.a, off, 64);
@@ -57,35 +61,20 @@ __device__ inline Acc wave_merge(Acc x) {
   return x;
 }
 
-// mode 0: unmask (row active iff masked[row]); mode 1: verify (row (s, i)
-// active iff first[s] <= i <= m).  kSum: also accumulate the exp-sum.
-template <int kMode, bool kSum, bool kVec>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restrict__ logits, int vocab,
-                                                             int n_chunks, ScanPartial* __restrict__ part,
-                                                             const uint8_t* __restrict__ masked,
-                                                             const int* __restrict__ first, int n_lrows,
-                                                             int m) {
-  const int chunk = blockIdx.x, row = blockIdx.y;
-  if constexpr (kMode == 0) {
-    if (!masked[row]) return;
-  } else {
-    const int s = row / n_lrows, i = row - s * n_lrows;
-    const int f = min(max(first[s], 0), m);
-    if (i < f || i > m) return;
-  }
+// One (chunk, row) partial: max, lowest argmax and (kSum) exp-sum of
+// logits[row][chunk * kScanChunk ...], written by thread 0.
+template <bool kSum, bool kVec>
+__device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk, ScanPartial* out,
+                           Acc* red) {
   const int tid = threadIdx.x;
   const int c0 = chunk * kScanChunk;
   const int c1 = min(vocab, c0 + kScanChunk);
-  const float* rowp = logits + (long long)row * vocab;
-
   constexpr int NV = kScanVecPerThread * 4;
   float v[NV];
-  int idx0[kScanVecPerThread];
   if constexpr (kVec) {
 #pragma unroll
     for (int it = 0; it < kScanVecPerThread; ++it) {
       const int idx = c0 + 4 * (tid + kScanThreads * it);
-      idx0[it] = idx;
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
       if (idx < c1) x = *reinterpret_cast<const float4*>(rowp + idx);
       v[4 * it] = x.x; v[4 * it + 1] = x.y; v[4 * it + 2] = x.z; v[4 * it + 3] = x.w;
@@ -100,7 +89,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
   Acc acc{kNegInf, INT_MAX, 0.f};
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
-    const int idx = kVec ? idx0[e / 4] + (e & 3) : c0 + tid + kScanThreads * e;
+    const int idx = kVec ? c0 + 4 * (tid + kScanThreads * (e / 4)) + (e & 3) : c0 + tid + kScanThreads * e;
     if (v[e] > acc.m) { acc.m = v[e]; acc.a = idx; }
   }
   if constexpr (kSum) {
@@ -111,25 +100,65 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
       acc.s = s;
     }
   }
-  acc = wave_merge(acc);
-  __shared__ Acc red[kScanThreads / 64];
+  acc = lanes_merge<64>(acc);
   if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
   if (tid == 0) {
     Acc t = red[0];
 #pragma unroll
     for (int w = 1; w < kScanThreads / 64; ++w) t = merge(t, red[w]);
-    part[(long long)row * n_chunks + chunk] = ScanPartial{t.m, t.a, t.s, 0};
+    *out = ScanPartial{t.m, t.a, t.s, 0};
   }
 }
 
-__device__ inline Acc combine_row(const ScanPartial* part, int row, int n_chunks) {
-  Acc t{kNegInf, INT_MAX, 0.f};
-  for (int c = 0; c < n_chunks; ++c) {
-    const ScanPartial p = part[(long long)row * n_chunks + c];
-    t = merge(t, Acc{p.m, p.a, p.s});
+// mode 0: rows with row_mask[row] != 0 (all rows when row_mask is null);
+// mode 1: verify, row (s, i) with first[s] <= i <= min(m, n_lrows - 1).
+template <int kMode, bool kSum, bool kVec>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restrict__ logits, int vocab,
+                                                             int n_chunks, ScanPartial* __restrict__ part,
+                                                             const uint8_t* __restrict__ row_mask,
+                                                             const int* __restrict__ first, int n_lrows,
+                                                             int m) {
+  __shared__ Acc red[kScanThreads / 64];
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  if constexpr (kMode == 0) {
+    if (row_mask && !row_mask[row]) return;
+  } else {
+    const int s = row / n_lrows, i = row - s * n_lrows;
+    const int f = min(max(first[s], 0), m);
+    if (i < f || i > min(m, n_lrows - 1)) return;
   }
-  return t;
+  scan_chunk<kSum, kVec>(logits + (long long)row * vocab, vocab, chunk,
+                         &part[(long long)row * n_chunks + chunk], red);
+}
+
+// Merge the chunk partials of rows r0 .. r0 + nr - 1 that `want(i)`:
+// 8 lanes per row, up to 4 chunks per lane per round, one round of loads for
+// vocabularies up to 32 chunks.  `sink(i, acc)` receives each merged row
+// (called by one lane per row).
+template <typename Want, typename Sink>
+__device__ void merge_rows(const ScanPartial* part, int n_chunks, int r0, int nr, Want want, Sink sink) {
+  constexpr int kLanes = 8;
+  const int tid = threadIdx.x;
+  const int sub = tid % kLanes;
+  for (int i0 = 0; i0 < nr; i0 += kScanThreads / kLanes) {
+    const int i = i0 + tid / kLanes;
+    const bool use = i < nr && want(i);
+    Acc t{kNegInf, INT_MAX, 0.f};
+    for (int c0 = 0; c0 < n_chunks; c0 += 4 * kLanes) {
+      ScanPartial p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + sub + kLanes * u;
+        p[u] = ScanPartial{kNegInf, INT_MAX, 0.f, 0};
+        if (use && c < n_chunks) p[u] = part[(long long)(r0 + i) * n_chunks + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t = merge(t, Acc{p[u].m, p[u].a, p[u].s});
+    }
+    t = lanes_merge<kLanes>(t);
+    if (use && sub == 0) sink(i, t);
+  }
 }
 
 // float64 sum_v exp(l_v - mx) over one row by the whole workgroup.
@@ -137,10 +166,10 @@ __device__ double row_sum_f64(const float* rowp, int vocab, float mx, double* re
   const int tid = threadIdx.x;
   const double m = (double)mx;
   double s = 0.0;
-  for (int v = tid; v < vocab; v += blockDim.x) s += exp((double)rowp[v] - m);
+  for (int v = tid; v < vocab; v += kScanThreads) s += exp((double)rowp[v] - m);
   red[tid] = s;
   __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+  for (int w = kScanThreads / 2; w > 0; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
@@ -149,61 +178,100 @@ __device__ double row_sum_f64(const float* rowp, int vocab, float mx, double* re
   return total;
 }
 
+// Workgroup reductions: wave shuffles, then one LDS slot per wave and a
+// single barrier.  Each call site passes its own slots.
+__device__ inline int block_sum(int v, int* slots) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) t += slots[w];
+  return t;
+}
+
+__device__ inline void block_min2(double& a, double& b, double* slots) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a = fmin(a, __shfl_xor(a, off, 64));
+    b = fmin(b, __shfl_xor(b, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    slots[2 * (threadIdx.x >> 6)] = a;
+    slots[2 * (threadIdx.x >> 6) + 1] = b;
+  }
+  __syncthreads();
+  a = slots[0];
+  b = slots[1];
+#pragma unroll
+  for (int w = 1; w < kScanThreads / 64; ++w) {
+    a = fmin(a, slots[2 * w]);
+    b = fmin(b, slots[2 * w + 1]);
+  }
+}
+
 enum : unsigned char { kInE = 1, kRefined = 2, kNeedRefine = 4 };
 
-__global__ __launch_bounds__(256) void unmask_select_kernel(const UnmaskArgs a) {
-  __shared__ double cf[BC_MAX_BLOCK_ROWS];
-  __shared__ float mrow[BC_MAX_BLOCK_ROWS];
-  __shared__ int tok[BC_MAX_BLOCK_ROWS];
-  __shared__ int rank[BC_MAX_BLOCK_ROWS];
-  __shared__ unsigned char st[BC_MAX_BLOCK_ROWS];
-  __shared__ double red[256];
-  __shared__ int s_nE, s_nA, s_new;
-  __shared__ double s_ck, s_ck1;
+struct SelectSmem {
+  double cf[BC_MAX_BLOCK_ROWS];     // confidence; -inf for rows outside E
+  float mrow[BC_MAX_BLOCK_ROWS];
+  int tok[BC_MAX_BLOCK_ROWS];
+  int rank[BC_MAX_BLOCK_ROWS];
+  unsigned char st[BC_MAX_BLOCK_ROWS];
+  double red[kScanThreads];
+  int cnt[2][kScanThreads / 64];
+  double lohi[2][2 * (kScanThreads / 64)];
+};
 
+// Decisions of block b, one workgroup.  Thread t owns rows t, t + 256, ...
+// after the merge, so only the few workgroup reductions need barriers.
+__global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const UnmaskArgs a) {
+  __shared__ SelectSmem sm;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int r0 = a.blk_off[b];
   const int nb = a.blk_off[b + 1] - r0;
   const double tau = (double)a.threshold;
-  if (tid == 0) { s_nE = 0; s_nA = 0; }
 
-  for (int i = tid; i < nb; i += 256) {
-    const int r = r0 + i;
-    unsigned char f = 0;
-    if (a.masked[r]) {
-      f = kInE;
-      const Acc t = combine_row(a.part, r, a.n_chunks);
-      const double c = 1.0 / (double)t.s;
-      cf[i] = c;
-      tok[i] = t.a;
-      mrow[i] = t.m;
-      if (fabs(c - tau) <= kBand * c) f |= kNeedRefine;
-    }
-    st[i] = f;
+  for (int i = tid; i < nb; i += kScanThreads) {
+    const bool e = a.masked[r0 + i] != 0;
+    sm.st[i] = e ? kInE : 0;
+    sm.cf[i] = -__builtin_huge_val();
   }
   __syncthreads();
+  merge_rows(a.part, a.n_chunks, r0, nb, [&](int i) { return sm.st[i] != 0; },
+             [&](int i, const Acc& t) {
+               const double c = 1.0 / (double)t.s;
+               sm.cf[i] = c;
+               sm.tok[i] = t.a;
+               sm.mrow[i] = t.m;
+               if (fabs(c - tau) <= kBand * c) sm.st[i] |= kNeedRefine;   // threshold inside the band
+             });
+  __syncthreads();
 
-  auto refine_marked = [&]() {
+  // Re-take marked rows in float64; `any` is a workgroup-uniform flag.
+  auto refine_marked = [&](bool any) {
+    if (!any) return;
     for (int i = 0; i < nb; ++i) {
-      if (!(st[i] & kNeedRefine)) continue;      // uniform: st[] is shared
-      const double s = row_sum_f64(a.logits + (long long)(r0 + i) * a.vocab, a.vocab, mrow[i], red);
+      if (!(sm.st[i] & kNeedRefine)) continue;      // uniform: st[] is shared
+      const double s = row_sum_f64(a.logits + (long long)(r0 + i) * a.vocab, a.vocab, sm.mrow[i], sm.red);
       if (tid == 0) {
-        cf[i] = 1.0 / s;
-        st[i] = (unsigned char)((st[i] & ~kNeedRefine) | kRefined);
+        sm.cf[i] = 1.0 / s;
+        sm.st[i] = (unsigned char)((sm.st[i] & ~kNeedRefine) | kRefined);
       }
       __syncthreads();
     }
   };
-  refine_marked();
-
-  for (int i = tid; i < nb; i += 256)
-    if (st[i] & kInE) {
-      atomicAdd(&s_nE, 1);
-      if (cf[i] > tau) atomicAdd(&s_nA, 1);
-    }
-  __syncthreads();
-  const int nE = s_nE, nA = s_nA;
+  int my_mark = 0, my_e = 0, my_a = 0;
+  for (int i = tid; i < nb; i += kScanThreads) {
+    my_mark |= (sm.st[i] & kNeedRefine) != 0;
+    my_e += (sm.st[i] & kInE) != 0;
+  }
+  refine_marked(__syncthreads_or(my_mark));
+  for (int i = tid; i < nb; i += kScanThreads) my_a += (sm.st[i] & kInE) && sm.cf[i] > tau;
+  const int packed = block_sum(my_e | (my_a << 16), sm.cnt[0]);
+  const int nE = packed & 0xffff, nA = packed >> 16;
   int k;
   if (a.mode[b] == BC_UNMASK_SEMI) {
     k = nA;
@@ -215,86 +283,108 @@ __global__ __launch_bounds__(256) void unmask_select_kernel(const UnmaskArgs a) 
   // 0: nothing, 1: all of E, 2: exactly A, 3: top-k by rank
   const int how = k == 0 ? 0 : k == nE ? 1 : k == nA ? 2 : 3;
   if (how == 3) {
+    // Rank with the current confidences; the cut is certain when the lowest
+    // possible value inside the top k exceeds the highest possible value
+    // outside it (refined rows carry no error).  Otherwise re-take the rows
+    // whose error interval reaches across the cut in float64 and rank again.
     for (int guard = 0; guard <= nb; ++guard) {
-      for (int i = tid; i < nb; i += 256) {
-        if (!(st[i] & kInE)) continue;
+      double lo = __builtin_huge_val(), hi_neg = __builtin_huge_val();
+      for (int i = tid; i < nb; i += kScanThreads) {
+        if (!(sm.st[i] & kInE)) continue;
+        const double ci = sm.cf[i];
         int rk = 0;
-        const double ci = cf[i];
-        for (int q = 0; q < nb; ++q)
-          if ((st[q] & kInE) && (cf[q] > ci || (cf[q] == ci && q < i))) ++rk;
-        rank[i] = rk;
+#pragma unroll 8
+        for (int q = 0; q < nb; ++q) {       // rows outside E hold -inf and never count
+          const double cq = sm.cf[q];
+          rk += cq > ci || (cq == ci && q < i);
+        }
+        sm.rank[i] = rk;
+        const double e = (sm.st[i] & kRefined) ? 0.0 : kBand * ci;
+        if (rk < k) lo = fmin(lo, ci - e);
+        else hi_neg = fmin(hi_neg, -(ci + e));
       }
-      __syncthreads();
-      for (int i = tid; i < nb; i += 256) {
-        if (!(st[i] & kInE)) continue;
-        if (rank[i] == k - 1) s_ck = cf[i];
-        if (rank[i] == k) s_ck1 = cf[i];
-      }
-      if (tid == 0) s_new = 0;
-      __syncthreads();
-      const double ck = s_ck, ck1 = s_ck1;
-      for (int i = tid; i < nb; i += 256) {
-        if (!(st[i] & kInE) || (st[i] & kRefined)) continue;
-        const double c = cf[i];
-        if (fabs(c - ck) <= 2.0 * kBand * ck || fabs(c - ck1) <= 2.0 * kBand * ck1) {
-          st[i] |= kNeedRefine;
-          atomicAdd(&s_new, 1);
+      block_min2(lo, hi_neg, sm.lohi[guard & 1]);
+      const double hi = -hi_neg;
+      if (lo > hi) break;
+      int my_new = 0;
+      for (int i = tid; i < nb; i += kScanThreads) {
+        if (!(sm.st[i] & kInE) || (sm.st[i] & kRefined)) continue;
+        const double c = sm.cf[i];
+        const double e = kBand * c;
+        if ((sm.rank[i] < k && c - e <= hi) || (sm.rank[i] >= k && c + e >= lo)) {
+          sm.st[i] |= kNeedRefine;
+          my_new = 1;
         }
       }
-      __syncthreads();
-      if (s_new == 0) break;
-      refine_marked();
+      if (!__syncthreads_or(my_new)) break;   // every row at the cut is exact: ranks decide
+      refine_marked(true);
     }
   }
 
-  for (int i = tid; i < nb; i += 256) {
-    if (!(st[i] & kInE)) continue;
+  for (int i = tid; i < nb; i += kScanThreads) {
+    if (!(sm.st[i] & kInE)) continue;
     const int r = r0 + i;
     bool take = false;
     if (how == 1) take = true;
-    else if (how == 2) take = cf[i] > tau;
-    else if (how == 3) take = rank[i] < k;
+    else if (how == 2) take = sm.cf[i] > tau;
+    else if (how == 3) take = sm.rank[i] < k;
     if (take) {
-      a.tokens[r] = tok[i];
+      a.tokens[r] = sm.tok[i];
       a.masked[r] = 0;
     }
-    if (a.conf) a.conf[r] = (float)cf[i];
+    if (a.conf) a.conf[r] = (float)sm.cf[i];
   }
   if (tid == 0) a.n_commit[b] = k;
 }
 
-__global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a) {
+__global__ __launch_bounds__(kScanThreads) void verify_decide_kernel(const VerifyArgs a) {
   __shared__ int s_k;
+  __shared__ int toks[BC_MAX_SCAN_ROWS];
   const int s = blockIdx.x, tid = threadIdx.x;
   const int f = min(max(a.first[s], 0), a.m);
+  const int last_row = min(a.m, a.n_lrows - 1);     // rows f .. last_row were scanned
+  const int nr = last_row - f + 1;                  // may be 0 (f == m == n_lrows)
   if (tid == 0) s_k = a.m;
+  merge_rows(a.part, a.n_chunks, s * a.n_lrows + f, max(nr, 0), [](int) { return true; },
+             [&](int i, const Acc& t) { toks[i] = t.a; });
   __syncthreads();
-  for (int i = f + tid; i < a.m; i += 256) {
-    const Acc t = combine_row(a.part, s * a.n_lrows + i, a.n_chunks);
-    const bool pass = (a.fixed && a.fixed[(long long)s * a.m + i]) || t.a == a.draft[(long long)s * a.m + i];
-    if (!pass) atomicMin(&s_k, i);
+  for (int i = tid; i < a.m - f; i += kScanThreads) {
+    const int r = f + i;
+    const bool pass = (a.fixed && a.fixed[(long long)s * a.m + r]) || toks[i] == a.draft[(long long)s * a.m + r];
+    if (!pass) atomicMin(&s_k, r);
   }
   __syncthreads();
   if (tid == 0) {
     const int k = s_k;
     a.accept_len[s] = k - f;
-    a.bonus[s] = k < a.n_lrows ? combine_row(a.part, s * a.n_lrows + k, a.n_chunks).a : -1;
+    a.bonus[s] = k < a.n_lrows ? toks[k - f] : -1;
   }
 }
 
 }  // namespace
 
-hipError_t launch_unmask(const UnmaskArgs& a, hipStream_t stream) {
-  const dim3 grid(a.n_chunks, a.n_rows);
-  if (a.vocab % 4 == 0)
-    hipLaunchKernelGGL((scan_kernel<0, true, true>), grid, dim3(kScanThreads), 0, stream, a.logits, a.vocab,
-                       a.n_chunks, a.part, a.masked, nullptr, 0, 0);
+hipError_t launch_scan(const float* logits, int n_rows, int vocab, const uint8_t* row_mask, bool with_sum,
+                       ScanPartial* part, hipStream_t stream) {
+  const dim3 grid(scan_chunks(vocab), n_rows);
+  const int nc = scan_chunks(vocab);
+  const bool vec = vocab % 4 == 0;
+  if (with_sum && vec)
+    hipLaunchKernelGGL((scan_kernel<0, true, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
+                       row_mask, nullptr, 0, 0);
+  else if (with_sum)
+    hipLaunchKernelGGL((scan_kernel<0, true, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
+                       row_mask, nullptr, 0, 0);
+  else if (vec)
+    hipLaunchKernelGGL((scan_kernel<0, false, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
+                       row_mask, nullptr, 0, 0);
   else
-    hipLaunchKernelGGL((scan_kernel<0, true, false>), grid, dim3(kScanThreads), 0, stream, a.logits, a.vocab,
-                       a.n_chunks, a.part, a.masked, nullptr, 0, 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unmask_select_kernel, dim3(a.n_blk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<0, false, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
+                       row_mask, nullptr, 0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask_decide(const UnmaskArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(unmask_decide_kernel, dim3(a.n_blk), dim3(kScanThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -308,7 +398,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
                        a.n_chunks, a.part, nullptr, a.first, a.n_lrows, a.m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_kernel, dim3(a.n_seq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(verify_decide_kernel, dim3(a.n_seq), dim3(kScanThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ extern "C" {
 #define BC_MAX_SEQ 64      /* sequences (or rollouts) per bc_attn_step call */
 #define BC_MAX_BLOCKS 64   /* active blocks per call */
 #define BC_MAX_BLOCK_ROWS 1024 /* rows of one block in bc_unmask_select */
+#define BC_MAX_SCAN_ROWS 4096  /* logit rows per bc_unmask_select / bc_spec_verify call */
 
 typedef enum {
   BC_OK = 0,
@@ -178,7 +179,11 @@ int bc_attn_step(const bc_kv_cache *prefix, const int32_t *prefix_len,
  *   conf    [n_rows] float32 or NULL: confidence of every row masked on
  *           entry (other rows are left untouched)
  *   n_commit [n_blk] int32
- *   ws      at least bc_unmask_workspace_bytes(n_rows, vocab) bytes */
+ *   ws      at least bc_unmask_workspace_bytes(n_rows, vocab) bytes (any
+ *           contents; it holds the per-chunk scan results between the two
+ *           kernels of the call)
+ * Errors: BC_ERR_ARG; BC_ERR_UNSUPPORTED (a block over BC_MAX_BLOCK_ROWS rows,
+ * n_rows over BC_MAX_SCAN_ROWS); BC_ERR_WORKSPACE. */
 size_t bc_unmask_workspace_bytes(int32_t n_rows, int32_t vocab);
 int bc_unmask_select(const float *logits, int32_t n_rows, int32_t vocab,
                      const int32_t *blk_off, int32_t n_blk,
@@ -205,12 +210,48 @@ int bc_unmask_select(const float *logits, int32_t n_rows, int32_t vocab,
  *   fixed    [n_seq][m] uint8 or NULL (scaffold rows, auto-accepted)
  *   first    [n_seq] int32 device, each in [0, m] (clamped to it)
  *   accept_len, bonus  [n_seq] int32
- *   ws       at least bc_verify_workspace_bytes(n_seq, n_lrows, vocab) */
+ *   ws       at least bc_verify_workspace_bytes(n_seq, n_lrows, vocab) bytes
+ *            (any contents).
+ * Errors: BC_ERR_ARG; BC_ERR_UNSUPPORTED (n_seq * n_lrows over
+ * BC_MAX_SCAN_ROWS); BC_ERR_WORKSPACE. */
 size_t bc_verify_workspace_bytes(int32_t n_seq, int32_t n_lrows, int32_t vocab);
 int bc_spec_verify(const float *logits, int32_t n_seq, int32_t n_lrows, int32_t vocab,
                    const int32_t *draft, int32_t m, const uint8_t *fixed,
                    const int32_t *first, int32_t *accept_len, int32_t *bonus,
                    void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sub-steps, exported so that each kernel can be timed or scheduled on its
+ * own.  They take exactly the arguments of the call they make up and must
+ * run on the same stream and workspace, in this order.
+ *
+ * bc_attn_step(args) == bc_attn_partial(args); bc_attn_combine(args).
+ *   The partial pass leaves, per key split, the running max, the softmax
+ *   denominator and the unnormalised output of every row in the workspace;
+ *   the combine pass merges them with log-sum-exp weights into `out`.
+ *
+ * bc_unmask_select(args) == bc_vocab_scan(logits, n_rows, vocab, masked, 1,
+ *   ws, ws_bytes, stream); bc_unmask_decide(args).
+ *   bc_vocab_scan leaves, for every row r with row_mask == NULL or
+ *   row_mask[r] != 0, the max, the lowest argmax and (with_sum != 0) the sum
+ *   of exp(l - max) of each 16384-logit chunk of the row in the workspace
+ *   (sized by bc_unmask_workspace_bytes); bc_unmask_decide merges them and
+ *   takes the decisions.  `masked` must not change between the two. */
+int bc_attn_partial(const bc_kv_cache *prefix, const int32_t *prefix_len,
+                    const bc_kv_cache *priv, const int32_t *priv_len,
+                    const bc_active *a, int32_t mask, float scale, int32_t n_prefix_splits,
+                    void *out, void *ws, size_t ws_bytes, void *stream);
+int bc_attn_combine(const bc_kv_cache *prefix, const int32_t *prefix_len,
+                    const bc_kv_cache *priv, const int32_t *priv_len,
+                    const bc_active *a, int32_t mask, float scale, int32_t n_prefix_splits,
+                    void *out, void *ws, size_t ws_bytes, void *stream);
+int bc_vocab_scan(const float *logits, int32_t n_rows, int32_t vocab, const uint8_t *row_mask,
+                  int32_t with_sum, void *ws, size_t ws_bytes, void *stream);
+int bc_unmask_decide(const float *logits, int32_t n_rows, int32_t vocab,
+                     const int32_t *blk_off, int32_t n_blk,
+                     const int32_t *mode, const int32_t *n_div, float threshold,
+                     uint8_t *masked, int32_t *tokens, float *conf, int32_t *n_commit,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable name of a bc_status value (never NULL). */
 const char *bc_status_str(int status);

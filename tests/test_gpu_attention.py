@@ -160,3 +160,23 @@ def test_workspace_and_argument_errors_before_launch():
                           check=False) == B.BC_ERR_ARG
     assert B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], 7, 0.1, out, ws,
                           check=False) == B.BC_ERR_ARG
+
+
+def test_partial_then_combine_equals_step():
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    seed, S, R, Hq, Hkv, D = 80, 2, 19, 16, 2, 128
+    (pk, pv), _ = synth.kv_cache(seed, S, Hkv, 700, D, [650, 333], "bf16")
+    (q, _), (k, _), (v, _) = synth.active_qkv(seed, S, R, Hq, Hkv, D, "bf16", 0)
+    prefix = B.KVCache(pk.to(G.DEV), pv.to(G.DEV))
+    q, k, v = q.to(G.DEV), k.to(G.DEV), v.to(G.DEV)
+    ws = torch.empty(B.bc_attn_workspace_bytes(prefix, None, (S, R, Hq, D), [0, 7, 19]), dtype=torch.uint8,
+                     device=G.DEV)
+    a = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+    b = torch.empty_like(a)
+    args = (prefix, [650, 333], None, None, q, k, v, [0, 7, 19], CAUSAL, D ** -0.5)
+    B.bc_attn_step(*args, a, ws)
+    B.bc_attn_partial(*args, b, ws)
+    B.bc_attn_combine(*args, b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -29,8 +29,8 @@ def run_gpu(logits, blk_off, mode, n_div, tau, masked, tokens):
     m = G.to_dev(masked.astype(np.uint8))
     t = G.to_dev(tokens.astype(np.int32))
     conf = torch.full((R,), float("nan"), dtype=torch.float32, device=G.DEV)
-    nc = torch.zeros(len(blk_off) - 1, dtype=torch.int32, device=G.DEV)
-    ws = torch.empty(B.bc_unmask_workspace_bytes(R, V), dtype=torch.uint8, device=G.DEV)
+    nc = torch.full((len(blk_off) - 1,), -7, dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(B.bc_unmask_workspace_bytes(R, V), dtype=torch.uint8, device=G.DEV)
     B.bc_unmask_select(lg, blk_off, mode, n_div, tau, m, t, conf, nc, ws)
     torch.cuda.synchronize()
     return m.cpu().numpy(), t.cpu().numpy(), nc.cpu().numpy(), conf.cpu().numpy()
@@ -154,9 +154,72 @@ def test_nothing_masked_and_errors():
     m = G.to_dev(np.ones(4, np.uint8))
     t = G.to_dev(np.zeros(4, np.int32))
     nc = torch.zeros(1, dtype=torch.int32, device=G.DEV)
-    ws = torch.empty(B.bc_unmask_workspace_bytes(4, 64), dtype=torch.uint8, device=G.DEV)
+    ws = torch.zeros(B.bc_unmask_workspace_bytes(4, 64), dtype=torch.uint8, device=G.DEV)
     assert B.bc_unmask_select(lg, [0, 4], [FULL], [0], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
     assert B.bc_unmask_select(lg, [0, 3], [FULL], [1], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
     assert B.bc_unmask_select(lg, [0, 4], [2], [1], 0.9, m, t, None, nc, ws, check=False) == B.BC_ERR_ARG
     assert B.bc_unmask_select(lg, [0, 4], [FULL], [1], 0.9, m, t, None, nc, ws[:8], check=False) \
         == B.BC_ERR_WORKSPACE
+
+
+def test_block_with_nothing_masked_reports_zero():
+    # the middle block has no masked rows: its count must still be written
+    x = synth.logits(9, 12, 3000, 4.0, 0)
+    masked = np.array([1, 0, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1], np.uint8)
+    compare(x, [0, 4, 8, 12], [FULL, FULL, SEMI], [2, 1, 1], 0.9, masked, np.zeros(12, np.int32))
+
+
+def test_one_workspace_across_shapes_and_entry_points():
+    # a workspace zeroed once serves calls of different row counts and vocab
+    # sizes, and a verify call, in any order (the counters sit at a fixed
+    # place and every call leaves them at zero)
+    from oracle import verify as OV
+    ws = torch.zeros(B.bc_unmask_workspace_bytes(64, 151936), dtype=torch.uint8, device=G.DEV)
+    rng = np.random.default_rng(21)
+    for it, (R, V) in enumerate([(12, 151936), (32, 151936), (6, 151936), (64, 5000), (32, 151936),
+                                 (7, 3001), (32, 151936)]):
+        x = synth.logits(21, R, V, 4.0, it)
+        masked = (rng.random(R) < 0.8).astype(np.uint8)
+        m = G.to_dev(masked)
+        t = G.to_dev(np.zeros(R, np.int32))
+        nc = torch.full((2,), -7, dtype=torch.int32, device=G.DEV)
+        half = R // 2
+        B.bc_unmask_select(G.to_dev(x), [0, half, R], [FULL, FULL], [3, 2], 0.9, m, t, None, nc, ws)
+        om, ot, on, _ = OU.unmask_select(x, [0, half, R], [FULL, FULL], [3, 2], np.float32(0.9),
+                                         masked, np.zeros(R, np.int32))
+        assert np.array_equal(m.cpu().numpy(), om) and np.array_equal(t.cpu().numpy(), ot)
+        assert np.array_equal(nc.cpu().numpy(), on)
+        if it % 2 == 1:
+            lg, tg = synth.argmax_planted_logits(21, 24, 151936, 4.0, 0.5, it)
+            d = synth.drafts_with_agreement(21, tg[:23], 0.8, 151936, it)
+            acc = torch.full((1,), -7, dtype=torch.int32, device=G.DEV)
+            bon = torch.full((1,), -7, dtype=torch.int32, device=G.DEV)
+            B.bc_spec_verify(G.to_dev(lg[None]), G.to_dev(d[None]), None,
+                             G.to_dev(np.zeros(1, np.int32)), acc, bon, ws)
+            oa, ob = OV.spec_verify(lg[None], d[None], None, [0])
+            assert int(acc.item()) == int(oa[0]) and int(bon.item()) == int(ob[0])
+
+
+def test_scan_then_decide_equals_select():
+    R, V = 40, 151936
+    x = synth.logits(30, R, V, 4.0, 0)
+    synth.plant_peaks(x, 30, 0.2, 12.0, 0)
+    lg = G.to_dev(x)
+    masked0 = (np.random.default_rng(30).random(R) < 0.75).astype(np.uint8)
+    outs = []
+    for split in (False, True):
+        m = G.to_dev(masked0)
+        t = G.to_dev(np.full(R, -1, np.int32))
+        c = torch.full((R,), float("nan"), dtype=torch.float32, device=G.DEV)
+        nc = torch.full((2,), -7, dtype=torch.int32, device=G.DEV)
+        ws = torch.empty(B.bc_unmask_workspace_bytes(R, V), dtype=torch.uint8, device=G.DEV)
+        args = (lg, [0, 16, R], [FULL, SEMI], [3, 1], 0.9, m, t, c, nc, ws)
+        if split:
+            B.bc_vocab_scan(lg, m, True, ws)
+            B.bc_unmask_decide(*args)
+        else:
+            B.bc_unmask_select(*args)
+        torch.cuda.synchronize()
+        outs.append([z.cpu().numpy() for z in (m, t, c, nc)])
+    for u, w in zip(*outs):
+        assert np.array_equal(u, w, equal_nan=True) if u.dtype.kind == "f" else np.array_equal(u, w)

@@ -20,9 +20,9 @@ def _lib():
 
 def run(logits, draft, fixed, first):
     S, L, V = logits.shape
-    acc = torch.zeros(S, dtype=torch.int32, device=G.DEV)
-    bon = torch.zeros(S, dtype=torch.int32, device=G.DEV)
-    ws = torch.empty(B.bc_verify_workspace_bytes(S, L, V), dtype=torch.uint8, device=G.DEV)
+    acc = torch.full((S,), -7, dtype=torch.int32, device=G.DEV)
+    bon = torch.full((S,), -7, dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(B.bc_verify_workspace_bytes(S, L, V), dtype=torch.uint8, device=G.DEV)
     B.bc_spec_verify(G.to_dev(logits), G.to_dev(draft.astype(np.int32)),
                      None if fixed is None else G.to_dev(fixed.astype(np.uint8)),
                      G.to_dev(np.asarray(first, np.int32)), acc, bon, ws)
@@ -87,5 +87,5 @@ def test_argument_errors():
     d = G.to_dev(np.zeros((1, 5), np.int32))
     f = G.to_dev(np.zeros(1, np.int32))
     a = torch.zeros(1, dtype=torch.int32, device=G.DEV)
-    ws = torch.empty(4096, dtype=torch.uint8, device=G.DEV)
+    ws = torch.zeros(4096, dtype=torch.uint8, device=G.DEV)
     assert B.bc_spec_verify(lg, d, None, f, a, a.clone(), ws, check=False) == B.BC_ERR_ARG  # m > n_lrows
