@@ -110,67 +110,64 @@ def main():
     assert int(dec.masked.sum().item()) == 0, "decode left masked rows"
     assert int((dec.tokens < 0).sum().item()) == 0
 
-    # ---- per-kernel device time: the same decode issued through the
-    # sub-step entry points, each bracketed by HIP events on its stream
-    kinds = ("attn_partial", "attn_combine", "vocab_scan", "unmask_decide", "commit")
-    events = {k: [] for k in kinds}
-    masked_counts = []
-
-    def timed(kind, fn):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        fn()
-        e1.record(stream)
-        events[kind].append((e0, e1))
-
-    def traced_run():
-        length = dec.len0.copy()
-        off = 0
+    # ---- per-kernel launch duration.  The decode is issued once more
+    # through the sub-step entry points, saving the masked rows each scan
+    # sees; then every step's launches of one kernel are captured back to
+    # back in a graph of their own and replayed between two HIP events on
+    # that graph's stream: total / launches is the average launch duration,
+    # with no host gaps and no event between launches.
+    masked_before = []
+    call_args = []
+    length = dec.len0.copy()
+    off = 0
+    with torch.cuda.stream(stream):
         for b, bs in enumerate(dec.blocks):
             masked = dec.masked[off: off + bs]
             tokens = dec.tokens[off: off + bs]
             masked.fill_(1)
             for st in range(dec.steps):
                 q, k, v = dec.qkv[b][st]
-                args = (dec.cache, length, None, None, q, k, v, [0, bs], B.BC_MASK_BLOCK_BIDIR, dec.scale,
-                        dec.out[bs], dec.ws_attn)
-                timed("attn_partial", lambda: B.bc_attn_partial(*args, stream=stream))
-                timed("attn_combine", lambda: B.bc_attn_combine(*args, stream=stream))
-                masked_counts.append(masked.sum())
+                a_args = (dec.cache, length.copy(), None, None, q, k, v, [0, bs], B.BC_MASK_BLOCK_BIDIR,
+                          dec.scale, dec.out[bs], dec.ws_attn)
+                B.bc_attn_partial(*a_args, stream=stream)
+                B.bc_attn_combine(*a_args, stream=stream)
+                masked_before.append(masked.clone())
                 lg = dec.logits[b][st]
-                timed("vocab_scan", lambda: B.bc_vocab_scan(lg, masked, True, dec.ws_unmask, stream=stream))
-                timed("unmask_decide", lambda: B.bc_unmask_decide(
-                    lg, [0, bs], [B.BC_UNMASK_FULL], [dec.steps - st], dec.tau, masked, tokens, dec.conf[:bs],
-                    dec.n_commit[:1], dec.ws_unmask, stream=stream))
+                B.bc_vocab_scan(lg, masked, True, dec.ws_unmask, stream=stream)
+                B.bc_unmask_decide(lg, [0, bs], [B.BC_UNMASK_FULL], [dec.steps - st], dec.tau, masked, tokens,
+                                   dec.conf[:bs], dec.n_commit[:1], dec.ws_unmask, stream=stream)
+                call_args.append((a_args, lg))
             q, k, v = dec.qkv[b][dec.steps - 1]
-            timed("commit", lambda: B.bc_kv_commit(dec.cache, length, 0, int(length[0]), bs, k[0], v[0],
-                                                   stream=stream))
+            B.bc_kv_commit(dec.cache, length, 0, int(length[0]), bs, k[0], v[0], stream=stream)
             off += bs
+    torch.cuda.synchronize()
+    assert int(dec.masked.sum().item()) == 0, "sub-step decode left masked rows"
+    masked_rows = [int(m.sum().item()) for m in masked_before]
 
-    # Queue ~0.1 s of unrelated GPU work first, so that every traced call is
-    # already enqueued when the GPU reaches it: the event pairs then bracket
-    # device time only, not the host's launch overhead.
-    gate_a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
-    gate_b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
-    gate_c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(120):
-            torch.matmul(gate_a, gate_b, out=gate_c)
-        gate_end = torch.cuda.Event(enable_timing=True)
-        gate_end.record(stream)
-        traced_run()
-        trace_end = torch.cuda.Event(enable_timing=True)
-        trace_end.record(stream)
-    torch.cuda.synchronize()
-    dur = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in events.items()}   # microseconds
-    first_pre = events["attn_partial"][0][0]
-    gate_slack_us = gate_end.elapsed_time(first_pre) * 1e3
-    trace_span_us = first_pre.elapsed_time(trace_end) * 1e3
-    del gate_a, gate_b, gate_c
-    masked_rows = [int(x.item()) for x in masked_counts]
-    assert int(dec.masked.sum().item()) == 0, "traced decode left masked rows"
+    def per_launch_us(issue, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            issue()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                issue()
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(call_args))
+
+    avg = {
+        "attn_partial": per_launch_us(lambda: [B.bc_attn_partial(*a, stream=stream) for a, _ in call_args]),
+        "attn_combine": per_launch_us(lambda: [B.bc_attn_combine(*a, stream=stream) for a, _ in call_args]),
+        "vocab_scan": per_launch_us(lambda: [B.bc_vocab_scan(lg, m, True, dec.ws_unmask, stream=stream)
+                                             for (_, lg), m in zip(call_args, masked_before)]),
+    }
 
     # algorithmic work
     Hq, Hkv, D, V = dec.Hq, dec.Hkv, dec.D, dec.V
@@ -183,16 +180,14 @@ def main():
             attn_flops += f_
             partial_bytes += b_ - bs * Hq * D * 2       # K/V and Q; the output is the combine's
         length += bs
-    avg = {k: float(np.mean(v)) for k, v in dur.items()}
-    n_attn = len(dur["attn_partial"])
+    n_attn = len(call_args)
     attn_us = avg["attn_partial"] + avg["attn_combine"]
     attn_gbs = attn_bytes / n_attn / (attn_us * 1e-6) / 1e9
     attn_tflops = attn_flops / n_attn / (attn_us * 1e-6) / 1e12
     scan_bytes = sum(4 * V * r for r in masked_rows)
-    n_scan = len(dur["vocab_scan"])
+    n_scan = len(masked_rows)
     scan_gbs = scan_bytes / n_scan / (avg["vocab_scan"] * 1e-6) / 1e9
-    unmask_us = avg["vocab_scan"] + avg["unmask_decide"]
-    tot = {k: float(np.sum(v)) for k, v in dur.items()}
+    tot = {k: v * n_attn for k, v in avg.items()}
     dominant = max(("attn_partial", "vocab_scan"), key=tot.get)
     if dominant == "vocab_scan":
         roof = {"kernel": "scan_kernel (bc_vocab_scan: per-row max/argmax/exp-sum over the vocabulary)",
@@ -231,11 +226,9 @@ def main():
                  "TFLOP_s": round(attn_tflops, 3), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 5),
                  "bytes_per_call": attn_bytes / n_attn, "flops_per_call": attn_flops / n_attn},
-        "unmask": {"avg_us": round(unmask_us, 3), "scan_GB_s": round(scan_gbs, 1),
+        "unmask": {"scan_us": round(avg["vocab_scan"], 3), "scan_GB_s": round(scan_gbs, 1),
                    "avg_masked_rows": float(np.mean(masked_rows))},
         "kernel_avg_us": kernel_us,
-        "trace": {"span_us": round(trace_span_us, 1), "kernels_us": round(sum(tot.values()), 1),
-                  "gate_to_first_call_us": round(gate_slack_us, 2)},
         "roofline": roof,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 2),

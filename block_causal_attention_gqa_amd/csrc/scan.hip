@@ -234,20 +234,24 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   const int nb = a.blk_off[b + 1] - r0;
   const double tau = (double)a.threshold;
 
-  for (int i = tid; i < nb; i += kScanThreads) {
-    const bool e = a.masked[r0 + i] != 0;
-    sm.st[i] = e ? kInE : 0;
-    sm.cf[i] = -__builtin_huge_val();
-  }
-  __syncthreads();
-  merge_rows(a.part, a.n_chunks, r0, nb, [&](int i) { return sm.st[i] != 0; },
+  // The masked flags and the chunk partials of every row are read in one
+  // round: partials of revealed rows were not written by the scan and are
+  // dropped below.
+  for (int i = tid; i < nb; i += kScanThreads) sm.st[i] = a.masked[r0 + i] != 0 ? kInE : 0;
+  merge_rows(a.part, a.n_chunks, r0, nb, [](int) { return true; },
              [&](int i, const Acc& t) {
-               const double c = 1.0 / (double)t.s;
-               sm.cf[i] = c;
+               sm.cf[i] = 1.0 / (double)t.s;
                sm.tok[i] = t.a;
                sm.mrow[i] = t.m;
-               if (fabs(c - tau) <= kBand * c) sm.st[i] |= kNeedRefine;   // threshold inside the band
              });
+  __syncthreads();
+  for (int i = tid; i < nb; i += kScanThreads) {
+    if (!(sm.st[i] & kInE)) {
+      sm.cf[i] = -__builtin_huge_val();
+    } else if (fabs(sm.cf[i] - tau) <= kBand * sm.cf[i]) {
+      sm.st[i] |= kNeedRefine;   // threshold decision inside the band
+    }
+  }
   __syncthreads();
 
   // Re-take marked rows in float64; `any` is a workgroup-uniform flag.
