@@ -168,7 +168,7 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   if (st) return st;
   if (!prefix_len || !out || (priv && !priv_len)) return BC_ERR_ARG;
   if (mask != BC_MASK_BLOCK_BIDIR && mask != BC_MASK_BLOCK_CAUSAL) return BC_ERR_ARG;
-  if (!std::isfinite(scale)) return BC_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return BC_ERR_ARG;
   for (int s = 0; s < prefix->n_seq; ++s)
     if (prefix_len[s] < 0 || prefix_len[s] > prefix->capacity) return BC_ERR_ARG;
   if (priv)

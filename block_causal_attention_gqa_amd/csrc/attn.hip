@@ -62,6 +62,12 @@ template <int D> struct Cfg<float, D> {
 
 __device__ inline float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// x when keep, else zero -- component-wise, so no aggregate select (which
+// the compiler lowers through stack memory)
+__device__ inline uint4 keep_or_zero(bool keep, const uint4& x) {
+  return uint4{keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u};
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
 // every outstanding global load of the wave, which would stall on the next
 // key tile's prefetch; here only LDS traffic is drained before the barrier.
@@ -84,7 +90,8 @@ __device__ inline int key_pos(int t, int jj, int i) {
 }
 
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_partial_kernel(const AttnArgs a) {
   using C = Cfg<T, D>;
   constexpr int NT = NW * 64;                 // threads
   constexpr int kTileRows = NW * kAttnRowsPerWave;
@@ -175,38 +182,61 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // row pointer of key `key` of this item (K or V)
-  auto key_row = [&](int key, bool want_v) -> const T* {
-    if (is_prefix) return (want_v ? vbase : kbase) + (long long)key * D;
-    if (key < lv) {
-      const T* base = static_cast<const T*>(want_v ? a.vv : a.vk);
-      return base + s_act * a.v_seq_stride + g * a.v_head_stride + (long long)key * D;
+  // ---- the item's keys as at most two contiguous segments, each read from
+  // one base pointer: the prefix chunk; or the rollout's private keys, then
+  // the active keys (the only segment the block predicate applies to).
+  const T *seg0_k, *seg0_v, *seg1_k = nullptr, *seg1_v = nullptr;
+  int seg0_n, seg1_n = 0;
+  bool seg0_masked;
+  if (is_prefix) {
+    seg0_k = kbase + (long long)key_begin * D;
+    seg0_v = vbase + (long long)key_begin * D;
+    seg0_n = max(0, key_end - key_begin);
+    seg0_masked = false;
+  } else {
+    const long long act_off = (long long)(s_act * a.Hkv + g) * a.R * D;
+    const T* ak = static_cast<const T*>(a.ak) + act_off;
+    const T* av = static_cast<const T*>(a.av) + act_off;
+    if (lv > 0) {
+      const long long prv_off = s_act * a.v_seq_stride + g * a.v_head_stride;
+      seg0_k = static_cast<const T*>(a.vk) + prv_off;
+      seg0_v = static_cast<const T*>(a.vv) + prv_off;
+      seg0_n = lv;
+      seg0_masked = false;
+      seg1_k = ak;
+      seg1_v = av;
+      seg1_n = a.R;
+    } else {
+      seg0_k = ak;
+      seg0_v = av;
+      seg0_n = a.R;
+      seg0_masked = true;
     }
-    const T* base = static_cast<const T*>(want_v ? a.av : a.ak);
-    return base + ((long long)(s_act * a.Hkv + g) * a.R + (key - lv)) * D;
-  };
+  }
 
   // ---- register staging of one key tile: the next tile's global loads are
   // issued before the current tile is computed, so HBM latency is paid once.
+  // Loads are clamped to the segment's last key and zeroed past its end, so
+  // they need no branches.
   constexpr int CPR = kBf16 ? D / 8 : D / 4;           // 16-byte units per key row
+  constexpr int EPU = kBf16 ? 8 : 4;                   // elements per 16-byte unit
   constexpr int NK = (KT * CPR + NT - 1) / NT;         // K units per thread
   constexpr int NVQ = ((KT / 4) * CPR + NT - 1) / NT;  // bf16: 4-key quads per thread
   constexpr int NV = kBf16 ? 4 * NVQ : NK;             // V units per thread
   uint4 kreg[NK], vreg[NV];
 
-  auto load_tile = [&](int kb) {
+  auto load_tile = [&](const T* kp, const T* vp, int nkeys, int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int idx = tid + NT * u;
       const int kr = idx / CPR, cc = idx - kr * CPR;
       const int key = kb + kr;
-      kreg[u] = uint4{0u, 0u, 0u, 0u};
-      if (idx < KT * CPR && key < key_end)
-        kreg[u] = *reinterpret_cast<const uint4*>(key_row(key, false) + (kBf16 ? 8 : 4) * cc);
+      const long long off = (long long)min(key, nkeys - 1) * D + EPU * cc;
+      const uint4 kx = *reinterpret_cast<const uint4*>(kp + off);
+      kreg[u] = keep_or_zero(key < nkeys, kx);
       if constexpr (!kBf16) {
-        vreg[u] = uint4{0u, 0u, 0u, 0u};
-        if (idx < KT * CPR && key < key_end)
-          vreg[u] = *reinterpret_cast<const uint4*>(key_row(key, true) + 4 * cc);
+        const uint4 vx = *reinterpret_cast<const uint4*>(vp + off);
+        vreg[u] = keep_or_zero(key < nkeys, vx);
       }
     }
     if constexpr (kBf16) {
@@ -214,18 +244,19 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
       for (int u = 0; u < NVQ; ++u) {
         const int idx = tid + NT * u;
         const int qd = idx % (KT / 4), cc = idx / (KT / 4);
+        const bool in_tile = idx < (KT / 4) * CPR;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb + 4 * qd + i;
-          vreg[4 * u + i] = uint4{0u, 0u, 0u, 0u};
-          if (idx < (KT / 4) * CPR && key < key_end)
-            vreg[4 * u + i] = *reinterpret_cast<const uint4*>(key_row(key, true) + 8 * cc);
+          const long long off = (long long)min(key, nkeys - 1) * D + 8 * min(cc, CPR - 1);
+          const uint4 vx = *reinterpret_cast<const uint4*>(vp + off);
+          vreg[4 * u + i] = keep_or_zero(in_tile && key < nkeys, vx);
         }
       }
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int idx = tid + NT * u;
@@ -262,13 +293,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
     }
   };
 
-  if (key_begin < key_end) load_tile(key_begin);
-  for (int kb = key_begin; kb < key_end; kb += KT) {
-    lds_barrier();             // the previous tile's LDS reads are complete
-    store_tile();
-    if (kb + KT < key_end) load_tile(kb + KT);
-    lds_barrier();
-
+  // one 64-key tile: keys kb .. kb + 63 of a segment of nkeys keys
+  auto process_tile = [&](int kb, int nkeys, bool masked) __attribute__((always_inline)) {
     // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
     f32x4 st[2][4];
 #pragma unroll
@@ -278,14 +304,17 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (kBf16) {
+        // all A operands of the 16-key tile first, so the LDS reads overlap
         const int krow = 32 * (t >> 1) + 8 * (n >> 2) + 4 * (t & 1) + (n & 3);
+        bf16x8 ka[D / 32];
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&k_lds[krow * C::KP + 32 * kk + 8 * jj]);
+        for (int kk = 0; kk < D / 32; ++kk)
+          ka[kk] = *reinterpret_cast<const bf16x8*>(&k_lds[krow * C::KP + 32 * kk + 8 * jj]);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[c][kk], st[c][t], 0, 0, 0);
-        }
+            st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[c][kk], st[c][t], 0, 0, 0);
       } else {
 #pragma unroll
         for (int kk = 0; kk < D / 4; ++kk) {
@@ -298,8 +327,11 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
     }
 
     // ---- online softmax, one query column per lane and column tile
-    // a prefix tile inside its key range is fully visible: no predicate
-    const bool full_tile = is_prefix && kb + KT <= key_end;
+    // a tile inside an unmasked segment is fully visible: no predicate.
+    // Scores stay unscaled here (scale > 0 keeps their order); the scale is
+    // applied inside the exponent, p = 2^(x * scale * log2 e - m).
+    const bool full_tile = !masked && kb + KT <= nkeys;
+    const float sl2 = a.scale_log2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float tmax = kNegInf;
@@ -307,26 +339,22 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = st[c][t][i] * a.scale_log2;
-            st[c][t][i] = x;
-            tmax = fmaxf(tmax, x);
-          }
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kb + key_pos<T>(t, jj, i);
-            const bool vis = key < key_end && (is_prefix || key < lv || key - lv < lim[c]);
-            const float x = vis ? st[c][t][i] * a.scale_log2 : kNegInf;
+            const bool vis = key < nkeys && (!masked || key < lim[c]);
+            const float x = vis ? st[c][t][i] : kNegInf;
             st[c][t][i] = x;
             tmax = fmaxf(tmax, x);
           }
       }
       tmax = fmaxf(tmax, wave_xor(tmax, 16));
       tmax = fmaxf(tmax, wave_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[c], tmax);
+      const float mnew = fmaxf(m_run[c], tmax * sl2);        // running max, scaled
       const float muse = mnew == kNegInf ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(m_run[c] - muse);
       float psum = 0.f;
@@ -334,7 +362,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(st[c][t][i] - muse);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse));
           st[c][t][i] = p;
           psum += p;
         }
@@ -359,14 +387,23 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
             pb[c][ks][e + 4] = (__bf16)st[c][2 * ks + 1][e];
           }
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
+      for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
+        // A operands of four 16-dim tiles first, then their MFMAs
+        bf16x8 va[4][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&v_lds[(16 * dt + n) * C::VP + 32 * ks + 8 * jj]);
+        for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[c][ks], o[c][dt], 0, 0, 0);
-        }
+          for (int ks = 0; ks < 2; ++ks)
+            va[d4][ks] = *reinterpret_cast<const bf16x8*>(
+                &v_lds[(16 * (dt0 + d4) + n) * C::VP + 32 * ks + 8 * jj]);
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              o[c][dt0 + d4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d4][ks], pb[c][ks], o[c][dt0 + d4], 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
@@ -379,6 +416,23 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_kernel(const AttnArgs a)
             for (int c = 0; c < 2; ++c)
               o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, st[c][t][i], o[c][dt], 0, 0, 0);
           }
+    }
+  };
+
+  // ---- stream the segments' key tiles through LDS (one code path for both)
+  for (int sgi = 0; sgi < 2; ++sgi) {
+    const T* kp = sgi ? seg1_k : seg0_k;
+    const T* vp = sgi ? seg1_v : seg0_v;
+    const int nkeys = sgi ? seg1_n : seg0_n;
+    const bool masked = sgi ? true : seg0_masked;
+    if (nkeys <= 0) continue;
+    load_tile(kp, vp, nkeys, 0);
+    for (int kb = 0; kb < nkeys; kb += KT) {
+      lds_barrier();           // the previous tile's LDS reads are complete
+      store_tile();
+      if (kb + KT < nkeys) load_tile(kp, vp, nkeys, kb + KT);
+      lds_barrier();
+      process_tile(kb, nkeys, masked);
     }
   }
 

@@ -136,7 +136,7 @@ int bc_kv_commit(const bc_kv_cache *cache, int32_t *len, int32_t seq, int32_t st
  *   priv        NULL, or each rollout's private cache (n_seq == a->n_seq).
  *   priv_len    HOST [a->n_seq] when priv != NULL.
  *   mask        bc_mask.
- *   scale       softmax scale, normally 1 / sqrt(head_dim).
+ *   scale       softmax scale (finite, > 0), normally 1 / sqrt(head_dim).
  *   n_prefix_splits  0 = automatic; otherwise the number of key chunks the
  *               prefix is cut into (1 .. 256), for tuning and tests.
  *   out         [n_seq][n_rows][n_q_heads][head_dim] in the q dtype.
