@@ -12,7 +12,7 @@
 // is (sequence, active row, query head within the GQA group), so one K/V
 // stream serves all `group` query heads.  A workgroup (2 or 4 waves x 32
 // rows) takes one row tile against one key range and writes an unnormalised
-// partial (running max, sum, output) to its slot:
+// partial (reference max, sum, output) to its slot:
 //   * prefix items: slot p < P covers chunk p of the committed prefix; under
 //     a fork the tile runs over the rows of ALL rollouts, so the shared prefix
 //     is streamed once per tile instead of once per rollout;
@@ -29,49 +29,80 @@
 // of the four 16-key tiles permuted so that tile pair (2s, 2s+1) gives lane
 // group jj the keys 32s + 8jj .. 32s + 8jj + 7, the probabilities P^T are
 // already laid out as the B operand of O^T = V^T P^T, so they never leave the
-// registers.  V^T is staged in LDS transposed (V is stored [key][dim] in HBM).
-// The per-column softmax scalars (max, rescale) are per lane.  fp32 inputs
-// use v_mfma_f32_16x16x4_f32 with the same structure.
+// registers.  The per-column softmax scalars (max, rescale) are per lane.
+//
+// Data movement (bf16).  K and V tiles of 64 keys go from HBM straight into
+// LDS with buffer loads that write LDS (no staging registers), 1 KB per wave
+// instruction, double-buffered so the next tile is in flight while the
+// current one is computed; one barrier per tile.  Rows past a segment's end
+// fall outside the buffer's record range and arrive as zeros.  Both tiles
+// stay [key][dim] in LDS with a 16-byte-chunk XOR swizzle per row; K operands
+// are plain 16-byte reads, V^T operands come from the transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of one dim.
+// fp32 inputs (small configurations) use v_mfma_f32_16x16x4_f32 with
+// register-staged tiles and the same softmax.
 
 #include <type_traits>
 
 #include "bc_internal.h"
 
+#define BC_LDS __attribute__((address_space(3)))
+
 namespace bc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;   // raw bf16 storage
 
 constexpr float kNegInf = -__builtin_huge_valf();
-
-template <typename T, int D> struct Cfg;
-template <int D> struct Cfg<bf16_t, D> {
-  static constexpr int KP = D + 8;                 // K row pitch (elements)
-  static constexpr int VP = kAttnKeyTile + 8;      // V^T row pitch (elements)
-  static constexpr int K_ELEMS = kAttnKeyTile * KP;
-  static constexpr int V_ELEMS = D * VP;
-};
-template <int D> struct Cfg<float, D> {
-  static constexpr int KP = D + 4;
-  static constexpr int VP = D + 4;                 // V kept [key][dim]
-  static constexpr int K_ELEMS = kAttnKeyTile * KP;
-  static constexpr int V_ELEMS = kAttnKeyTile * VP;
-};
+// probabilities are allowed up to 2^kRescaleSlack before the reference max moves
+constexpr float kRescaleSlack = 8.f;
+// buffer descriptor word 3 for raw (untyped, stride 0) buffers on the gfx9 family
+constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ inline float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
-
-// x when keep, else zero -- component-wise, so no aggregate select (which
-// the compiler lowers through stack memory)
-__device__ inline uint4 keep_or_zero(bool keep, const uint4& x) {
-  return uint4{keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u};
-}
 
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
 // every outstanding global load of the wave, which would stall on the next
 // key tile's prefetch; here only LDS traffic is drained before the barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One buffer-to-LDS load: every lane fetches the 16 bytes at byte offset
+// voff of the buffer described by rsrc and writes them to LDS at byte
+// lds + 16 * lane.  Inline assembly keeps the load out of the compiler's
+// wait-count bookkeeping, which would otherwise make the reads of the stage
+// being computed wait for the loads filling the other stage; completion is
+// awaited explicitly by dma_barrier().  Extra untracked loads only make the
+// compiler's own (in-order) vmcnt waits stricter.
+__device__ inline void buffer_load_lds16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// raw buffer descriptor: base, stride 0, num_records bytes (reads past it
+// return zero)
+__device__ inline u32x4 raw_buffer(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kRawBufferWord3};
+}
+
+__device__ inline uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((BC_LDS const uint8_t*)p);
+}
+
+// Barrier after this wave's buffer-to-LDS loads have landed: once every wave
+// passes it, the tile written by all waves is visible to all of them.
+// The wait is the compiler builtin (encoding: vmcnt 0, expcnt and lgkmcnt
+// unconstrained) so that the compiler's own bookkeeping knows every earlier
+// vector-memory load, e.g. of the Q operand, has completed there.
+__device__ inline void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map
 // hardware id -> logical id so that consecutive logical ids (the row tiles
@@ -83,70 +114,103 @@ __device__ inline int xcd_remap(int hw, int n) {
 }
 
 // position inside the 64-key tile of the value held in C-register i of tile t
-template <typename T>
+template <bool kBf16>
 __device__ inline int key_pos(int t, int jj, int i) {
-  if constexpr (sizeof(T) == 2) return 32 * (t >> 1) + 8 * jj + 4 * (t & 1) + i;
+  if constexpr (kBf16) return 32 * (t >> 1) + 8 * jj + 4 * (t & 1) + i;
   else return 16 * t + 4 * jj + i;
 }
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_partial_kernel(const AttnArgs a) {
-  using C = Cfg<T, D>;
-  constexpr int NT = NW * 64;                 // threads
-  constexpr int kTileRows = NW * kAttnRowsPerWave;
-  constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int KT = kAttnKeyTile;
-  __shared__ __attribute__((aligned(16))) T k_lds[C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) T v_lds[C::V_ELEMS];
+// 16-byte chunk swizzles of the bf16 K and V tiles in LDS (row r of a tile,
+// D / 8 chunks per row; chunk c of row r is stored at position c ^ swz(r)).
+// swz_k spreads the 16 rows one K operand read touches (row bits 0, 1, 3, 4)
+// over distinct chunk positions; swz_v does the same for the 4 rows x 32
+// bytes per 16 lanes of a transposing V read (row bits 0, 1, 3).  Neither
+// depends on row bits 2 and 5, so the per-tile row offsets of the reads stay
+// immediates.
+template <int D> __device__ inline int swz_k(int r) {
+  if constexpr (D == 128) return (r & 3) | ((r >> 1) & 12);
+  else return ((r >> 1) & 1) | ((r >> 2) & 6);
+}
+template <int D> __device__ inline int swz_v(int r) {
+  if constexpr (D == 128) return ((r & 3) | ((r >> 1) & 4)) << 1;
+  else return (((r >> 1) & 1) | ((r >> 2) & 2)) << 1;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, jj = lane >> 4;
+// ---- what one workgroup computes: its row tile, slot and key segments
+template <typename T>
+struct Item {
+  int g, mt, slot, s_item, rows_in_group;
+  // the item's keys as at most two contiguous segments: the prefix chunk; or
+  // the rollout's private keys, then the active keys (the only segment the
+  // block predicate applies to)
+  const T *k0, *v0, *k1, *v1;
+  int n0, n1;
+  bool masked0;
+};
 
-  // ---- which item this workgroup computes
-  const int item = xcd_remap(blockIdx.x, a.n_items);
-  const bool is_prefix = item < a.n_prefix_items;
-  int g, mt, slot, s_item, rows_in_group, key_begin, key_end, lv = 0;
-  const T* kbase = nullptr;   // prefix items: row 0 of the (seq, kv head) cache
-  const T* vbase = nullptr;
-  if (is_prefix) {
-    mt = item % a.n_mt_prefix;
+template <typename T>
+__device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
+  Item<T> it;
+  it.k1 = it.v1 = nullptr;
+  it.n1 = 0;
+  it.masked0 = false;
+  if (item < a.n_prefix_items) {
+    it.mt = item % a.n_mt_prefix;
     const int rest = item / a.n_mt_prefix;
-    slot = rest % a.n_splits;
+    it.slot = rest % a.n_splits;
     const int grp = rest / a.n_splits;
     int ps;
-    if (a.fork) { g = grp; s_item = -1; ps = 0; rows_in_group = a.S * a.R * a.group; }
-    else { g = grp % a.Hkv; s_item = grp / a.Hkv; ps = s_item; rows_in_group = a.R * a.group; }
-    key_begin = slot * a.chunk[ps];
-    key_end = min(a.prefix_len[ps], key_begin + a.chunk[ps]);
-    const long long off = ps * a.p_seq_stride + g * a.p_head_stride;
-    kbase = static_cast<const T*>(a.pk) + off;
-    vbase = static_cast<const T*>(a.pv) + off;
+    if (a.fork) { it.g = grp; it.s_item = -1; ps = 0; it.rows_in_group = a.S * a.R * a.group; }
+    else { it.g = grp % a.Hkv; it.s_item = grp / a.Hkv; ps = it.s_item; it.rows_in_group = a.R * a.group; }
+    const int key_begin = it.slot * a.chunk[ps];
+    const int key_end = min(a.prefix_len[ps], key_begin + a.chunk[ps]);
+    const long long off = ps * a.p_seq_stride + it.g * a.p_head_stride + (long long)key_begin * a.D;
+    it.k0 = static_cast<const T*>(a.pk) + off;
+    it.v0 = static_cast<const T*>(a.pv) + off;
+    it.n0 = max(0, key_end - key_begin);
   } else {
-    const int it = item - a.n_prefix_items;
-    mt = it % a.n_mt_active;
-    const int rest = it / a.n_mt_active;
-    g = rest % a.Hkv;
-    s_item = rest / a.Hkv;
-    slot = a.n_splits;
-    rows_in_group = a.R * a.group;
-    lv = a.fork ? a.priv_len[s_item] : 0;
-    key_begin = 0;
-    key_end = lv + a.R;
+    const int i2 = item - a.n_prefix_items;
+    it.mt = i2 % a.n_mt_active;
+    const int rest = i2 / a.n_mt_active;
+    it.g = rest % a.Hkv;
+    it.s_item = rest / a.Hkv;
+    it.slot = a.n_splits;
+    it.rows_in_group = a.R * a.group;
+    const int lv = a.fork ? a.priv_len[it.s_item] : 0;
+    const long long act_off = (long long)(it.s_item * a.Hkv + it.g) * a.R * a.D;
+    const T* ak = static_cast<const T*>(a.ak) + act_off;
+    const T* av = static_cast<const T*>(a.av) + act_off;
+    if (lv > 0) {
+      const long long prv_off = it.s_item * a.v_seq_stride + it.g * a.v_head_stride;
+      it.k0 = static_cast<const T*>(a.vk) + prv_off;
+      it.v0 = static_cast<const T*>(a.vv) + prv_off;
+      it.n0 = lv;
+      it.k1 = ak;
+      it.v1 = av;
+      it.n1 = a.R;
+    } else {
+      it.k0 = ak;
+      it.v0 = av;
+      it.n0 = a.R;
+      it.masked0 = true;
+    }
   }
+  return it;
+}
 
-  // ---- this lane's two query columns
-  bool valid[2];
-  int orow[2], lim[2];
+// this lane's two query columns: validity, output row, and the end of the
+// active keys it may see
+template <typename T>
+__device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0, int n, bool (&valid)[2],
+                                 int (&orow)[2], int (&lim)[2]) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int m = mt * kTileRows + wave * kAttnRowsPerWave + c * 16 + n;
-    valid[c] = m < rows_in_group;
-    int s = s_item, rem = m;
-    if (s_item < 0) { s = m / (a.R * a.group); rem = m - s * (a.R * a.group); }
+    const int m = row0 + c * 16 + n;
+    valid[c] = m < it.rows_in_group;
+    int s = it.s_item, rem = m;
+    if (it.s_item < 0) { s = m / (a.R * a.group); rem = m - s * (a.R * a.group); }
     const int r = rem / a.group, hh = rem - r * a.group;
-    orow[c] = valid[c] ? (s * a.R + r) * a.Hq + g * a.group + hh : 0;
+    orow[c] = valid[c] ? (s * a.R + r) * a.Hq + it.g * a.group + hh : 0;
     int l = r + 1;
     if (!a.causal) {
       l = a.R;
@@ -155,288 +219,72 @@ void attn_partial_kernel(const AttnArgs a) {
     }
     lim[c] = l;
   }
-  const int s_act = s_item;   // active items: the sequence whose private/active keys are read
+}
 
-  // ---- Q^T operand, resident for the whole item
-  const T* q = static_cast<const T*>(a.q);
-  constexpr int QK = kBf16 ? D / 32 : D / 4;
-  using QOp = typename std::conditional<kBf16, bf16x8, float>::type;
-  QOp qop[2][QK];
+// Online softmax over one 64-key tile held transposed in st (raw scores,
+// one query column per lane and column tile); leaves the probabilities in st
+// and rescales o when a column's reference max moves.  A tile inside an
+// unmasked segment is fully visible: no predicate.  The scale is applied in
+// the exponent, p = 2^(x * scale * log2 e - m) (scale > 0 keeps the order).
+// Lazy rescale: the reference max only moves when the tile's max exceeds it
+// by more than kRescaleSlack (log2 units), so after the first tiles the
+// accumulator is almost never rescaled; probabilities stay below
+// 2^kRescaleSlack and o, l and m stay consistent, so o / l is unchanged.
+template <bool kBf16, int D>
+__device__ inline void softmax_tile(f32x4 (&st)[2][4], f32x4 (&o)[2][D / 16], float (&m_run)[2],
+                                    float (&l_run)[2], const int (&lim)[2], int jj, int kb, int nkeys,
+                                    bool masked, float sl2) {
+  const bool full_tile = !masked && kb + kAttnKeyTile <= nkeys;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < 2; ++c) {
+    float tmax = kNegInf;
+    if (full_tile) {
 #pragma unroll
-    for (int kk = 0; kk < QK; ++kk) {
-      if constexpr (kBf16) {
-        bf16x8 z = {};
-        qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
-      } else {
-        qop[c][kk] = valid[c] ? q[(long long)orow[c] * D + 4 * kk + jj] : 0.f;
-      }
-    }
-
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 o[2][D / 16];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- the item's keys as at most two contiguous segments, each read from
-  // one base pointer: the prefix chunk; or the rollout's private keys, then
-  // the active keys (the only segment the block predicate applies to).
-  const T *seg0_k, *seg0_v, *seg1_k = nullptr, *seg1_v = nullptr;
-  int seg0_n, seg1_n = 0;
-  bool seg0_masked;
-  if (is_prefix) {
-    seg0_k = kbase + (long long)key_begin * D;
-    seg0_v = vbase + (long long)key_begin * D;
-    seg0_n = max(0, key_end - key_begin);
-    seg0_masked = false;
-  } else {
-    const long long act_off = (long long)(s_act * a.Hkv + g) * a.R * D;
-    const T* ak = static_cast<const T*>(a.ak) + act_off;
-    const T* av = static_cast<const T*>(a.av) + act_off;
-    if (lv > 0) {
-      const long long prv_off = s_act * a.v_seq_stride + g * a.v_head_stride;
-      seg0_k = static_cast<const T*>(a.vk) + prv_off;
-      seg0_v = static_cast<const T*>(a.vv) + prv_off;
-      seg0_n = lv;
-      seg0_masked = false;
-      seg1_k = ak;
-      seg1_v = av;
-      seg1_n = a.R;
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
     } else {
-      seg0_k = ak;
-      seg0_v = av;
-      seg0_n = a.R;
-      seg0_masked = true;
-    }
-  }
-
-  // ---- register staging of one key tile: the next tile's global loads are
-  // issued before the current tile is computed, so HBM latency is paid once.
-  // Loads are clamped to the segment's last key and zeroed past its end, so
-  // they need no branches.
-  constexpr int CPR = kBf16 ? D / 8 : D / 4;           // 16-byte units per key row
-  constexpr int EPU = kBf16 ? 8 : 4;                   // elements per 16-byte unit
-  constexpr int NK = (KT * CPR + NT - 1) / NT;         // K units per thread
-  constexpr int NVQ = ((KT / 4) * CPR + NT - 1) / NT;  // bf16: 4-key quads per thread
-  constexpr int NV = kBf16 ? 4 * NVQ : NK;             // V units per thread
-  uint4 kreg[NK], vreg[NV];
-
-  auto load_tile = [&](const T* kp, const T* vp, int nkeys, int kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int idx = tid + NT * u;
-      const int kr = idx / CPR, cc = idx - kr * CPR;
-      const int key = kb + kr;
-      const long long off = (long long)min(key, nkeys - 1) * D + EPU * cc;
-      const uint4 kx = *reinterpret_cast<const uint4*>(kp + off);
-      kreg[u] = keep_or_zero(key < nkeys, kx);
-      if constexpr (!kBf16) {
-        const uint4 vx = *reinterpret_cast<const uint4*>(vp + off);
-        vreg[u] = keep_or_zero(key < nkeys, vx);
-      }
-    }
-    if constexpr (kBf16) {
-#pragma unroll
-      for (int u = 0; u < NVQ; ++u) {
-        const int idx = tid + NT * u;
-        const int qd = idx % (KT / 4), cc = idx / (KT / 4);
-        const bool in_tile = idx < (KT / 4) * CPR;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 4 * qd + i;
-          const long long off = (long long)min(key, nkeys - 1) * D + 8 * min(cc, CPR - 1);
-          const uint4 vx = *reinterpret_cast<const uint4*>(vp + off);
-          vreg[4 * u + i] = keep_or_zero(in_tile && key < nkeys, vx);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int idx = tid + NT * u;
-      if (idx >= KT * CPR) continue;
-      const int kr = idx / CPR, cc = idx - kr * CPR;
-      if constexpr (kBf16) {
-        *reinterpret_cast<uint4*>(&k_lds[kr * C::KP + 8 * cc]) = kreg[u];
-      } else {
-        *reinterpret_cast<uint4*>(&k_lds[kr * C::KP + 4 * cc]) = kreg[u];
-        *reinterpret_cast<uint4*>(&v_lds[kr * C::VP + 4 * cc]) = vreg[u];
-      }
-    }
-    if constexpr (kBf16) {
-      // V transposed: 4 consecutive keys x 8 dims -> 8 rows of V^T, 4 keys each
-#pragma unroll
-      for (int u = 0; u < NVQ; ++u) {
-        const int idx = tid + NT * u;
-        if (idx >= (KT / 4) * CPR) continue;
-        const int qd = idx % (KT / 4), cc = idx / (KT / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sh = (e & 1) * 16;
-          const int w = e >> 1;
-          auto pick = [&](const uint4& x) -> uint32_t {
-            const uint32_t word = w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w;
-            return (word >> sh) & 0xffffu;
-          };
-          uint2 packed;
-          packed.x = pick(vreg[4 * u]) | (pick(vreg[4 * u + 1]) << 16);
-          packed.y = pick(vreg[4 * u + 2]) | (pick(vreg[4 * u + 3]) << 16);
-          *reinterpret_cast<uint2*>(&v_lds[(8 * cc + e) * C::VP + 4 * qd]) = packed;
-        }
-      }
-    }
-  };
-
-  // one 64-key tile: keys kb .. kb + 63 of a segment of nkeys keys
-  auto process_tile = [&](int kb, int nkeys, bool masked) __attribute__((always_inline)) {
-    // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
-    f32x4 st[2][4];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) st[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (kBf16) {
-        // all A operands of the 16-key tile first, so the LDS reads overlap
-        const int krow = 32 * (t >> 1) + 8 * (n >> 2) + 4 * (t & 1) + (n & 3);
-        bf16x8 ka[D / 32];
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          ka[kk] = *reinterpret_cast<const bf16x8*>(&k_lds[krow * C::KP + 32 * kk + 8 * jj]);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[c][kk], st[c][t], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 4; ++kk) {
-          const float ka = k_lds[(16 * t + n) * C::KP + 4 * kk + jj];
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            st[c][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qop[c][kk], st[c][t], 0, 0, 0);
-        }
-      }
-    }
-
-    // ---- online softmax, one query column per lane and column tile
-    // a tile inside an unmasked segment is fully visible: no predicate.
-    // Scores stay unscaled here (scale > 0 keeps their order); the scale is
-    // applied inside the exponent, p = 2^(x * scale * log2 e - m).
-    const bool full_tile = !masked && kb + KT <= nkeys;
-    const float sl2 = a.scale_log2;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float tmax = kNegInf;
-      if (full_tile) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb + key_pos<T>(t, jj, i);
-            const bool vis = key < nkeys && (!masked || key < lim[c]);
-            const float x = vis ? st[c][t][i] : kNegInf;
-            st[c][t][i] = x;
-            tmax = fmaxf(tmax, x);
-          }
-      }
-      tmax = fmaxf(tmax, wave_xor(tmax, 16));
-      tmax = fmaxf(tmax, wave_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[c], tmax * sl2);        // running max, scaled
-      const float muse = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[c] - muse);
-      float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse));
-          st[c][t][i] = p;
-          psum += p;
+          const int key = kb + key_pos<kBf16>(t, jj, i);
+          const bool vis = key < nkeys && (!masked || key < lim[c]);
+          const float x = vis ? st[c][t][i] : kNegInf;
+          st[c][t][i] = x;
+          tmax = fmaxf(tmax, x);
         }
-      l_run[c] = l_run[c] * alpha + psum;
-      m_run[c] = mnew;
-      if (__any(alpha != 1.f)) {   // wave-uniform: skip when no column's max moved
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha;
-      }
     }
-
-    // ---- O^T += V^T P^T
-    if constexpr (kBf16) {
-      bf16x8 pb[2][2];
+    tmax = fmaxf(tmax, wave_xor(tmax, 16));
+    tmax = fmaxf(tmax, wave_xor(tmax, 32));
+    const float tm = tmax * sl2;
+    const bool move = tm > m_run[c] + kRescaleSlack;
+    const float mnew = move ? tm : m_run[c];
+    const float muse = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run[c] - muse) : 1.f;
+    float psum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[c][ks][e] = (__bf16)st[c][2 * ks][e];
-            pb[c][ks][e + 4] = (__bf16)st[c][2 * ks + 1][e];
-          }
-#pragma unroll
-      for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
-        // A operands of four 16-dim tiles first, then their MFMAs
-        bf16x8 va[4][2];
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            va[d4][ks] = *reinterpret_cast<const bf16x8*>(
-                &v_lds[(16 * (dt0 + d4) + n) * C::VP + 32 * ks + 8 * jj]);
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              o[c][dt0 + d4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d4][ks], pb[c][ks], o[c][dt0 + d4], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse));
+        st[c][t][i] = p;
+        psum += p;
       }
-    } else {
+    l_run[c] = l_run[c] * alpha + psum;
+    m_run[c] = mnew;
+    if (__any(move)) {   // wave-uniform: skip when no column's reference moved
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float va = v_lds[(16 * t + 4 * jj + i) * C::VP + 16 * dt + n];
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, st[c][t][i], o[c][dt], 0, 0, 0);
-          }
-    }
-  };
-
-  // ---- stream the segments' key tiles through LDS (one code path for both)
-  for (int sgi = 0; sgi < 2; ++sgi) {
-    const T* kp = sgi ? seg1_k : seg0_k;
-    const T* vp = sgi ? seg1_v : seg0_v;
-    const int nkeys = sgi ? seg1_n : seg0_n;
-    const bool masked = sgi ? true : seg0_masked;
-    if (nkeys <= 0) continue;
-    load_tile(kp, vp, nkeys, 0);
-    for (int kb = 0; kb < nkeys; kb += KT) {
-      lds_barrier();           // the previous tile's LDS reads are complete
-      store_tile();
-      if (kb + KT < nkeys) load_tile(kp, vp, nkeys, kb + KT);
-      lds_barrier();
-      process_tile(kb, nkeys, masked);
+      for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha;
     }
   }
+}
 
-  // ---- write this item's partial
+// this item's partial for the lane's two columns
+template <int D>
+__device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[2], const int (&orow)[2],
+                                     const float (&m_run)[2], const float (&l_run)[2],
+                                     const f32x4 (&o)[2][D / 16], int jj) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float l = l_run[c];
@@ -449,6 +297,296 @@ void attn_partial_kernel(const AttnArgs a) {
     for (int dt = 0; dt < D / 16; ++dt)
       *reinterpret_cast<f32x4*>(&a.ws_o[prow * D + 16 * dt + 4 * jj]) = o[c][dt];
   }
+}
+
+// ============================================================ bf16 partial
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_partial_bf16_kernel(const AttnArgs a) {
+  constexpr int KT = kAttnKeyTile;
+  constexpr int RB = D * 2;            // bytes per key row
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int TB = KT * RB;          // bytes per tile and tensor
+  constexpr int NLD = TB / 1024;       // 1 KB buffer-to-LDS loads per tile and tensor
+  static_assert(NLD % NW == 0, "loads must split evenly over the waves");
+  constexpr int LPW = NLD / NW;        // ... issued by each wave
+  constexpr int RPL = 1024 / RB;       // rows per load
+  constexpr int kTileRows = NW * kAttnRowsPerWave;
+  // separate objects per stage, so the compiler can tell the tile being read
+  // from the one in flight
+  __shared__ __attribute__((aligned(16))) uint8_t k_st0[TB], k_st1[TB], v_st0[TB], v_st1[TB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, jj = lane >> 4;
+
+  const Item<bf16_t> it = decode_item<bf16_t>(a, xcd_remap(blockIdx.x, a.n_items));
+  bool valid[2];
+  int orow[2], lim[2];
+  lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
+
+  // ---- Q^T operand, resident for the whole item
+  const bf16_t* q = static_cast<const bf16_t*>(a.q);
+  constexpr int QK = D / 32;
+  bf16x8 qop[2][QK];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) {
+      const bf16x8 z = {};
+      qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
+    }
+
+  float m_run[2] = {kNegInf, kNegInf};
+  float l_run[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- per-lane byte offsets: the global chunk each of this wave's loads
+  // fetches (load u covers tile rows u * RPL ..; lane l writes LDS bytes
+  // 16 l .. 16 l + 15 of it), and the LDS addresses of the operand reads
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (wave * LPW + i) * RPL + lane / CPR, pos = lane % CPR;
+    koff[i] = row * RB + (pos ^ swz_k<D>(row)) * 16;
+    voff[i] = row * RB + (pos ^ swz_v<D>(row)) * 16;
+  }
+  uint32_t kaddr[QK], vaddr[D / 16];
+  {
+    const int kr = 8 * (n >> 2) + (n & 3);    // K row of tile 0 for A-operand row n
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) kaddr[kk] = kr * RB + ((4 * kk + jj) ^ swz_k<D>(kr)) * 16;
+    const int vr = 8 * jj + (n >> 2);         // V row read by this lane in a transposing read
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      vaddr[dt] = vr * RB + ((2 * dt + ((n & 3) >> 1)) ^ swz_v<D>(vr)) * 16 + (n & 1) * 8;
+  }
+
+  const int nt0 = (it.n0 + KT - 1) / KT;
+  const int nt = nt0 + (it.n1 + KT - 1) / KT;
+
+  // tile j of the item: its segment and first key
+  auto tile_src = [&](int j, const bf16_t*& kp, const bf16_t*& vp, int& nk, int& kb, bool& msk)
+                      __attribute__((always_inline)) {
+    if (j < nt0) { kp = it.k0; vp = it.v0; nk = it.n0; kb = j * KT; msk = it.masked0; }
+    else { kp = it.k1; vp = it.v1; nk = it.n1; kb = (j - nt0) * KT; msk = true; }
+  };
+
+  auto issue = [&](auto stage, int j) __attribute__((always_inline)) {
+    const bf16_t *kp, *vp;
+    int nk, kb;
+    bool msk;
+    tile_src(j, kp, vp, nk, kb, msk);
+    const int bytes = min(nk - kb, KT) * RB;   // rows past the segment read as zero
+    const u32x4 rk = raw_buffer(kp + (long long)kb * D, bytes);
+    const u32x4 rv = raw_buffer(vp + (long long)kb * D, bytes);
+    const uint32_t kd = lds_offset(decltype(stage)::value ? k_st1 : k_st0) + wave * LPW * 1024;
+    const uint32_t vd = lds_offset(decltype(stage)::value ? v_st1 : v_st0) + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rk, kd + i * 1024, koff[i]);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rv, vd + i * 1024, voff[i]);
+  };
+
+  const float sl2 = a.scale_log2;
+  auto compute = [&](auto stage, int j) __attribute__((always_inline)) {
+    const bf16_t *kp, *vp;
+    int nk, kb;
+    bool msk;
+    tile_src(j, kp, vp, nk, kb, msk);
+    const BC_LDS uint8_t* ks = (const BC_LDS uint8_t*)(decltype(stage)::value ? k_st1 : k_st0);
+    const BC_LDS uint8_t* vs = (const BC_LDS uint8_t*)(decltype(stage)::value ? v_st1 : v_st0);
+
+    // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
+    f32x4 st[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int trow = 32 * (t >> 1) + 4 * (t & 1);   // row offset of key tile t (swizzle-neutral bits)
+      bf16x8 ka[QK];
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) ka[kk] = *(const BC_LDS bf16x8*)(ks + kaddr[kk] + trow * RB);
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[c][kk], st[c][t], 0, 0, 0);
+    }
+
+    softmax_tile<true, D>(st, o, m_run, l_run, lim, jj, kb, nk, msk, sl2);
+
+    // ---- O^T += V^T P^T
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[c][s2][e] = (__bf16)st[c][2 * s2][e];
+          pb[c][s2][e + 4] = (__bf16)st[c][2 * s2 + 1][e];
+        }
+#pragma unroll
+    for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
+      bf16x8 va[4][2];
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          // keys 32 s2 + 8 jj + 0..3 and + 4..7 of dim 16 (dt0 + d4) + n
+          const BC_LDS uint8_t* base = vs + vaddr[dt0 + d4] + 32 * s2 * RB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BC_LDS i16x4*)base);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BC_LDS i16x4*)(base + 4 * RB));
+          va[d4][s2] = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            o[c][dt0 + d4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d4][s2], pb[c][s2], o[c][dt0 + d4], 0, 0, 0);
+    }
+  };
+
+  // ---- tile pipeline: tile j + 1 is loaded while tile j is computed.  The
+  // barrier at step j publishes tile j and also tells every wave that all
+  // waves have finished tile j - 1, whose stage tile j + 1 then overwrites.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (nt > 0) issue(S0{}, 0);
+  for (int j = 0; j < nt; j += 2) {
+    dma_barrier();
+    if (j + 1 < nt) issue(S1{}, j + 1);
+    compute(S0{}, j);
+    if (j + 1 < nt) {
+      dma_barrier();
+      if (j + 2 < nt) issue(S0{}, j + 2);
+      compute(S1{}, j + 1);
+    }
+  }
+
+  write_partial<D>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+}
+
+// ============================================================ fp32 partial
+// Register-staged: the next tile's global loads are issued before the
+// current tile is computed and written to LDS one iteration later.  Loads
+// past a segment's end are clamped to its last key: finite data that the
+// softmax gives probability 0.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KT = kAttnKeyTile;
+  constexpr int KP = D + 4;                    // LDS row pitch (elements)
+  constexpr int kTileRows = NW * kAttnRowsPerWave;
+  __shared__ __attribute__((aligned(16))) float k_lds[KT * KP];
+  __shared__ __attribute__((aligned(16))) float v_lds[KT * KP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, jj = lane >> 4;
+
+  const Item<float> it = decode_item<float>(a, xcd_remap(blockIdx.x, a.n_items));
+  bool valid[2];
+  int orow[2], lim[2];
+  lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
+
+  const float* q = static_cast<const float*>(a.q);
+  constexpr int QK = D / 4;
+  float qop[2][QK];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) qop[c][kk] = valid[c] ? q[(long long)orow[c] * D + 4 * kk + jj] : 0.f;
+
+  float m_run[2] = {kNegInf, kNegInf};
+  float l_run[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int CPR = D / 4;                   // 16-byte units per key row
+  constexpr int NK = (KT * CPR + NT - 1) / NT; // units per thread
+  u32x4 kreg[NK], vreg[NK];
+  auto load_tile = [&](const float* kp, const float* vp, int nkeys, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int idx = tid + NT * u;
+      const int kr = min(idx / CPR, KT - 1), cc = idx % CPR;
+      const long long off = (long long)min(kb + kr, nkeys - 1) * D + 4 * cc;
+      kreg[u] = *reinterpret_cast<const u32x4*>(kp + off);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+  };
+  auto store_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int idx = tid + NT * u;
+      if (idx >= KT * CPR) continue;
+      const int kr = idx / CPR, cc = idx % CPR;
+      *reinterpret_cast<u32x4*>(&k_lds[kr * KP + 4 * cc]) = kreg[u];
+      *reinterpret_cast<u32x4*>(&v_lds[kr * KP + 4 * cc]) = vreg[u];
+    }
+  };
+
+  const float sl2 = a.scale_log2;
+  auto process_tile = [&](int kb, int nkeys, bool masked) __attribute__((always_inline)) {
+    f32x4 st[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) {
+        const float ka = k_lds[(16 * t + n) * KP + 4 * kk + jj];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          st[c][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qop[c][kk], st[c][t], 0, 0, 0);
+      }
+    softmax_tile<false, D>(st, o, m_run, l_run, lim, jj, kb, nkeys, masked, sl2);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float va = v_lds[(16 * t + 4 * jj + i) * KP + 16 * dt + n];
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, st[c][t][i], o[c][dt], 0, 0, 0);
+        }
+  };
+
+  for (int sgi = 0; sgi < 2; ++sgi) {
+    const float* kp = sgi ? it.k1 : it.k0;
+    const float* vp = sgi ? it.v1 : it.v0;
+    const int nkeys = sgi ? it.n1 : it.n0;
+    const bool masked = sgi ? true : it.masked0;
+    if (nkeys <= 0) continue;
+    load_tile(kp, vp, nkeys, 0);
+    for (int kb = 0; kb < nkeys; kb += KT) {
+      lds_barrier();           // the previous tile's LDS reads are complete
+      store_tile();
+      if (kb + KT < nkeys) load_tile(kp, vp, nkeys, kb + KT);
+      lds_barrier();
+      process_tile(kb, nkeys, masked);
+    }
+  }
+
+  write_partial<D>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
@@ -533,12 +671,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_partial_typed(const AttnArgs& a, hipStream_t stream) {
+template <int D>
+hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.waves == 2)
-    hipLaunchKernelGGL((attn_partial_kernel<T, D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_kernel<T, D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
+  if (a.waves == 2)
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -551,9 +698,8 @@ hipError_t launch_combine_typed(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream) {
-  if (dtype == BC_BF16)
-    return a.D == 128 ? launch_partial_typed<bf16_t, 128>(a, stream) : launch_partial_typed<bf16_t, 64>(a, stream);
-  return a.D == 128 ? launch_partial_typed<float, 128>(a, stream) : launch_partial_typed<float, 64>(a, stream);
+  if (dtype == BC_BF16) return a.D == 128 ? launch_partial_bf16<128>(a, stream) : launch_partial_bf16<64>(a, stream);
+  return a.D == 128 ? launch_partial_f32<128>(a, stream) : launch_partial_f32<64>(a, stream);
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream) {
