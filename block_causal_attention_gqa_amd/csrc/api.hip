@@ -66,6 +66,37 @@ int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_a
   return BC_OK;
 }
 
+// Prefix split count P when the caller leaves it to the library.  A
+// launch's time is modelled as
+//   max(rounds * (tiles per item * t_tile + t_item), kv_bytes / bw + t_item)
+//   + (P + 1) * t_slot
+// with rounds = ceil(items / co-resident workgroups): splitting the prefix
+// shortens every item but adds a partial slot per output row that the
+// combine writes and reads back, and no split count beats streaming the
+// K/V bytes from HBM once.  Constants measured on MI355X: ~1.9 us per
+// 64-key tile with one workgroup per CU and ~2.5 us with two (512
+// co-resident), ~2 us of fixed cost per item (Q load, first tile, partial
+// write), K/V and partial slots streamed at ~5 TB/s.
+int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, int D) {
+  constexpr int kCUs = 256, kSlotsResident = 512;
+  constexpr double kTileUs1 = 1.9, kTileUs2 = 2.5, kItemUs = 2.0, kBytesPerUs = 5.0e6;
+  const double slot_us = (double)rows_total * (D * 4.0 + 8.0) * 2.0 / kBytesPerUs;
+  const double floor_us = kv_bytes / kBytesPerUs + kItemUs;
+  const int most = std::max(1, std::min(256, (maxlen + kAttnKeyTile - 1) / kAttnKeyTile));
+  int best = 1;
+  double best_us = 1e300;
+  for (int P = 1; P <= most; ++P) {
+    const int per = (maxlen + P - 1) / P;
+    const int tiles = std::max(1, (per + kAttnKeyTile - 1) / kAttnKeyTile);
+    const long long items = (long long)row_tiles * P;
+    const long long rounds = (items + kSlotsResident - 1) / kSlotsResident;
+    const double tile_us = items <= kCUs ? kTileUs1 : kTileUs2;
+    const double us = std::max(rounds * (tiles * tile_us + kItemUs), floor_us) + (P + 1) * slot_us;
+    if (us < best_us - 1e-9) { best_us = us; best = P; }
+  }
+  return best;
+}
+
 // lengths[s] are the prefix lengths the plan is made for (the capacities when
 // sizing the workspace: the plan is monotone in the lengths, so that bound
 // covers every call with the same shapes).
@@ -86,12 +117,10 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   for (int s = 0; s < prefix->n_seq; ++s) maxlen = std::max(maxlen, lengths[s]);
   int P = n_splits;
   if (P == 0) {
-    // enough workgroups to cover the 256 CUs about twice, but no chunk
-    // shorter than 128 keys (partial traffic grows with the chunk count)
-    const int base = groups * p->n_mt_prefix;
-    const int want = (512 + base - 1) / base;
-    const int most = std::max(1, (maxlen + 127) / 128);
-    P = std::max(1, std::min(want, most));
+    // K/V bytes of the prefix as streamed from HBM (a shared fork prefix once)
+    double kv = 0;
+    for (int s = 0; s < prefix->n_seq; ++s) kv += (double)lengths[s] * Hkv * D * 2.0 * elem_bytes(prefix->dtype);
+    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, D);
   }
   p->P = P;
   for (int s = 0; s < prefix->n_seq; ++s) {
@@ -176,17 +205,20 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
       if (priv_len[s] < 0 || priv_len[s] > priv->capacity) return BC_ERR_ARG;
 
   std::memset(args, 0, sizeof(*args));
+  if (!ws) return BC_ERR_WORKSPACE;
   Plan p;
   make_plan(prefix, priv, a, prefix_len, n_prefix_splits, &p, args->chunk);
-  if (!ws) return BC_ERR_WORKSPACE;
-  {
-    // the caller sized the workspace for the capacities; check against that bound
-    int caps[BC_MAX_SEQ];
-    for (int s = 0; s < prefix->n_seq; ++s) caps[s] = prefix->capacity;
-    Plan pmax;
-    int chunk_max[BC_MAX_SEQ];
-    make_plan(prefix, priv, a, caps, n_prefix_splits, &pmax, chunk_max);
-    if (ws_bytes < pmax.total_bytes || ws_bytes < p.total_bytes) return BC_ERR_WORKSPACE;
+  if (ws_bytes < p.total_bytes) {
+    // An explicit split count must fit.  An automatic one is reduced to
+    // what the workspace holds (a workspace sized by bc_attn_workspace_bytes
+    // always holds at least the split count chosen at full capacity).
+    if (n_prefix_splits > 0) return BC_ERR_WORKSPACE;
+    int P = p.P;
+    while (P > 1 && ws_bytes < p.total_bytes) {
+      --P;
+      make_plan(prefix, priv, a, prefix_len, P, &p, args->chunk);
+    }
+    if (ws_bytes < p.total_bytes) return BC_ERR_WORKSPACE;
   }
   const int D = prefix->head_dim;
   args->q = a->q;

@@ -66,42 +66,29 @@ constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ inline float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lane groups that
+// hold one query column's keys).  v_permlane16_swap / v_permlane32_swap with
+// both operands x return the two halves of each lane pair, so max of the
+// pair is the max over l and l ^ 16 (l ^ 32); no LDS round trip.
+__device__ inline float group4_max(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+  const uint32_t c = __builtin_bit_cast(uint32_t, x);
+  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)q[0]), __builtin_bit_cast(float, (uint32_t)q[1]));
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
 // every outstanding global load of the wave, which would stall on the next
 // key tile's prefetch; here only LDS traffic is drained before the barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One buffer-to-LDS load: every lane fetches the 16 bytes at byte offset
-// voff of the buffer described by rsrc and writes them to LDS at byte
-// lds + 16 * lane.  Inline assembly keeps the load out of the compiler's
-// wait-count bookkeeping, which would otherwise make the reads of the stage
-// being computed wait for the loads filling the other stage; completion is
-// awaited explicitly by dma_barrier().  Extra untracked loads only make the
-// compiler's own (in-order) vmcnt waits stricter.
-__device__ inline void buffer_load_lds16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
-}
-
-// raw buffer descriptor: base, stride 0, num_records bytes (reads past it
-// return zero)
-__device__ inline u32x4 raw_buffer(const void* base, int bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kRawBufferWord3};
-}
-
-__device__ inline uint32_t lds_offset(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((BC_LDS const uint8_t*)p);
-}
-
-// Barrier after this wave's buffer-to-LDS loads have landed: once every wave
-// passes it, the tile written by all waves is visible to all of them.
-// The wait is the compiler builtin (encoding: vmcnt 0, expcnt and lgkmcnt
-// unconstrained) so that the compiler's own bookkeeping knows every earlier
-// vector-memory load, e.g. of the Q operand, has completed there.
-__device__ inline void dma_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  asm volatile("s_barrier" ::: "memory");
+// 16 bytes per lane from a raw buffer (base, stride 0, `bytes` records):
+// offsets at or past `bytes` read as zero, so a tile running past its
+// segment's end needs no clamping or masking of the loaded values.
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map
@@ -113,11 +100,22 @@ __device__ inline int xcd_remap(int hw, int n) {
   return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
 }
 
-// position inside the 64-key tile of the value held in C-register i of tile t
-template <bool kBf16>
-__device__ inline int key_pos(int t, int jj, int i) {
-  if constexpr (kBf16) return 32 * (t >> 1) + 8 * jj + 4 * (t & 1) + i;
-  else return 16 * t + 4 * jj + i;
+// Position inside the 64-key tile of the value held in C-register i of tile
+// t: (lane-group offset) + (compile-time offset).  bf16: 32 (t >> 1) + 8 jj +
+// 4 (t & 1) + i; fp32: 16 t + 4 jj + i.
+template <bool kBf16> __device__ inline int key_group_off(int jj) { return kBf16 ? 8 * jj : 4 * jj; }
+template <bool kBf16> constexpr int key_const_off(int t, int i) {
+  return kBf16 ? 32 * (t >> 1) + 4 * (t & 1) + i : 16 * t + i;
+}
+
+// Logical item of this workgroup.  Workgroups are dispatched in block-id
+// order, so the (long) prefix items take the lowest ids and start first; the
+// short active items fill in behind them.  Within each class the XCD remap
+// keeps neighbouring items on one XCD.
+__device__ inline int item_of_block(const AttnArgs& a) {
+  const int hw = blockIdx.x;
+  if (hw < a.n_prefix_items) return xcd_remap(hw, a.n_prefix_items);
+  return a.n_prefix_items + xcd_remap(hw - a.n_prefix_items, a.n_items - a.n_prefix_items);
 }
 
 // 16-byte chunk swizzles of the bf16 K and V tiles in LDS (row r of a tile,
@@ -238,25 +236,21 @@ __device__ inline void softmax_tile(f32x4 (&st)[2][4], f32x4 (&o)[2][D / 16], fl
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float tmax = kNegInf;
-    if (full_tile) {
+    if (!full_tile) {
+      // visible iff key < nkeys (and key < lim for the active keys); with
+      // key = kb + group offset + constant offset, one threshold per column
+      const int thr = (masked ? min(nkeys, lim[c]) : nkeys) - kb - key_group_off<kBf16>(jj);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + key_pos<kBf16>(t, jj, i);
-          const bool vis = key < nkeys && (!masked || key < lim[c]);
-          const float x = vis ? st[c][t][i] : kNegInf;
-          st[c][t][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (!(key_const_off<kBf16>(t, i) < thr)) st[c][t][i] = kNegInf;
     }
-    tmax = fmaxf(tmax, wave_xor(tmax, 16));
-    tmax = fmaxf(tmax, wave_xor(tmax, 32));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
+    tmax = group4_max(tmax);
     const float tm = tmax * sl2;
     const bool move = tm > m_run[c] + kRescaleSlack;
     const float mnew = move ? tm : m_run[c];
@@ -307,21 +301,19 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   constexpr int RB = D * 2;            // bytes per key row
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int TB = KT * RB;          // bytes per tile and tensor
-  constexpr int NLD = TB / 1024;       // 1 KB buffer-to-LDS loads per tile and tensor
-  static_assert(NLD % NW == 0, "loads must split evenly over the waves");
-  constexpr int LPW = NLD / NW;        // ... issued by each wave
-  constexpr int RPL = 1024 / RB;       // rows per load
+  constexpr int NT = NW * 64;          // threads
+  static_assert(TB % (NT * 16) == 0, "tile chunks must split evenly over the threads");
+  constexpr int LPT = TB / (NT * 16);  // 16-byte chunks per thread, tile and tensor
   constexpr int kTileRows = NW * kAttnRowsPerWave;
-  // separate objects per stage, so the compiler can tell the tile being read
-  // from the one in flight
+  // two stages: tile j + 1 is written while tile j is read
   __shared__ __attribute__((aligned(16))) uint8_t k_st0[TB], k_st1[TB], v_st0[TB], v_st1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = tid >> 6;
   const int n = lane & 15, jj = lane >> 4;
 
-  const Item<bf16_t> it = decode_item<bf16_t>(a, xcd_remap(blockIdx.x, a.n_items));
+  const Item<bf16_t> it = decode_item<bf16_t>(a, item_of_block(a));
   bool valid[2];
   int orow[2], lim[2];
   lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
@@ -346,15 +338,17 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- per-lane byte offsets: the global chunk each of this wave's loads
-  // fetches (load u covers tile rows u * RPL ..; lane l writes LDS bytes
-  // 16 l .. 16 l + 15 of it), and the LDS addresses of the operand reads
-  uint32_t koff[LPW], voff[LPW];
+  // ---- register staging: thread tid moves 16-byte chunks g = tid + NT u
+  // (u < LPT) of each tile, row g / CPR, chunk g % CPR; it reads them in
+  // order from HBM (coalesced) and writes them to their swizzled LDS
+  // positions.  Also the LDS addresses of the operand reads.
+  uint32_t goff[LPT], koff[LPT], voff[LPT];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int row = (wave * LPW + i) * RPL + lane / CPR, pos = lane % CPR;
-    koff[i] = row * RB + (pos ^ swz_k<D>(row)) * 16;
-    voff[i] = row * RB + (pos ^ swz_v<D>(row)) * 16;
+  for (int u = 0; u < LPT; ++u) {
+    const int g = tid + NT * u, row = g / CPR, c = g % CPR;
+    goff[u] = row * RB + c * 16;
+    koff[u] = row * RB + (c ^ swz_k<D>(row)) * 16;
+    voff[u] = row * RB + (c ^ swz_v<D>(row)) * 16;
   }
   uint32_t kaddr[QK], vaddr[D / 16];
   {
@@ -377,20 +371,29 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     else { kp = it.k1; vp = it.v1; nk = it.n1; kb = (j - nt0) * KT; msk = true; }
   };
 
-  auto issue = [&](auto stage, int j) __attribute__((always_inline)) {
+  u32x4 kreg[LPT], vreg[LPT];
+  auto load = [&](int j) __attribute__((always_inline)) {
     const bf16_t *kp, *vp;
     int nk, kb;
     bool msk;
     tile_src(j, kp, vp, nk, kb, msk);
     const int bytes = min(nk - kb, KT) * RB;   // rows past the segment read as zero
-    const u32x4 rk = raw_buffer(kp + (long long)kb * D, bytes);
-    const u32x4 rv = raw_buffer(vp + (long long)kb * D, bytes);
-    const uint32_t kd = lds_offset(decltype(stage)::value ? k_st1 : k_st0) + wave * LPW * 1024;
-    const uint32_t vd = lds_offset(decltype(stage)::value ? v_st1 : v_st0) + wave * LPW * 1024;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kp + (long long)kb * D), 0, bytes, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vp + (long long)kb * D), 0, bytes, kRawBufferWord3);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rk, kd + i * 1024, koff[i]);
+    for (int u = 0; u < LPT; ++u) kreg[u] = buffer_load16(rk, goff[u]);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rv, vd + i * 1024, voff[i]);
+    for (int u = 0; u < LPT; ++u) vreg[u] = buffer_load16(rv, goff[u]);
+  };
+  auto store = [&](auto stage) __attribute__((always_inline)) {
+    uint8_t* kd = decltype(stage)::value ? k_st1 : k_st0;
+    uint8_t* vd = decltype(stage)::value ? v_st1 : v_st0;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) *reinterpret_cast<u32x4*>(kd + koff[u]) = kreg[u];
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) *reinterpret_cast<u32x4*>(vd + voff[u]) = vreg[u];
   };
 
   const float sl2 = a.scale_log2;
@@ -457,20 +460,31 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- tile pipeline: tile j + 1 is loaded while tile j is computed.  The
+  // ---- tile pipeline: tile j + 1 is read from HBM into registers while
+  // tile j is computed, and written to the other LDS stage after it.  The
   // barrier at step j publishes tile j and also tells every wave that all
   // waves have finished tile j - 1, whose stage tile j + 1 then overwrites.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (nt > 0) issue(S0{}, 0);
+  if (nt > 0) {
+    load(0);
+    store(S0{});
+  }
+  // Every load so far (Q operand, first tile) has landed on every path into
+  // the loop; with this the compiler's wait bookkeeping does not wait for
+  // the Q loads again inside the loop, where that wait would also drain the
+  // next tile's loads.  (Encoding: vmcnt 0, expcnt and lgkmcnt unconstrained.)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   for (int j = 0; j < nt; j += 2) {
-    dma_barrier();
-    if (j + 1 < nt) issue(S1{}, j + 1);
+    lds_barrier();
+    if (j + 1 < nt) load(j + 1);
     compute(S0{}, j);
     if (j + 1 < nt) {
-      dma_barrier();
-      if (j + 2 < nt) issue(S0{}, j + 2);
+      store(S1{});
+      lds_barrier();
+      if (j + 2 < nt) load(j + 2);
       compute(S1{}, j + 1);
+      if (j + 2 < nt) store(S0{});
     }
   }
 
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, jj = lane >> 4;
 
-  const Item<float> it = decode_item<float>(a, xcd_remap(blockIdx.x, a.n_items));
+  const Item<float> it = decode_item<float>(a, item_of_block(a));
   bool valid[2];
   int orow[2], lim[2];
   lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
@@ -590,35 +604,39 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
-// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  One row per
-// workgroup; wave w takes slots w, w + 4, ... eight at a time with every load
-// of the batch issued before any is used, rescaling online when a batch
-// raises the running max; the four waves then merge through LDS.
-template <typename T, int D>
+// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  D / 4
+// lanes per row take 4 dims (16 bytes) each, so a row's slot is one
+// contiguous read.  SW groups of those lanes split the slots of a row (SW = 1
+// for many rows and few slots, 8 for few rows and many slots); each group
+// takes its slots four at a time with every load of the batch issued first,
+// rescaling its running sums when a batch raises the max, and the groups
+// merge through LDS.
+template <typename T, int D, int SW>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
-  constexpr int E = D / 64;
-  constexpr int B = 8;
-  __shared__ float red_o[4][D];
-  __shared__ float red_m[4], red_l[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x;
-  float wm = kNegInf, wl = 0.f, acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s0 = wave; s0 < a.n_slots; s0 += 4 * B) {
+  constexpr int LPR = D / 4;            // lanes per row and slot group
+  constexpr int RPB = 256 / (LPR * SW); // rows per workgroup
+  constexpr int B = 4;
+  __shared__ float red_m[SW > 1 ? 256 : 1], red_l[SW > 1 ? 256 : 1];
+  __shared__ f32x4 red_o[SW > 1 ? 256 : 1];
+  const int t = threadIdx.x;
+  const int sub = (t / LPR) % SW;
+  const int row = blockIdx.x * RPB + t / (LPR * SW);
+  const int d0 = (t % LPR) * 4;
+  const bool live = row < a.rows_total;
+  float wm = kNegInf, wl = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sub; live && s0 < a.n_slots; s0 += B * SW) {
     float2 ml[B];
-    float ov[B][E];
+    f32x4 ov[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const int s = s0 + 4 * u;
-      const long long prow = (long long)s * a.rows_total + row;
+      const int s = s0 + u * SW;
       ml[u] = float2{kNegInf, 0.f};
-#pragma unroll
-      for (int e = 0; e < E; ++e) ov[u][e] = 0.f;
+      ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < a.n_slots) {
+        const long long prow = (long long)s * a.rows_total + row;
         ml[u] = a.ws_ml[prow];
-#pragma unroll
-        for (int e = 0; e < E; ++e) ov[u][e] = a.ws_o[prow * D + lane + 64 * e];
+        ov[u] = *reinterpret_cast<const f32x4*>(&a.ws_o[prow * D + d0]);
       }
     }
     float bm = kNegInf;
@@ -628,46 +646,51 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
     if (nm == kNegInf) continue;
     const float sc = __builtin_amdgcn_exp2f(wm - nm);
     wl *= sc;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= sc;
+    acc *= sc;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const float w = ml[u].x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - nm);
       wl += w * ml[u].y;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += w * ov[u][e];
+      acc += w * ov[u];
     }
     wm = nm;
   }
-  if (lane == 0) { red_m[wave] = wm; red_l[wave] = wl; }
+  if constexpr (SW > 1) {
+    red_m[t] = wm;
+    red_l[t] = wl;
+    red_o[t] = acc;
+    __syncthreads();
+    if (sub != 0 || !live) return;
+    float M = kNegInf;
 #pragma unroll
-  for (int e = 0; e < E; ++e) red_o[wave][lane + 64 * e] = acc[e];
-  __syncthreads();
-  if (wave != 0) return;
-  float M = kNegInf;
+    for (int g = 0; g < SW; ++g) M = fmaxf(M, red_m[t + g * LPR]);
+    wl = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (M != kNegInf) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w]);
-  float L = 0.f, o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float f = red_m[w] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(red_m[w] - M);
-    L += f * red_l[w];
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += f * red_o[w][lane + 64 * e];
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = static_cast<T*>(a.out) + (long long)row * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float v = o[e] * inv;
-    if constexpr (sizeof(T) == 2) {
-      const __bf16 b = (__bf16)v;
-      out[lane + 64 * e] = *reinterpret_cast<const uint16_t*>(&b);
-    } else {
-      out[lane + 64 * e] = v;
+      for (int g = 0; g < SW; ++g) {
+        const float mg = red_m[t + g * LPR];
+        const float f = mg == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mg - M);
+        wl += f * red_l[t + g * LPR];
+        acc += f * red_o[t + g * LPR];
+      }
     }
+  } else {
+    if (!live) return;
+  }
+  const float inv = wl > 0.f ? 1.f / wl : 0.f;
+  acc *= inv;
+  T* out = static_cast<T*>(a.out) + (long long)row * D + d0;
+  if constexpr (sizeof(T) == 2) {
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 b = (__bf16)acc[e];
+      h[e] = __builtin_bit_cast(uint16_t, b);
+    }
+    *reinterpret_cast<uint2*>(out) = uint2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+  } else {
+    *reinterpret_cast<f32x4*>(out) = acc;
   }
 }
 
@@ -689,10 +712,20 @@ hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int SW>
+hipError_t launch_combine_sw(const AttnArgs& a, hipStream_t stream) {
+  constexpr int rows_per_block = 256 / (D / 4 * SW);
+  hipLaunchKernelGGL((attn_combine_kernel<T, D, SW>), dim3((a.rows_total + rows_per_block - 1) / rows_per_block),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// slot groups per row: split the slots when there are many of them and too
+// few rows to fill the GPU otherwise
 template <typename T, int D>
 hipError_t launch_combine_typed(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(a.rows_total), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.n_slots >= 8 && a.rows_total < 2048) return launch_combine_sw<T, D, 8>(a, stream);
+  return launch_combine_sw<T, D, 1>(a, stream);
 }
 
 }  // namespace

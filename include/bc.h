@@ -137,14 +137,19 @@ int bc_kv_commit(const bc_kv_cache *cache, int32_t *len, int32_t seq, int32_t st
  *   priv_len    HOST [a->n_seq] when priv != NULL.
  *   mask        bc_mask.
  *   scale       softmax scale (finite, > 0), normally 1 / sqrt(head_dim).
- *   n_prefix_splits  0 = automatic; otherwise the number of key chunks the
- *               prefix is cut into (1 .. 256), for tuning and tests.
+ *   n_prefix_splits  0 = automatic (a cost model over the shapes and the
+ *               prefix lengths, limited to what `ws` holds); otherwise the
+ *               number of key chunks the prefix is cut into (1 .. 256), for
+ *               tuning and tests.
  *   out         [n_seq][n_rows][n_q_heads][head_dim] in the q dtype.
  *   ws          workspace of at least bc_attn_workspace_bytes(...) bytes
- *               for the same shapes, capacities and n_prefix_splits.
+ *               for the same shapes, capacities and n_prefix_splits.  With
+ *               automatic splits a smaller workspace is accepted as long as
+ *               it holds one split; fewer splits are then used.
  * Errors: BC_ERR_ARG (shapes / pointers / blk_off / lengths);
  * BC_ERR_UNSUPPORTED (head_dim not 64 or 128, n_seq > BC_MAX_SEQ,
- * n_blk > BC_MAX_BLOCKS, mixed dtypes); BC_ERR_WORKSPACE. */
+ * n_blk > BC_MAX_BLOCKS, mixed dtypes); BC_ERR_WORKSPACE (ws NULL, or too
+ * small for the explicit split count, or for one split). */
 size_t bc_attn_workspace_bytes(const bc_kv_cache *prefix, const bc_kv_cache *priv,
                                const bc_active *a, int32_t n_prefix_splits);
 int bc_attn_step(const bc_kv_cache *prefix, const int32_t *prefix_len,

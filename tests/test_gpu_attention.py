@@ -149,9 +149,16 @@ def test_workspace_and_argument_errors_before_launch():
     prefix = B.KVCache(pk_t.to(G.DEV), pv_t.to(G.DEV))
     out = torch.empty((1, 8, 16, 128), dtype=torch.bfloat16, device=G.DEV)
     nb = B.bc_attn_workspace_bytes(prefix, None, (1, 8, 16, 128), [0, 8])
-    small = torch.empty(nb - 256, dtype=torch.uint8, device=G.DEV)
     q, k, v = q_t.to(G.DEV), k_t.to(G.DEV), v_t.to(G.DEV)
-    st = B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, small, check=False)
+    # too small for a single split
+    tiny = torch.empty(256, dtype=torch.uint8, device=G.DEV)
+    st = B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, tiny, check=False)
+    assert st == B.BC_ERR_WORKSPACE
+    # an explicit split count must fit the workspace
+    nb3 = B.bc_attn_workspace_bytes(prefix, None, (1, 8, 16, 128), [0, 8], 3)
+    small = torch.empty(nb3 - 256, dtype=torch.uint8, device=G.DEV)
+    st = B.bc_attn_step(prefix, [100], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, small, n_prefix_splits=3,
+                        check=False)
     assert st == B.BC_ERR_WORKSPACE
     ws = torch.empty(nb, dtype=torch.uint8, device=G.DEV)
     assert B.bc_attn_step(prefix, [129], None, None, q, k, v, [0, 8], BIDIR, 0.1, out, ws,
@@ -180,3 +187,25 @@ def test_partial_then_combine_equals_step():
     B.bc_attn_combine(*args, b, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_automatic_splits_shrink_to_the_workspace():
+    # a workspace that holds fewer slots than the automatic choice wants:
+    # the call uses fewer splits and the result still matches the oracle
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    seed, S, R, Hq, Hkv, D = 90, 1, 32, 16, 2, 128
+    (pk, pv), (k32, v32) = synth.kv_cache(seed, S, Hkv, 3352, D, [3100], "bf16")
+    (q, q32), (k, ka), (v, va) = synth.active_qkv(seed, S, R, Hq, Hkv, D, "bf16", 0)
+    prefix = B.KVCache(pk.to(G.DEV), pv.to(G.DEV))
+    full = B.bc_attn_workspace_bytes(prefix, None, (S, R, Hq, D), [0, R])
+    one = B.bc_attn_workspace_bytes(prefix, None, (S, R, Hq, D), [0, R], 1)
+    assert one < full
+    out = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+    want = OA.attention_step(q32, k32, v32, [3100], ka, va, [0, R], BIDIR, scale=D ** -0.5)
+    for nbytes in (one, (one + full) // 2, full):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=G.DEV)
+        B.bc_attn_step(prefix, [3100], None, None, q.to(G.DEV), k.to(G.DEV), v.to(G.DEV), [0, R], BIDIR,
+                       D ** -0.5, out, ws)
+        got = out.float().cpu().numpy()
+        assert np.abs(got - want).max() <= TOL["bf16"]
