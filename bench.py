@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle decode until this much CPU time is spent")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the secondary measurements (fork round, batch-16 attention, verify scan)")
     return ap.parse_args()
 
 
@@ -234,9 +236,91 @@ def main():
         "setup_s": round(setup_s, 2),
     }
 
+    if not args.no_legs:
+        result["legs"] = legs(stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dec, args)
     print(json.dumps(result), flush=True)
+
+
+def graph_us(fn, stream, reps=10, replays=5):
+    """Average duration of one fn() on `stream`: reps calls captured back to
+    back in a graph, replayed between two events on that stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * reps)
+
+
+def legs(stream):
+    """Secondary measurements on the other workloads of the pages' systems:
+    the shared-prefix fork round at N = 4, 16, 64 rollouts (attention there
+    is MFMA-bound), the verify scan over N = 64 rollouts' logits (HBM-bound),
+    the large-block decode's attention at batch 16 (HBM-bound), and the
+    duration of a minimal kernel as the launch floor."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    from block_causal_attention_gqa_amd import decode, synth
+    out = {}
+    fork = []
+    for N in (4, 16, 64):
+        fv = decode.ForkVerify(N, seed=0, device="cuda:0", block=0)
+        rec = {"N": N, "rows": N * fv.R, "shared_prefix": fv.prefix}
+        for pass_id, name in ((0, "draft_bidir"), (1, "verify_causal")):
+            us = graph_us(lambda: fv.attention(pass_id, stream), stream)
+            fl = fv.attention_flops(pass_id)
+            rec[name] = {"attn_us": round(us, 3), "TFLOP_s": round(fl / us / 1e6, 1),
+                         "mfma_frac": round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        rec["draft_argmax_us"] = round(graph_us(lambda: fv.draft_argmax(stream), stream), 3)
+        vus = graph_us(lambda: fv.verify(stream), stream)
+        vbytes = N * fv.R * fv.V * 4
+        rec["verify"] = {"us": round(vus, 3), "GB_s": round(vbytes / vus / 1e3, 1),
+                         "hbm_frac": round(vbytes / vus / 1e3 / HBM_PEAK_GBS, 4)}
+        rec["round_us"] = round(graph_us(lambda: fv.run(stream), stream, reps=4), 3)
+        fork.append(rec)
+        del fv
+        torch.cuda.empty_cache()
+    out["fork_round"] = fork
+
+    # large-block decode attention at batch 16: 32q/8kv, D 128, prefixes
+    # 2048 .. 2288, one block of 32 rows per sequence
+    p = synth.PRESETS["large_block"]
+    S, R, Hq, Hkv, D = 16, 32, p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
+    cap = p["prefix"] + sum(p["blocks"])
+    lens = [p["prefix"] + 16 * s for s in range(S)]
+    (pk, pv), _ = synth.kv_cache(0, S, Hkv, cap, D, lens, "bf16")
+    (q, _), (k, _), (v, _) = synth.active_qkv(0, S, R, Hq, Hkv, D, "bf16", 0)
+    cache = B.KVCache(pk.to("cuda:0"), pv.to("cuda:0"))
+    q, k, v = q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0")
+    o = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.zeros(B.bc_attn_workspace_bytes(cache, None, (S, R, Hq, D), [0, R]), dtype=torch.uint8,
+                     device="cuda:0")
+    us = graph_us(lambda: B.bc_attn_step(cache, lens, None, None, q, k, v, [0, R], B.BC_MASK_BLOCK_BIDIR,
+                                         D ** -0.5, o, ws, stream=stream), stream)
+    nbytes = sum(attn_bytes_flops(L, R, Hq, Hkv, D)[0] for L in lens)
+    flops = sum(attn_bytes_flops(L, R, Hq, Hkv, D)[1] for L in lens)
+    out["large_block_b16_attn"] = {"attn_us": round(us, 3), "TB_s": round(nbytes / us / 1e6, 3),
+                                   "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                   "TFLOP_s": round(flops / us / 1e6, 1), "bytes": nbytes}
+    del pk, pv, cache, ws
+    # launch floor: a one-element fill kernel
+    x = torch.zeros(1, device="cuda:0")
+    out["launch_floor_us"] = round(graph_us(lambda: x.fill_(1.0), stream, reps=50), 3)
+    return out
 
 
 def cpu_baseline(dec, args):
