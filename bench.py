@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle decode until this much CPU time is spent")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="for hardware-counter runs: issue one decode's attention-partial launches and a "
+                         "256 MiB device copy (the counters' calibration), print one JSON line, exit")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the secondary measurements (fork round, batch-16 attention, verify scan)")
     return ap.parse_args()
@@ -72,6 +75,9 @@ def main():
     dec = decode.SectionDecode(preset, seed=args.seed, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
+    if args.pmc_pass:
+        pmc_pass(dec)
+        return
 
     stream = torch.cuda.Stream()
     graph = None
@@ -198,9 +204,9 @@ def main():
                 "bytes_per_launch": scan_bytes / n_scan, "avg_launch_us": round(avg["vocab_scan"], 3)}
     else:
         pgbs = partial_bytes / n_attn / (avg["attn_partial"] * 1e-6) / 1e9
-        roof = {"kernel": "attn_partial_kernel (bc_attn_partial: block-causal GQA attention, split-KV)",
+        roof = {"kernel": "attn_partial_bf16_kernel (bc_attn_partial: block-causal GQA attention, split-KV)",
                 "bound": "hbm", "achieved": round(pgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": partial_bytes / n_attn, "avg_launch_us": round(avg["attn_partial"], 3)}
     kernel_us = {k: round(v, 3) for k, v in avg.items()}
 
@@ -241,6 +247,59 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dec, args)
     print(json.dumps(result), flush=True)
+
+
+TRAFFIC_SUMMARY = "profiles/attn_partial_section_decode_traffic.md"
+
+
+def measured_traffic():
+    """HBM bytes per attn_partial launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the attention
+    sources changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        text = open(os.path.join(root, TRAFFIC_SUMMARY)).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_sha256", "sources"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if not {"traffic_bytes_per_launch", "source_sha256", "sources"} <= fields.keys():
+        return None
+    h = hashlib.sha256()
+    for f in fields["sources"].split(", "):
+        h.update(open(os.path.join(root, f), "rb").read())
+    if h.hexdigest() != fields["source_sha256"]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def pmc_pass(dec):
+    """One decode's attention-partial launches (the kernel the roofline
+    covers), then a plain 256 MiB device-to-device copy whose FETCH_SIZE /
+    WRITE_SIZE readings calibrate the counters (expected 256 MiB each)."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    dec.run()                # warm; the cache ends committed to full length
+    torch.cuda.synchronize()
+    length = dec.len0.copy()
+    n = 0
+    for b, bs in enumerate(dec.blocks):
+        for st in range(dec.steps):
+            q, k, v = dec.qkv[b][st]
+            B.bc_attn_partial(dec.cache, length.copy(), None, None, q, k, v, [0, bs], B.BC_MASK_BLOCK_BIDIR,
+                              dec.scale, dec.out[bs], dec.ws_attn)
+            n += 1
+        length += bs          # the warm run already wrote the block's K/V
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"partial_launches": n, "copy_bytes": src.numel() * 4}), flush=True)
 
 
 def graph_us(fn, stream, reps=10, replays=5):
