@@ -1,4 +1,4 @@
-// Internal declarations shared by the host entry points (bc_api.cpp) and the
+// Internal declarations shared by the host entry points (api.hip) and the
 // kernel translation units.  Not part of the public ABI.
 #pragma once
 
