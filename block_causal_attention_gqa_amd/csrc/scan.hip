@@ -222,7 +222,62 @@ struct SelectSmem {
   double red[kScanThreads];
   int cnt[2][kScanThreads / 64];
   double lohi[2][2 * (kScanThreads / 64)];
+  double cw[64];          // one-wave path: confidence of row i, -inf outside E
+  double cut[2];          // one-wave path: values at ranks k - 1 and k
+  int done;
 };
+
+// Decisions of a block of at most 64 rows by wave 0 alone, lane i owning
+// row i, when no float64 refine is needed: counts are ballots, the rank is
+// taken against the block's confidences broadcast from LDS, and -- with no
+// refined row in the block, every row carries the same relative error band
+// -- the extreme of (c - e) over the top k and of (c + e) over the rest sit
+// at ranks k - 1 and k.  Returns false, having written nothing, when a row
+// is inside the threshold band or the cut is not certain; the caller then
+// takes the workgroup-wide path, which refines.
+__device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, double tau, SelectSmem& sm) {
+  const int i = threadIdx.x;
+  const bool inE = i < nb && (sm.st[i] & kInE);
+  const double c = inE ? sm.cf[i] : -__builtin_huge_val();
+  if (__ballot(inE && fabs(c - tau) <= kBand * c)) return false;
+  sm.cw[i] = c;
+  const unsigned long long eb = __ballot(inE), ab = __ballot(inE && c > tau);
+  const int nE = __popcll(eb), nA = __popcll(ab);
+  int k;
+  if (a.mode[b] == BC_UNMASK_SEMI) {
+    k = nA;
+  } else {
+    const int fb = (nE + a.n_div[b] - 1) / a.n_div[b];
+    k = min(nE, max(nA, fb));
+  }
+  const int how = k == 0 ? 0 : k == nE ? 1 : k == nA ? 2 : 3;
+  int rk = 0;
+  if (how == 3) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt 0: cw[] written by every lane
+    __builtin_amdgcn_wave_barrier();
+    for (int q = 0; q < nb; ++q) {             // rows outside E hold -inf and never count
+      const double cq = sm.cw[q];
+      rk += cq > c || (cq == c && q < i);
+    }
+    if (inE && rk == k - 1) sm.cut[0] = c;
+    if (inE && rk == k) sm.cut[1] = c;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const double lo = sm.cut[0] - kBand * sm.cut[0], hi = sm.cut[1] + kBand * sm.cut[1];
+    if (!(lo > hi)) return false;
+  }
+  if (inE) {
+    const int r = r0 + i;
+    const bool take = how == 1 || (how == 2 && c > tau) || (how == 3 && rk < k);
+    if (take) {
+      a.tokens[r] = sm.tok[i];
+      a.masked[r] = 0;
+    }
+    if (a.conf) a.conf[r] = (float)c;
+  }
+  if (i == 0) a.n_commit[b] = k;
+  return true;
+}
 
 // Decisions of block b, one workgroup.  Thread t owns rows t, t + 256, ...
 // after the merge, so only the few workgroup reductions need barriers.
@@ -245,6 +300,14 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
                sm.mrow[i] = t.m;
              });
   __syncthreads();
+  if (nb <= 64) {
+    if (tid < 64) {
+      const bool ok = decide_one_wave(a, b, r0, nb, tau, sm);
+      if (tid == 0) sm.done = ok;
+    }
+    __syncthreads();
+    if (sm.done) return;
+  }
   for (int i = tid; i < nb; i += kScanThreads) {
     if (!(sm.st[i] & kInE)) {
       sm.cf[i] = -__builtin_huge_val();

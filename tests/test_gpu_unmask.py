@@ -223,3 +223,17 @@ def test_scan_then_decide_equals_select():
         outs.append([z.cpu().numpy() for z in (m, t, c, nc)])
     for u, w in zip(*outs):
         assert np.array_equal(u, w, equal_nan=True) if u.dtype.kind == "f" else np.array_equal(u, w)
+
+
+@pytest.mark.parametrize("sizes", [[64], [65], [200, 64, 1], [63, 2, 129]])
+def test_block_sizes_around_one_wave(sizes):
+    # blocks of up to 64 rows are decided by one wave, larger ones by the
+    # whole workgroup; both must agree with the oracle, with confident rows
+    # planted so that both the threshold and the ranking branches run
+    R, V = sum(sizes), 3000
+    x = synth.logits(80 + len(sizes), R, V, 4.0, 0)
+    synth.plant_peaks(x, 80 + len(sizes), 0.25, 12.0, 0)
+    off = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    masked = (np.random.default_rng(80 + R).random(R) < 0.8).astype(np.uint8)
+    nb = len(sizes)
+    compare(x, off, [FULL, SEMI, FULL, FULL][:nb], [5, 1, 3, 2][:nb], 0.9, masked, np.zeros(R, np.int32))
