@@ -10,7 +10,7 @@
 //     disagrees (scaffold rows pass) -> accept length and bonus token.
 //
 // Two kernels per call.  The scan is one pass over HBM: a (chunk, row) grid
-// where each workgroup reads 16384 logits with 16-byte loads (16 per lane,
+// where each workgroup reads 8192 logits with 16-byte loads (8 per lane,
 // all in flight before any arithmetic), reduces max / argmax / exp-sum inside
 // the wave and across the 4 waves, and leaves one 16-byte partial.  Rows that
 // need no scan (already revealed, or outside the verified range) skip the
