@@ -38,7 +38,7 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 
 // ------------------------------------------------------------ attention plan
 struct Plan {
-  int waves, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  int waves, cols, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
   size_t o_bytes, ml_bytes, total_bytes;
 };
 
@@ -107,10 +107,13 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   const bool fork = priv != nullptr;
   const int groups = fork ? Hkv : S * Hkv;
   const int rows_group = fork ? S * R * group : R * group;
-  // Few row tiles (small batch): 2-wave workgroups double the tiles, so the
-  // key range needs half as many splits for the same parallelism.
-  p->waves = groups * ((rows_group + 127) / 128) < 32 ? 2 : 4;
-  const int tile_rows = p->waves * kAttnRowsPerWave;
+  // Row tiles of 128 rows (4 waves x 32).  With few row tiles (small
+  // batch) the tiles halve to 64 rows: bf16 as 4 waves x 16 rows, which
+  // also halves each wave's per-tile dependency chain; fp32 as 2 waves x 32.
+  const bool small = groups * ((rows_group + 127) / 128) < 32;
+  if (prefix->dtype == BC_BF16) { p->waves = 4; p->cols = small ? 1 : 2; }
+  else { p->waves = small ? 2 : 4; p->cols = 2; }
+  const int tile_rows = p->waves * p->cols * 16;
   p->n_mt_prefix = (rows_group + tile_rows - 1) / tile_rows;
   p->n_mt_active = (R * group + tile_rows - 1) / tile_rows;
   int maxlen = 0;
@@ -245,6 +248,7 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   args->group = a->n_q_heads / prefix->n_kv_heads;
   args->D = D;
   args->waves = p.waves;
+  args->cols = p.cols;
   args->fork = priv ? 1 : 0;
   args->causal = mask == BC_MASK_BLOCK_CAUSAL;
   args->n_splits = p.P;

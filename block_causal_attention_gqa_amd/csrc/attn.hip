@@ -10,8 +10,9 @@
 //
 // Work decomposition.  Query rows are grouped per KV head: row m of a group
 // is (sequence, active row, query head within the GQA group), so one K/V
-// stream serves all `group` query heads.  A workgroup (2 or 4 waves x 32
-// rows) takes one row tile against one key range and writes an unnormalised
+// stream serves all `group` query heads.  A workgroup (bf16: 4 waves x 16
+// or 32 rows; fp32: 2 or 4 waves x 32 rows) takes one row tile against one
+// key range and writes an unnormalised
 // partial (reference max, sum, output) to its slot:
 //   * prefix items: slot p < P covers chunk p of the committed prefix; under
 //     a fork the tile runs over the rows of ALL rollouts, so the shared prefix
@@ -198,11 +199,11 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
 
 // this lane's two query columns: validity, output row, and the end of the
 // active keys it may see
-template <typename T>
-__device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0, int n, bool (&valid)[2],
-                                 int (&orow)[2], int (&lim)[2]) {
+template <int CT, typename T>
+__device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0, int n, bool (&valid)[CT],
+                                 int (&orow)[CT], int (&lim)[CT]) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CT; ++c) {
     const int m = row0 + c * 16 + n;
     valid[c] = m < it.rows_in_group;
     int s = it.s_item, rem = m;
@@ -228,13 +229,13 @@ __device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0,
 // by more than kRescaleSlack (log2 units), so after the first tiles the
 // accumulator is almost never rescaled; probabilities stay below
 // 2^kRescaleSlack and o, l and m stay consistent, so o / l is unchanged.
-template <bool kBf16, int D>
-__device__ inline void softmax_tile(f32x4 (&st)[2][4], f32x4 (&o)[2][D / 16], float (&m_run)[2],
-                                    float (&l_run)[2], const int (&lim)[2], int jj, int kb, int nkeys,
+template <bool kBf16, int D, int CT>
+__device__ inline void softmax_tile(f32x4 (&st)[CT][4], f32x4 (&o)[CT][D / 16], float (&m_run)[CT],
+                                    float (&l_run)[CT], const int (&lim)[CT], int jj, int kb, int nkeys,
                                     bool masked, float sl2) {
   const bool full_tile = !masked && kb + kAttnKeyTile <= nkeys;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CT; ++c) {
     float tmax = kNegInf;
     if (!full_tile) {
       // visible iff key < nkeys (and key < lim for the active keys); with
@@ -275,12 +276,12 @@ __device__ inline void softmax_tile(f32x4 (&st)[2][4], f32x4 (&o)[2][D / 16], fl
 }
 
 // this item's partial for the lane's two columns
-template <int D>
-__device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[2], const int (&orow)[2],
-                                     const float (&m_run)[2], const float (&l_run)[2],
-                                     const f32x4 (&o)[2][D / 16], int jj) {
+template <int D, int CT>
+__device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
+                                     const float (&m_run)[CT], const float (&l_run)[CT],
+                                     const f32x4 (&o)[CT][D / 16], int jj) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CT; ++c) {
     float l = l_run[c];
     l += wave_xor(l, 16);
     l += wave_xor(l, 32);
@@ -294,7 +295,8 @@ __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&v
 }
 
 // ============================================================ bf16 partial
-template <int D, int NW>
+// NW waves, each with CT column tiles of 16 query rows.
+template <int D, int NW, int CT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_bf16_kernel(const AttnArgs a) {
   constexpr int KT = kAttnKeyTile;
@@ -304,7 +306,8 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   constexpr int NT = NW * 64;          // threads
   static_assert(TB % (NT * 16) == 0, "tile chunks must split evenly over the threads");
   constexpr int LPT = TB / (NT * 16);  // 16-byte chunks per thread, tile and tensor
-  constexpr int kTileRows = NW * kAttnRowsPerWave;
+  constexpr int kWaveRows = 16 * CT;
+  constexpr int kTileRows = NW * kWaveRows;
   // two stages: tile j + 1 is written while tile j is read
   __shared__ __attribute__((aligned(16))) uint8_t k_st0[TB], k_st1[TB], v_st0[TB], v_st1[TB];
 
@@ -314,27 +317,31 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   const int n = lane & 15, jj = lane >> 4;
 
   const Item<bf16_t> it = decode_item<bf16_t>(a, item_of_block(a));
-  bool valid[2];
-  int orow[2], lim[2];
-  lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
+  bool valid[CT];
+  int orow[CT], lim[CT];
+  lane_rows<CT>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
 
   // ---- Q^T operand, resident for the whole item
   const bf16_t* q = static_cast<const bf16_t*>(a.q);
   constexpr int QK = D / 32;
-  bf16x8 qop[2][QK];
+  bf16x8 qop[CT][QK];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
     for (int kk = 0; kk < QK; ++kk) {
       const bf16x8 z = {};
       qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
     }
 
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 o[2][D / 16];
+  float m_run[CT], l_run[CT];
+  f32x4 o[CT][D / 16];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < CT; ++c) {
+    m_run[c] = kNegInf;
+    l_run[c] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -406,9 +413,9 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     const BC_LDS uint8_t* vs = (const BC_LDS uint8_t*)(decltype(stage)::value ? v_st1 : v_st0);
 
     // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
-    f32x4 st[2][4];
+    f32x4 st[CT][4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int t = 0; t < 4; ++t) st[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -420,16 +427,16 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < QK; ++kk)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < CT; ++c)
           st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[c][kk], st[c][t], 0, 0, 0);
     }
 
-    softmax_tile<true, D>(st, o, m_run, l_run, lim, jj, kb, nk, msk, sl2);
+    softmax_tile<true, D, CT>(st, o, m_run, l_run, lim, jj, kb, nk, msk, sl2);
 
     // ---- O^T += V^T P^T
-    bf16x8 pb[2][2];
+    bf16x8 pb[CT][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -455,7 +462,7 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int c = 0; c < CT; ++c)
             o[c][dt0 + d4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d4][s2], pb[c][s2], o[c][dt0 + d4], 0, 0, 0);
     }
   };
@@ -488,7 +495,7 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     }
   }
 
-  write_partial<D>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  write_partial<D, CT>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // ============================================================ fp32 partial
@@ -501,7 +508,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   constexpr int NT = NW * 64;
   constexpr int KT = kAttnKeyTile;
   constexpr int KP = D + 4;                    // LDS row pitch (elements)
-  constexpr int kTileRows = NW * kAttnRowsPerWave;
+  constexpr int kWaveRows = 32;                // 2 column tiles of 16 rows
+  constexpr int kTileRows = NW * kWaveRows;
   __shared__ __attribute__((aligned(16))) float k_lds[KT * KP];
   __shared__ __attribute__((aligned(16))) float v_lds[KT * KP];
 
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   const Item<float> it = decode_item<float>(a, item_of_block(a));
   bool valid[2];
   int orow[2], lim[2];
-  lane_rows(a, it, it.mt * kTileRows + wave * kAttnRowsPerWave, n, valid, orow, lim);
+  lane_rows<2>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
 
   const float* q = static_cast<const float*>(a.q);
   constexpr int QK = D / 4;
@@ -570,7 +578,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
         for (int c = 0; c < 2; ++c)
           st[c][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, qop[c][kk], st[c][t], 0, 0, 0);
       }
-    softmax_tile<false, D>(st, o, m_run, l_run, lim, jj, kb, nkeys, masked, sl2);
+    softmax_tile<false, D, 2>(st, o, m_run, l_run, lim, jj, kb, nkeys, masked, sl2);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
@@ -600,7 +608,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
     }
   }
 
-  write_partial<D>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  write_partial<D, 2>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
@@ -696,10 +704,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
 
 template <int D>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
-  if (a.waves == 2)
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
+  if (a.cols == 1)
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1>), dim3(a.n_items), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 2>), dim3(a.n_items), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

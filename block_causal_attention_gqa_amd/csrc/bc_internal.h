@@ -10,7 +10,6 @@
 namespace bc {
 
 // ---------------------------------------------------------------- attention
-constexpr int kAttnRowsPerWave = 32;      // query rows per wave (2 MFMA column tiles)
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 
 struct AttnArgs {
@@ -28,7 +27,8 @@ struct AttnArgs {
   float2* ws_ml;       // [n_slots][rows_total] (running max in log2 units, sum)
   float scale_log2;    // softmax scale * log2(e)
   int S, R, Hq, Hkv, group, D;
-  int waves;           // waves per workgroup (2 or 4); a row tile is waves * 32 rows
+  int waves;           // waves per workgroup (2 or 4)
+  int cols;            // 16-row MFMA column tiles per wave (1 or 2); a row tile is waves * cols * 16 rows
   int fork;            // 1: one shared prefix for all S rollouts + private caches
   int causal;          // bc_mask
   int n_splits;        // prefix chunks P; slot P holds private + active keys
