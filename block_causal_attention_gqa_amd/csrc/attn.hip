@@ -275,7 +275,8 @@ __device__ inline void softmax_tile(f32x4 (&st)[CT][4], f32x4 (&o)[CT][D / 16], 
   }
 }
 
-// this item's partial for the lane's two columns
+// this item's partial for the lane's columns.  Non-temporal stores: the
+// partials are read once, by the combine, so they are not kept in L2.
 template <int D, int CT>
 __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
                                      const float (&m_run)[CT], const float (&l_run)[CT],
@@ -287,10 +288,13 @@ __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&v
     l += wave_xor(l, 32);
     if (!valid[c]) continue;
     const long long prow = (long long)slot * a.rows_total + orow[c];
-    if (jj == 0) a.ws_ml[prow] = float2{m_run[c], l};
+    if (jj == 0) {
+      __builtin_nontemporal_store(m_run[c], &a.ws_ml[prow].x);
+      __builtin_nontemporal_store(l, &a.ws_ml[prow].y);
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<f32x4*>(&a.ws_o[prow * D + 16 * dt + 4 * jj]) = o[c][dt];
+      __builtin_nontemporal_store(o[c][dt], reinterpret_cast<f32x4*>(&a.ws_o[prow * D + 16 * dt + 4 * jj]));
   }
 }
 

@@ -48,15 +48,48 @@ __device__ inline Acc merge(Acc x, Acc y) {
   return r;
 }
 
+// Lane exchanges for the butterfly merges, all in VALU (no LDS round trip):
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 1 and 2 apart; once each
+// quad (half row) holds one value, row_half_mirror (row_mirror) pairs it with
+// the neighbouring quad (half row); v_permlane16_swap / v_permlane32_swap
+// with both operands x return the two halves of each 16 (32) lane pair.
+template <int kStep>
+__device__ inline uint32_t lane_xchg(uint32_t x) {
+  if constexpr (kStep == 0) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (kStep == 1) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (kStep == 2) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+  else if constexpr (kStep == 3) return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);
+  else {
+    // the other half of the pair: swap returns (lower half, upper half) in
+    // every lane, so the partner is whichever of the two is not this lane's
+    const auto p = kStep == 4 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const int bit = kStep == 4 ? 16 : 32;
+    return (threadIdx.x & bit) ? (uint32_t)p[0] : (uint32_t)p[1];
+  }
+}
+
+template <int kStep>
+__device__ inline Acc merge_step(Acc x) {
+  Acc y;
+  y.m = __builtin_bit_cast(float, lane_xchg<kStep>(__builtin_bit_cast(uint32_t, x.m)));
+  y.a = (int)lane_xchg<kStep>((uint32_t)x.a);
+  y.s = __builtin_bit_cast(float, lane_xchg<kStep>(__builtin_bit_cast(uint32_t, x.s)));
+  return merge(x, y);
+}
+
+// Merge over aligned groups of kWidth lanes (8 or 64); every lane of a group
+// ends with the group's result.
 template <int kWidth>
 __device__ inline Acc lanes_merge(Acc x) {
-#pragma unroll
-  for (int off = kWidth / 2; off > 0; off >>= 1) {
-    Acc y;
-    y.m = __shfl_xor(x.m, off, 64);
-    y.a = __shfl_xor(x.a, off, 64);
-    y.s = __shfl_xor(x.s, off, 64);
-    x = merge(x, y);
+  static_assert(kWidth == 8 || kWidth == 64, "group width");
+  x = merge_step<0>(x);
+  x = merge_step<1>(x);
+  x = merge_step<2>(x);
+  if constexpr (kWidth == 64) {
+    x = merge_step<3>(x);
+    x = merge_step<4>(x);
+    x = merge_step<5>(x);
   }
   return x;
 }
