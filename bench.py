@@ -350,6 +350,13 @@ def legs(stream):
         rec["verify"] = {"us": round(vus, 3), "GB_s": round(vbytes / vus / 1e3, 1),
                          "hbm_frac": round(vbytes / vus / 1e3 / HBM_PEAK_GBS, 4)}
         rec["round_us"] = round(graph_us(lambda: fv.run(stream), stream, reps=4), 3)
+        if N == 64:
+            # trajectory-only sampling: the verify also reads the Gumbel noise
+            fs = decode.ForkVerify(N, seed=0, device="cuda:0", block=0, temperature=0.7)
+            sus = graph_us(lambda: fs.verify(stream), stream)
+            rec["verify_sampled"] = {"us": round(sus, 3), "GB_s": round(2 * vbytes / sus / 1e3, 1),
+                                     "hbm_frac": round(2 * vbytes / sus / 1e3 / HBM_PEAK_GBS, 4)}
+            del fs
         fork.append(rec)
         del fv
         torch.cuda.empty_cache()

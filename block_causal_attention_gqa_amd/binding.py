@@ -36,8 +36,8 @@ BC_MAX_BLOCK_ROWS = 1024
 BC_MAX_SCAN_ROWS = 4096
 
 EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
-            "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_status_str",
-            "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide")
+            "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
+            "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -96,6 +96,8 @@ def lib():
     L.bc_verify_workspace_bytes.restype = sz
     L.bc_spec_verify.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.bc_spec_verify.restype = ctypes.c_int
+    L.bc_spec_verify_sampled.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.bc_spec_verify_sampled.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -290,6 +292,21 @@ def _unmask_call(name, logits, blk_off, mode, n_div, threshold, masked, tokens, 
 
 def bc_verify_workspace_bytes(n_seq, n_lrows, vocab):
     return int(lib().bc_verify_workspace_bytes(int(n_seq), int(n_lrows), int(vocab)))
+
+
+def bc_spec_verify_sampled(logits, noise, inv_temperature, draft, fixed, first, accept_len, bonus, ws,
+                           stream=None, check=True):
+    S, L, V = (int(x) for x in logits.shape)
+    m = int(draft.shape[1])
+    st = lib().bc_spec_verify_sampled(
+        _dev(logits, "logits", torch.float32, S * L * V), _dev(noise, "noise", torch.float32, S * L * V),
+        ctypes.c_float(inv_temperature), S, L, V, _dev(draft, "draft", torch.int32, S * m), m,
+        _dev(fixed, "fixed", torch.uint8, S * m, allow_none=True), _dev(first, "first", torch.int32, S),
+        _dev(accept_len, "accept_len", torch.int32, S), _dev(bonus, "bonus", torch.int32, S),
+        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_spec_verify_sampled")
+    return st
 
 
 def bc_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=None, check=True):

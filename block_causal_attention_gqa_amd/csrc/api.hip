@@ -283,6 +283,36 @@ int validate_unmask(const float* logits, int32_t n_rows, int32_t vocab, const in
   return BC_OK;
 }
 
+// Verify with the row tokens t_i = argmax(l_i * inv_t + g_i) (g null:
+// argmax l_i).
+int spec_verify(const float* logits, const float* noise, float inv_t, int32_t n_seq, int32_t n_lrows, int32_t vocab,
+                const int32_t* draft, int32_t m, const uint8_t* fixed, const int32_t* first, int32_t* accept_len,
+                int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !draft || !first || !accept_len || !bonus) return BC_ERR_ARG;
+  if (n_seq < 1 || n_lrows < 1 || vocab < 1 || m < 1 || m > n_lrows) return BC_ERR_ARG;
+  if ((long long)n_seq * n_lrows > BC_MAX_SCAN_ROWS) return BC_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < bc_verify_workspace_bytes(n_seq, n_lrows, vocab)) return BC_ERR_WORKSPACE;
+  VerifyArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.logits = logits;
+  args.noise = noise;
+  args.inv_temperature = inv_t;
+  args.n_seq = n_seq;
+  args.n_lrows = n_lrows;
+  args.vocab = vocab;
+  args.n_chunks = scan_chunks(vocab);
+  args.m = m;
+  args.draft = draft;
+  args.fixed = fixed;
+  args.first = first;
+  args.accept_len = accept_len;
+  args.bonus = bonus;
+  args.part = static_cast<ScanPartial*>(ws);
+  (void)hipGetLastError();
+  if (launch_verify(args, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
 void fill_unmask(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
                  const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
                  float* conf, int32_t* n_commit, void* ws, UnmaskArgs* args) {
@@ -400,27 +430,18 @@ size_t bc_verify_workspace_bytes(int32_t n_seq, int32_t n_lrows, int32_t vocab) 
 int bc_spec_verify(const float* logits, int32_t n_seq, int32_t n_lrows, int32_t vocab, const int32_t* draft,
                    int32_t m, const uint8_t* fixed, const int32_t* first, int32_t* accept_len,
                    int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
-  if (!logits || !draft || !first || !accept_len || !bonus) return BC_ERR_ARG;
-  if (n_seq < 1 || n_lrows < 1 || vocab < 1 || m < 1 || m > n_lrows) return BC_ERR_ARG;
-  if ((long long)n_seq * n_lrows > BC_MAX_SCAN_ROWS) return BC_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < bc_verify_workspace_bytes(n_seq, n_lrows, vocab)) return BC_ERR_WORKSPACE;
-  VerifyArgs args;
-  std::memset(&args, 0, sizeof(args));
-  args.logits = logits;
-  args.n_seq = n_seq;
-  args.n_lrows = n_lrows;
-  args.vocab = vocab;
-  args.n_chunks = scan_chunks(vocab);
-  args.m = m;
-  args.draft = draft;
-  args.fixed = fixed;
-  args.first = first;
-  args.accept_len = accept_len;
-  args.bonus = bonus;
-  args.part = static_cast<ScanPartial*>(ws);
-  (void)hipGetLastError();
-  if (launch_verify(args, static_cast<hipStream_t>(stream)) != hipSuccess) return BC_ERR_HIP;
-  return BC_OK;
+  return spec_verify(logits, nullptr, 1.f, n_seq, n_lrows, vocab, draft, m, fixed, first, accept_len, bonus, ws,
+                     ws_bytes, stream);
+}
+
+int bc_spec_verify_sampled(const float* logits, const float* noise, float inv_temperature, int32_t n_seq,
+                           int32_t n_lrows, int32_t vocab, const int32_t* draft, int32_t m, const uint8_t* fixed,
+                           const int32_t* first, int32_t* accept_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!noise) return BC_ERR_ARG;
+  if (!std::isfinite(inv_temperature) || !(inv_temperature > 0.f)) return BC_ERR_ARG;
+  return spec_verify(logits, noise, inv_temperature, n_seq, n_lrows, vocab, draft, m, fixed, first, accept_len,
+                     bonus, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -90,6 +90,8 @@ struct VerifyArgs {
   int* accept_len;
   int* bonus;
   ScanPartial* part;   // [n_seq * n_lrows][n_chunks]
+  const float* noise;  // [n_seq][n_lrows][vocab] Gumbel noise, or null (greedy)
+  float inv_temperature;
 };
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);

@@ -7,7 +7,10 @@
 //     top-k rows by (confidence desc, row asc).
 //   verify (Fast-dDrive method summary 3.2, Scaffold Speculative decoding):
 //     per row the lowest argmax, then the first row from `first` whose draft
-//     disagrees (scaffold rows pass) -> accept length and bonus token.
+//     disagrees (scaffold rows pass) -> accept length and bonus token.  The
+//     sampled variant (sec. 3.3, trajectory-only sampling) takes the argmax
+//     of l / T + g with caller-supplied Gumbel noise g (Gumbel-max: a draw
+//     from softmax(l / T)).
 //
 // Two kernels per call.  The scan is one pass over HBM: a (chunk, row) grid
 // where each workgroup reads 8192 logits with 16-byte loads (8 per lane,
@@ -96,9 +99,12 @@ __device__ inline Acc lanes_merge(Acc x) {
 
 // One (chunk, row) partial: max, lowest argmax and (kSum) exp-sum of
 // logits[row][chunk * kScanChunk ...], written by thread 0.
-template <bool kSum, bool kVec>
+// With kNoise the value scanned is l * inv_t + g (g from noisep at the same
+// index): one float32 multiply and one float32 add, each rounded, never
+// contracted into an FMA, so a float32 reference reproduces every value.
+template <bool kSum, bool kVec, bool kNoise = false>
 __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk, ScanPartial* out,
-                           Acc* red) {
+                           Acc* red, const float* __restrict__ noisep = nullptr, float inv_t = 1.f) {
   const int tid = threadIdx.x;
   const int c0 = chunk * kScanChunk;
   const int c1 = min(vocab, c0 + kScanChunk);
@@ -109,14 +115,26 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
     for (int it = 0; it < kScanVecPerThread; ++it) {
       const int idx = c0 + 4 * (tid + kScanThreads * it);
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
-      if (idx < c1) x = *reinterpret_cast<const float4*>(rowp + idx);
+      if (idx < c1) {
+        x = *reinterpret_cast<const float4*>(rowp + idx);
+        if constexpr (kNoise) {
+          const float4 g = *reinterpret_cast<const float4*>(noisep + idx);
+          x = float4{__fadd_rn(__fmul_rn(x.x, inv_t), g.x), __fadd_rn(__fmul_rn(x.y, inv_t), g.y),
+                     __fadd_rn(__fmul_rn(x.z, inv_t), g.z), __fadd_rn(__fmul_rn(x.w, inv_t), g.w)};
+        }
+      }
       v[4 * it] = x.x; v[4 * it + 1] = x.y; v[4 * it + 2] = x.z; v[4 * it + 3] = x.w;
     }
   } else {
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
       const int idx = c0 + tid + kScanThreads * e;
-      v[e] = idx < c1 ? rowp[idx] : kNegInf;
+      float x = kNegInf;
+      if (idx < c1) {
+        x = rowp[idx];
+        if constexpr (kNoise) x = __fadd_rn(__fmul_rn(x, inv_t), noisep[idx]);
+      }
+      v[e] = x;
     }
   }
   Acc acc{kNegInf, INT_MAX, 0.f};
@@ -146,12 +164,13 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
 
 // mode 0: rows with row_mask[row] != 0 (all rows when row_mask is null);
 // mode 1: verify, row (s, i) with first[s] <= i <= min(m, n_lrows - 1).
-template <int kMode, bool kSum, bool kVec>
+template <int kMode, bool kSum, bool kVec, bool kNoise = false>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restrict__ logits, int vocab,
                                                              int n_chunks, ScanPartial* __restrict__ part,
                                                              const uint8_t* __restrict__ row_mask,
                                                              const int* __restrict__ first, int n_lrows,
-                                                             int m) {
+                                                             int m, const float* __restrict__ noise = nullptr,
+                                                             float inv_t = 1.f) {
   __shared__ Acc red[kScanThreads / 64];
   const int chunk = blockIdx.x, row = blockIdx.y;
   if constexpr (kMode == 0) {
@@ -161,8 +180,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
     const int f = min(max(first[s], 0), m);
     if (i < f || i > min(m, n_lrows - 1)) return;
   }
-  scan_chunk<kSum, kVec>(logits + (long long)row * vocab, vocab, chunk,
-                         &part[(long long)row * n_chunks + chunk], red);
+  scan_chunk<kSum, kVec, kNoise>(logits + (long long)row * vocab, vocab, chunk,
+                                 &part[(long long)row * n_chunks + chunk], red,
+                                 kNoise ? noise + (long long)row * vocab : nullptr, inv_t);
 }
 
 // Merge the chunk partials of rows r0 .. r0 + nr - 1 that `want(i)`:
@@ -490,7 +510,14 @@ hipError_t launch_unmask_decide(const UnmaskArgs& a, hipStream_t stream) {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_chunks, a.n_seq * a.n_lrows);
-  if (a.vocab % 4 == 0)
+  const bool vec = a.vocab % 4 == 0;
+  if (a.noise && vec)
+    hipLaunchKernelGGL((scan_kernel<1, false, true, true>), grid, dim3(kScanThreads), 0, stream, a.logits, a.vocab,
+                       a.n_chunks, a.part, nullptr, a.first, a.n_lrows, a.m, a.noise, a.inv_temperature);
+  else if (a.noise)
+    hipLaunchKernelGGL((scan_kernel<1, false, false, true>), grid, dim3(kScanThreads), 0, stream, a.logits,
+                       a.vocab, a.n_chunks, a.part, nullptr, a.first, a.n_lrows, a.m, a.noise, a.inv_temperature);
+  else if (vec)
     hipLaunchKernelGGL((scan_kernel<1, false, true>), grid, dim3(kScanThreads), 0, stream, a.logits, a.vocab,
                        a.n_chunks, a.part, nullptr, a.first, a.n_lrows, a.m);
   else

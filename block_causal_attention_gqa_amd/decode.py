@@ -137,13 +137,16 @@ class ForkVerify:
          masked row, token = argmax of its draft logits;
       3. verify pass: causal attention of the same rows;
       4. speculative verify of the drafts against the verify logits, scaffold
-         rows accepted as they are.
+         rows accepted as they are; with a temperature, the verify samples
+         its tokens (trajectory-only sampling, sec. 3.3) by Gumbel-max over
+         seeded per-rollout noise.
 
     Logits, the rows' Q/K/V and the private caches are seeded synthetic
     tensors made up-front and resident on the device; the drafts the verify
     call checks are the tokens step 2 produced."""
 
-    def __init__(self, n_rollouts, seed=0, device="cuda:0", block=0, scaffold_frac=0.3, preset=None):
+    def __init__(self, n_rollouts, seed=0, device="cuda:0", block=0, scaffold_frac=0.3, preset=None,
+                 temperature=None):
         p = dict(preset or synth.PRESETS["fork"])
         self.N = n_rollouts
         self.Hq, self.Hkv, self.D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
@@ -170,6 +173,12 @@ class ForkVerify:
             synth.logits(seed, N * R, self.V, self.sigma, 300 + block)).to(device).view(N, R, self.V)
         g = synth.rng(seed, "misc", 400 + block)
         self.fixed = torch.from_numpy((g.random((N, R)) < scaffold_frac).astype(np.uint8)).to(device)
+        # trajectory-only sampling (method summary sec. 3.3): the verify
+        # samples softmax(l / T) through Gumbel-max on per-rollout noise
+        self.temperature = temperature
+        self.noise = None
+        if temperature is not None:
+            self.noise = torch.from_numpy(synth.gumbel(seed, (N, R, self.V), 500 + block)).to(device)
         tdt = synth.torch_dtype(self.dtype)
         self.out = torch.empty((N, R, Hq, D), dtype=tdt, device=device)
         self.masked = torch.ones(N * R, dtype=torch.uint8, device=device)
@@ -196,7 +205,10 @@ class ForkVerify:
         for pass_id in (0, 1):
             (_, q), (_, k), (_, v) = synth.active_qkv(seed, N, R, Hq, Hkv, D, self.dtype, 100 + block, pass_id)
             qkv[pass_id] = (q, k, v)
-        return dict(pk=pk, pv=pv, vk=vk, vv=vv, qkv=qkv,
+        noise = None
+        if self.temperature is not None:
+            noise = synth.gumbel(seed, (N, R, self.V), 500 + block)
+        return dict(pk=pk, pv=pv, vk=vk, vv=vv, qkv=qkv, noise=noise,
                     draft_logits=synth.logits(seed, N * R, self.V, self.sigma, 200 + block),
                     verify_logits=synth.logits(seed, N * R, self.V, self.sigma, 300 + block).reshape(N, R, self.V),
                     fixed=self.fixed.cpu().numpy())
@@ -213,8 +225,13 @@ class ForkVerify:
                            self.masked, self.tokens, None, self.n_commit, self.ws_unmask, stream=stream)
 
     def verify(self, stream=None):
-        B.bc_spec_verify(self.verify_logits, self.tokens.view(self.N, self.R), self.fixed, self.first,
-                         self.accept_len, self.bonus, self.ws_verify, stream=stream)
+        if self.noise is not None:
+            B.bc_spec_verify_sampled(self.verify_logits, self.noise, 1.0 / self.temperature,
+                                     self.tokens.view(self.N, self.R), self.fixed, self.first, self.accept_len,
+                                     self.bonus, self.ws_verify, stream=stream)
+        else:
+            B.bc_spec_verify(self.verify_logits, self.tokens.view(self.N, self.R), self.fixed, self.first,
+                             self.accept_len, self.bonus, self.ws_verify, stream=stream)
 
     def run(self, stream=None):
         self.attention(0, stream)

@@ -21,7 +21,7 @@ import torch
 _TAGS = {
     "prefix_k": 1, "prefix_v": 2, "q": 3, "k": 4, "v": 5, "logits": 6,
     "priv_k": 7, "priv_v": 8, "draft": 9, "peak": 10, "ratio": 11,
-    "subset": 12, "commit_k": 13, "commit_v": 14, "misc": 15,
+    "subset": 12, "commit_k": 13, "commit_v": 14, "misc": 15, "gumbel": 16,
 }
 
 
@@ -169,3 +169,11 @@ def drafts_with_agreement(seed, target, p_agree, vocab, *idx):
             alt = int(g.integers(vocab - 1))
             d[i] = alt if alt < target[i] else alt + 1
     return d
+
+
+def gumbel(seed, shape, *idx):
+    """float32 Gumbel(0, 1) noise, -log(-log U) with U uniform in (0, 1),
+    for the sampled verify (the random numbers the method draws are inputs)."""
+    u = rng(seed, "gumbel", *idx).random(shape)
+    u = np.clip(u, np.finfo(np.float64).tiny, 1.0 - 2.0 ** -53)
+    return (-np.log(-np.log(u))).astype(np.float32)

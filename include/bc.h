@@ -225,6 +225,27 @@ int bc_spec_verify(const float *logits, int32_t n_seq, int32_t n_lrows, int32_t 
                    const int32_t *first, int32_t *accept_len, int32_t *bonus,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* Scaffold speculative verify with a sampled AR pass.
+ * Fast-dDrive method summary sec. 3.3, design principle one (and the
+ * Fast-dDrive paper's introduction): the trajectory section samples the AR
+ * verifier instead of taking its argmax, to fork diverse rollouts.  The
+ * sample is Gumbel-max over caller-supplied noise, so it is reproducible:
+ *   t_i = argmax_v (logits[s][i][v] * inv_temperature + noise[s][i][v])
+ * (lowest index on ties), one float32 multiply and one float32 add, each
+ * rounded, no fused multiply-add; with noise drawn as -log(-log U), U
+ * uniform in (0, 1), t_i is a draw from softmax(logits / temperature).
+ * Everything else is bc_spec_verify.
+ *
+ *   noise            [n_seq][n_lrows][vocab] float32, finite
+ *   inv_temperature  1 / temperature, finite and > 0
+ * Errors: as bc_spec_verify; BC_ERR_ARG for a NULL noise or a bad
+ * inv_temperature. */
+int bc_spec_verify_sampled(const float *logits, const float *noise, float inv_temperature,
+                           int32_t n_seq, int32_t n_lrows, int32_t vocab,
+                           const int32_t *draft, int32_t m, const uint8_t *fixed,
+                           const int32_t *first, int32_t *accept_len, int32_t *bonus,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sub-steps, exported so that each kernel can be timed or scheduled on its
  * own.  They take exactly the arguments of the call they make up and must

@@ -59,3 +59,26 @@ def spec_verify(logits, draft, fixed, first):
         acc[s], bon[s] = spec_verify_one(
             logits[s], draft[s], None if fixed is None else fixed[s], int(first[s]))
     return acc, bon
+
+
+# ---------------------------------------------------------------------------
+# Trajectory-only sampling (Fast-dDrive method summary sec. 3.3, design
+# principle one): in the trajectory section the AR verifier samples from
+# softmax(l / T) instead of taking its argmax.  The sample is taken with the
+# Gumbel-max construction on caller-supplied noise g ~ Gumbel(0, 1):
+# argmax_v (l_v / T + g_v) is distributed as softmax(l / T).  Reading: the
+# library's definition of the perturbed value is one float32 multiply by
+# 1 / T and one float32 add, each rounded to nearest (numpy float32 scalar
+# arithmetic is IEEE single precision, so this is that definition).
+
+def perturbed_row(row, noise, inv_temperature):
+    """float32 l * inv_temperature + g, each operation rounded to float32."""
+    x = np.asarray(row, dtype=np.float32) * np.float32(inv_temperature)
+    return (x.astype(np.float32) + np.asarray(noise, dtype=np.float32)).astype(np.float32)
+
+
+def spec_verify_sampled(logits, noise, inv_temperature, draft, fixed, first):
+    """spec_verify with every row's token taken from the perturbed row."""
+    pert = np.stack([np.stack([perturbed_row(logits[s, i], noise[s, i], inv_temperature)
+                               for i in range(logits.shape[1])]) for s in range(logits.shape[0])])
+    return spec_verify(pert, draft, fixed, first)

@@ -18,12 +18,12 @@ def _lib():
     G.require_lib()
 
 
-@pytest.mark.parametrize("N,block", [(4, 0), (4, 1), (16, 2)])
-def test_fork_verify_round_matches_oracle(N, block):
+@pytest.mark.parametrize("N,block,temperature", [(4, 0, None), (4, 1, None), (16, 2, None), (4, 2, 0.7)])
+def test_fork_verify_round_matches_oracle(N, block, temperature):
     import torch
     from block_causal_attention_gqa_amd import decode
-    print("fork/verify round N=%d block=%d" % (N, block), flush=True)
-    fv = decode.ForkVerify(N, seed=5, device=G.DEV, block=block)
+    print("fork/verify round N=%d block=%d T=%s" % (N, block, temperature), flush=True)
+    fv = decode.ForkVerify(N, seed=5, device=G.DEV, block=block, temperature=temperature)
     h = fv.host_inputs(seed=5, block=block)
     R = fv.R
     for pass_id, mode in ((0, OA.MASK_BIDIR), (1, OA.MASK_CAUSAL)):
@@ -45,6 +45,10 @@ def test_fork_verify_round_matches_oracle(N, block):
     assert np.array_equal(fv.n_commit.cpu().numpy(), n_want)
     fv.verify()
     torch.cuda.synchronize()
-    acc, bon = OV.spec_verify(h["verify_logits"], t_want.reshape(N, R), h["fixed"], np.zeros(N, np.int32))
+    if temperature is None:
+        acc, bon = OV.spec_verify(h["verify_logits"], t_want.reshape(N, R), h["fixed"], np.zeros(N, np.int32))
+    else:
+        acc, bon = OV.spec_verify_sampled(h["verify_logits"], h["noise"], 1.0 / temperature, t_want.reshape(N, R),
+                                          h["fixed"], np.zeros(N, np.int32))
     assert np.array_equal(fv.accept_len.cpu().numpy(), acc)
     assert np.array_equal(fv.bonus.cpu().numpy(), bon)

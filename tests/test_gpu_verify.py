@@ -1,6 +1,8 @@
 """GPU parity of bc_spec_verify against the oracle: accept lengths and bonus
 tokens bit for bit."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -89,3 +91,43 @@ def test_argument_errors():
     a = torch.zeros(1, dtype=torch.int32, device=G.DEV)
     ws = torch.zeros(4096, dtype=torch.uint8, device=G.DEV)
     assert B.bc_spec_verify(lg, d, None, f, a, a.clone(), ws, check=False) == B.BC_ERR_ARG  # m > n_lrows
+
+
+@pytest.mark.parametrize("inv_t", [1.0, 1.0 / 0.7, 2.0])
+@pytest.mark.parametrize("V", [151936, 1001])
+def test_sampled_verify_matches_oracle(inv_t, V):
+    # trajectory-only sampling: Gumbel-max over supplied noise, drafts taken
+    # from the oracle's sampled tokens with 80% agreement
+    S, L, m = 4, 24, 24
+    print("sampled verify V=%d inv_t=%.3f" % (V, inv_t), flush=True)
+    x = synth.logits(70, S * L, V, 4.0, 0).reshape(S, L, V)
+    g = synth.gumbel(70, (S, L, V), 0)
+    t = np.array([[OV.argmax_lowest(OV.perturbed_row(x[s, i], g[s, i], inv_t)) for i in range(L)]
+                  for s in range(S)], np.int32)
+    draft = np.stack([synth.drafts_with_agreement(70, t[s, :m], 0.8, V, s) for s in range(S)])
+    fixed = (np.random.default_rng(70).random((S, m)) < 0.3).astype(np.uint8)
+    first = np.array([0, 3, 10, 24], np.int32)
+    acc = torch.full((S,), -7, dtype=torch.int32, device=G.DEV)
+    bon = torch.full((S,), -7, dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(B.bc_verify_workspace_bytes(S, L, V), dtype=torch.uint8, device=G.DEV)
+    B.bc_spec_verify_sampled(G.to_dev(x), G.to_dev(g), inv_t, G.to_dev(draft), G.to_dev(fixed), G.to_dev(first),
+                             acc, bon, ws)
+    torch.cuda.synchronize()
+    oa, ob = OV.spec_verify_sampled(x, g, inv_t, draft, fixed, first)
+    assert np.array_equal(acc.cpu().numpy(), oa)
+    assert np.array_equal(bon.cpu().numpy(), ob)
+
+
+def test_sampled_verify_argument_errors():
+    S, L, V = 1, 4, 64
+    x = G.to_dev(np.zeros((S, L, V), np.float32))
+    d = G.to_dev(np.zeros((S, L), np.int32))
+    f = G.to_dev(np.zeros(S, np.int32))
+    acc = torch.zeros(S, dtype=torch.int32, device=G.DEV)
+    bon = torch.zeros(S, dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(B.bc_verify_workspace_bytes(S, L, V), dtype=torch.uint8, device=G.DEV)
+    for inv_t in (0.0, -1.0, float("nan"), float("inf")):
+        assert B.bc_spec_verify_sampled(x, x, inv_t, d, None, f, acc, bon, ws, check=False) == B.BC_ERR_ARG
+    st = B.lib().bc_spec_verify_sampled(x.data_ptr(), None, ctypes.c_float(1.0), S, L, V, d.data_ptr(), L, None,
+                                        f.data_ptr(), acc.data_ptr(), bon.data_ptr(), ws.data_ptr(), ws.numel(), None)
+    assert st == B.BC_ERR_ARG

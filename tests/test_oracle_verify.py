@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import verify as V
+from oracle import verify as OV
 
 
 def _planted(n_rows, vocab, targets, seed=0):
@@ -121,3 +122,50 @@ def test_batched_matches_single():
     acc, bon = V.spec_verify(lg, draft, fixed, first)
     for s in range(S):
         assert (acc[s], bon[s]) == V.spec_verify_one(lg[s], draft[s], fixed[s], int(first[s]))
+
+
+# ---- trajectory-only sampling (Gumbel-max over supplied noise)
+
+def test_gumbel_max_frequencies_follow_softmax():
+    # the Gumbel-max construction: argmax(l / T + g), g ~ Gumbel(0, 1), is a
+    # draw from softmax(l / T); checked on 200k seeded draws within 5 sigma
+    from block_causal_attention_gqa_amd import synth
+    l = np.array([1.0, 0.3, -0.5, 2.0, 0.0], np.float32)
+    for T in (1.0, 0.7, 2.5):
+        n = 200_000
+        g = synth.gumbel(3, (n, l.size), int(T * 10))
+        pert = OV.perturbed_row(np.broadcast_to(l, (n, l.size)), g, 1.0 / T)
+        freq = np.bincount(pert.argmax(axis=1), minlength=l.size) / n
+        p = np.exp(l.astype(np.float64) / T)
+        p /= p.sum()
+        sigma = np.sqrt(p * (1 - p) / n)
+        assert np.all(np.abs(freq - p) < 5 * sigma + 1e-12), (T, freq, p)
+
+
+def test_cold_limit_is_the_argmax():
+    from block_causal_attention_gqa_amd import synth
+    l = synth.logits(4, 3, 500, 4.0, 0)
+    g = synth.gumbel(4, (3, 500), 0)
+    for r in range(3):
+        assert OV.argmax_lowest(OV.perturbed_row(l[r], g[r], 1e6)) == OV.argmax_lowest(l[r])
+
+
+def test_perturbed_value_is_rounded_to_float32_before_comparing():
+    # l = (1, 1), g = (0, 2^-25): in float32, 1 + 2^-25 rounds to 1, so the
+    # two values tie and the lowest index wins; in float64 index 1 would win
+    l = np.array([1.0, 1.0], np.float32)
+    g = np.array([0.0, 2.0 ** -25], np.float32)
+    assert OV.argmax_lowest(OV.perturbed_row(l, g, 1.0)) == 0
+    assert np.argmax(l.astype(np.float64) + g.astype(np.float64)) == 1
+
+
+def test_sampled_verify_uses_the_perturbed_tokens():
+    # drafts equal to the perturbed argmax are all accepted; the bonus comes
+    # from the perturbed row
+    from block_causal_attention_gqa_amd import synth
+    S, L, V = 2, 5, 300
+    x = synth.logits(6, S * L, V, 4.0, 0).reshape(S, L, V)
+    g = synth.gumbel(6, (S, L, V), 0)
+    t = np.array([[OV.argmax_lowest(OV.perturbed_row(x[s, i], g[s, i], 0.5)) for i in range(L)] for s in range(S)])
+    acc, bon = OV.spec_verify_sampled(x, g, 0.5, t[:, :4].astype(np.int32), None, np.zeros(S, np.int32))
+    assert list(acc) == [4, 4] and list(bon) == list(t[:, 4])
