@@ -13,7 +13,10 @@ Modules
   kvcache    in-order append of completed blocks to a per-sequence cache
   unmask     per-row max / argmax / softmax confidence and the threshold +
              ceil(remaining / n) fallback selection
-  verify     left-to-right speculative verification (accept length + bonus)
+  verify     left-to-right speculative verification (accept length + bonus),
+             and its sampled form (Gumbel-max over supplied noise)
+  pipeline   the pipelined parallel decoding schedule (semi / fully active
+             blocks, add and activation thresholds, in-order commit)
 
 Sources (the pages the method is described on):
   * "Fast-dDrive" (Chinese translation of arXiv 2605.23163): abstract, sec. 1
