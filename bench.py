@@ -329,8 +329,9 @@ def legs(stream):
     """Secondary measurements on the other workloads of the pages' systems:
     the shared-prefix fork round at N = 4, 16, 64 rollouts (attention there
     is MFMA-bound), the verify scan over N = 64 rollouts' logits (HBM-bound),
-    the large-block decode's attention at batch 16 (HBM-bound), and the
-    duration of a minimal kernel as the launch floor."""
+    the large-block decode's attention at batch 16 (HBM-bound), a
+    pipelined-parallel decode of 625 tokens against the same decode without
+    overlap, and the duration of a minimal kernel as the launch floor."""
     import torch
     from block_causal_attention_gqa_amd import binding as B
     from block_causal_attention_gqa_amd import decode, synth
@@ -383,6 +384,28 @@ def legs(stream):
                                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                    "TFLOP_s": round(flops / us / 1e6, 1), "bytes": nbytes}
     del pk, pv, cache, ws
+    # pipelined parallel decoding of a 625-token output (blocks of 32 and a
+    # last of 17 over a 512-token prefix, 16q/2kv heads, vocab 2048): each
+    # step's commit counts decide the next step's blocks, so the host reads
+    # them back every step and a decode is timed whole on the wall clock,
+    # inputs resident; "sequential" is the same decode without overlap
+    pip = {}
+    for name, kw in (("pipelined", dict(add=0.5, act=0.9)), ("sequential", dict(add=1.0, act=1.0))):
+        pd = decode.PipelinedDecode(seed=0, device="cuda:0", tau=0.5, n_div=4, window=3, **kw)
+        pd.keep_inputs = True
+        pd.run(stream)
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            n = pd.run(stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        pip[name] = {"steps": n, "ms": round(ms, 3), "step_us": round(ms * 1e3 / n, 2),
+                     "tok_s": round(sum(pd.blocks) / ms * 1e3, 1),
+                     "max_active": max(len(st["active"]) for st in pd.trace)}
+        del pd
+    out["pipelined_625"] = pip
     # launch floor: a one-element fill kernel
     x = torch.zeros(1, device="cuda:0")
     out["launch_floor_us"] = round(graph_us(lambda: x.fill_(1.0), stream, reps=50), 3)

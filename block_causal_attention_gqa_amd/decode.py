@@ -16,6 +16,10 @@ describe:
   trajectory block and round, a bidirectional draft pass, a draft argmax
   (threshold 0 reveals every masked row), a causal verify pass and the
   verify call.
+* ``PipelinedDecode`` -- pipelined parallel decoding (Fast-dVLA notes, key
+  design 4): up to ``window`` consecutive blocks denoised together, later
+  ones semi-active until their predecessor is far enough along; one
+  attention call and one unmask call per step, in-order commits.
 
 The model between attention and logits is not part of this library:
 attention outputs are produced and discarded, logits and the active rows'
@@ -248,3 +252,160 @@ class ForkVerify:
             base = self.prefix + self.priv_len[s]
             vis += R * base + (R * R if pass_id == 0 else R * (R + 1) // 2)
         return 4 * self.D * self.Hq * vis
+
+
+class PipelinedDecode:
+    """Pipelined parallel decoding (Fast-dVLA notes, key design 4 and its
+    complete example) over the library calls.
+
+    The output is a sequence of blocks decoded causally over a committed
+    prefix, several at a time:
+      * the first uncommitted block is fully active;
+      * the block after an active one joins as semi-active (threshold-only
+        commits) once its predecessor's completion ratio -- revealed tokens /
+        block size, in double precision -- reaches ``add``, if fewer than
+        ``window`` blocks are active; it becomes fully active (threshold plus
+        at least ceil(remaining / n_div) per step) once the ratio reaches
+        ``act``;
+      * every step runs one attention call over the committed cache with all
+        active blocks (bidirectional inside a block, causal across) and one
+        unmask call with a mode per block;
+      * a block whose tokens are all revealed is committed to the cache, with
+        the K/V of its last step, as soon as every earlier block is: strictly
+        in order, right after that step.
+    Transitions need each step's commit counts, so the host reads them back
+    after every step: the schedule is data-dependent and host-driven.
+
+    Block b's synthetic model outputs at its s-th active step are seeded
+    draws: logits (``logits_for``) and the rows' Q/K/V (``qkv_for``)."""
+
+    def __init__(self, preset=None, seed=0, device="cuda:0", add=0.5, act=0.9, tau=0.5, n_div=4,
+                 window=None, planted_frac=0.2):
+        p = dict(preset or synth.PRESETS["pipelined_625"])
+        self.Hq, self.Hkv, self.D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
+        self.dtype, self.V, self.sigma = p["dtype"], p["vocab"], p["sigma"]
+        self.blocks = list(p["blocks"])
+        self.prefix = p["prefix"]
+        self.window = int(window or p.get("window", 3))
+        self.add, self.act, self.tau, self.n_div = float(add), float(act), float(tau), int(n_div)
+        if self.window < 1 or self.n_div < 1:
+            raise ValueError("window and n_div must be at least 1")
+        self.seed, self.planted_frac, self.dev = seed, planted_frac, device
+        nb = len(self.blocks)
+        self.cap = self.prefix + sum(self.blocks)
+        self.row0 = [0] + [int(x) for x in np.cumsum(self.blocks)]
+        (k, v), _ = synth.kv_cache(seed, 1, self.Hkv, self.cap, self.D, [self.prefix], self.dtype)
+        self.cache = B.KVCache(k.to(device), v.to(device))
+        n_out = sum(self.blocks)
+        self.masked = torch.ones(n_out, dtype=torch.uint8, device=device)
+        self.tokens = torch.full((n_out,), -1, dtype=torch.int32, device=device)
+        self.n_commit = torch.zeros(self.window, dtype=torch.int32, device=device)
+        # active sets are runs of at most `window` consecutive blocks
+        runs = [self.blocks[i:i + w] for i in range(nb) for w in range(1, self.window + 1) if i + w <= nb]
+        ws = 0
+        for r in runs:
+            off = [0] + [int(x) for x in np.cumsum(r)]
+            ws = max(ws, B.bc_attn_workspace_bytes(self.cache, None, (1, off[-1], self.Hq, self.D), off))
+        rmax = max(sum(r) for r in runs)
+        self.ws_attn = torch.zeros(ws, dtype=torch.uint8, device=device)
+        self.ws_unmask = torch.zeros(B.bc_unmask_workspace_bytes(rmax, self.V), dtype=torch.uint8, device=device)
+        self.out = torch.empty((1, rmax, self.Hq, self.D), dtype=synth.torch_dtype(self.dtype), device=device)
+        self.scale = 1.0 / np.sqrt(self.D)
+        self.trace = []
+        self.length = np.array([self.prefix], np.int32)
+        self.keep_inputs = False
+        self._resident = {}
+
+    def logits_for(self, b, s):
+        x = synth.logits(self.seed, self.blocks[b], self.V, self.sigma, 700 + b, s)
+        if self.planted_frac:
+            synth.plant_peaks(x, self.seed, self.planted_frac, 12.0, 700 + b, s)
+        return x
+
+    def qkv_for(self, b, s):
+        """((q, q32), (k, k32), (v, v32)) of block b at its s-th active step:
+        q [1][rows][Hq][D], k / v [1][Hkv][rows][D]."""
+        return synth.active_qkv(self.seed, 1, self.blocks[b], self.Hq, self.Hkv, self.D, self.dtype, 800 + b, s)
+
+    def _step_inputs(self, active, steps):
+        """Device q, k, v, logits of one step (the active blocks' rows in
+        order).  With keep_inputs set they stay resident, keyed by the step's
+        (blocks, local steps): the schedule is deterministic, so a second run
+        finds every step's inputs already on the device."""
+        key = (tuple(active), tuple(steps))
+        hit = self._resident.get(key)
+        if hit is not None:
+            return hit
+        qkv = [self.qkv_for(b, st) for b, st in zip(active, steps)]
+        x = (torch.cat([t[0][0] for t in qkv], dim=1).to(self.dev),
+             torch.cat([t[1][0] for t in qkv], dim=2).to(self.dev),
+             torch.cat([t[2][0] for t in qkv], dim=2).to(self.dev),
+             torch.from_numpy(np.concatenate([self.logits_for(b, st) for b, st in zip(active, steps)])).to(self.dev),
+             [(t[1][0][0].to(self.dev), t[2][0][0].to(self.dev)) for t in qkv])   # per block [Hkv][rows][D]
+        if self.keep_inputs:
+            self._resident[key] = x
+        return x
+
+    def run(self, stream=None, after_attn=None):
+        """Decode every block; returns the number of steps (the trace of each
+        step is in ``self.trace``, tokens in ``self.tokens``).
+        after_attn(step, active, local_steps, length, out) is called after each
+        step's attention call (``out`` is the view it wrote).  Every device
+        operation, torch's own fills and copies included, is issued on
+        ``stream`` (a torch stream, or None for the current one)."""
+        if stream is None:
+            return self._run(None, after_attn)
+        with torch.cuda.stream(stream):
+            return self._run(stream, after_attn)
+
+    def _run(self, stream, after_attn):
+        nb = len(self.blocks)
+        state = ["wait"] * nb
+        local = [0] * nb
+        revealed = [0] * nb
+        committed = 0
+        self.length[0] = self.prefix
+        self.masked.fill_(1)
+        self.tokens.fill_(-1)
+        self.trace = []
+        while committed < nb:
+            state[committed] = "full"
+            n_active = sum(1 for x in range(committed, nb) if state[x] != "wait")
+            for b in range(committed + 1, nb):
+                if state[b - 1] == "wait":
+                    break
+                r = revealed[b - 1] / self.blocks[b - 1]
+                if state[b] == "wait" and r >= self.add and n_active < self.window:
+                    state[b] = "semi"
+                    n_active += 1
+                if state[b] == "semi" and r >= self.act:
+                    state[b] = "full"
+            active = [b for b in range(committed, nb) if state[b] != "wait"]
+            off = [0] + [int(x) for x in np.cumsum([self.blocks[b] for b in active])]
+            rows = off[-1]
+            q, k, v, lg, blk_kv = self._step_inputs(active, [local[b] for b in active])
+            out = self.out[:, :rows]
+            B.bc_attn_step(self.cache, self.length, None, None, q, k, v, off, B.BC_MASK_BLOCK_BIDIR, self.scale,
+                           out, self.ws_attn, stream=stream)
+            if after_attn is not None:
+                after_attn(len(self.trace), list(active), [local[b] for b in active], int(self.length[0]), out)
+            r0, r1 = self.row0[active[0]], self.row0[active[-1] + 1]
+            modes = [B.BC_UNMASK_FULL if state[b] == "full" else B.BC_UNMASK_SEMI for b in active]
+            divs = [self.n_div if state[b] == "full" else 1 for b in active]
+            nc = self.n_commit[:len(active)]
+            B.bc_unmask_select(lg, off, modes, divs, self.tau, self.masked[r0:r1], self.tokens[r0:r1], None, nc,
+                               self.ws_unmask, stream=stream)
+            counts = [int(x) for x in nc.cpu()]        # the next transitions depend on them
+            for j, b in enumerate(active):
+                revealed[b] += counts[j]
+                local[b] += 1
+            done = []
+            while committed < nb and state[committed] != "wait" and revealed[committed] == self.blocks[committed]:
+                blk_k, blk_v = blk_kv[active.index(committed)]      # K/V of its last step
+                B.bc_kv_commit(self.cache, self.length, 0, int(self.length[0]), self.blocks[committed],
+                               blk_k, blk_v, stream=stream)
+                done.append(committed)
+                committed += 1
+            self.trace.append(dict(active=list(active), modes=[state[b] for b in active], n_commit=counts,
+                                   committed=done))
+        return len(self.trace)

@@ -1,0 +1,100 @@
+"""Pipelined parallel decoding on the GPU (Fast-dVLA notes, key design 4):
+the scheduler that drives the attention, unmask and commit calls is checked
+against the float64 schedule oracle on the same seeded model outputs -- every
+step's active blocks, modes and commit counts, the decoded tokens, sampled
+steps' attention outputs, and the cache the in-order commits leave."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA, pipeline as OP
+from tests import gpu_util as G
+from block_causal_attention_gqa_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = 9
+P = synth.PRESETS["pipelined_625"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.require_lib()
+
+
+def _logits_for(b, s):
+    x = synth.logits(SEED, P["blocks"][b], P["vocab"], P["sigma"], 700 + b, s)
+    synth.plant_peaks(x, SEED, 0.2, 12.0, 700 + b, s)
+    return x
+
+
+def _qkv32(b, s):
+    (_, q), (_, k), (_, v) = synth.active_qkv(SEED, 1, P["blocks"][b], P["n_q_heads"], P["n_kv_heads"],
+                                              P["head_dim"], P["dtype"], 800 + b, s)
+    return q, k, v
+
+
+@pytest.mark.parametrize("add,act,tau,n_div,window", [
+    (0.5, 0.9, 0.5, 4, 3),     # three blocks in flight, semi phase
+    (0.25, 0.5, 0.5, 8, 3),    # early joins, slow full blocks
+    (1.0, 1.0, 0.5, 4, 3),     # no overlap: plain block-by-block decoding
+    (0.0, 0.0, 0.9, 2, 2),     # successor always full at once, window 2
+])
+def test_pipelined_625_matches_oracle(add, act, tau, n_div, window):
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 add=%g act=%g tau=%g n=%d window=%d" % (add, act, tau, n_div, window), flush=True)
+    sizes = list(P["blocks"])
+    want_tok, want_trace = OP.pipelined_decode(sizes, _logits_for, add, act, tau, n_div, window)
+    n_steps = len(want_trace)
+    widest = max(range(n_steps), key=lambda k: len(want_trace[k]["active"]))
+    sample = sorted({0, widest, n_steps // 2, n_steps - 1})
+
+    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV, add=add, act=act, tau=tau, n_div=n_div, window=window)
+    seen = {}
+
+    def after_attn(k, active, steps, length, out):
+        if k in sample:
+            torch.cuda.synchronize()
+            seen[k] = (active, steps, length, out.float().cpu().numpy())
+
+    assert pd.run(after_attn=after_attn) == n_steps
+    torch.cuda.synchronize()
+    for k, (got, want) in enumerate(zip(pd.trace, want_trace)):
+        assert got == want, "step %d: %s != %s" % (k, got, want)
+    assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok))
+    assert not pd.masked.cpu().numpy().any()
+
+    # the step at which each block was last active: its K/V are the ones committed
+    last = {}
+    for k, st in enumerate(want_trace):
+        for b in st["active"]:
+            last[b] = sum(1 for x in want_trace[:k + 1] if b in x["active"]) - 1
+    (_, _), (pk, pv) = synth.kv_cache(SEED, 1, P["n_kv_heads"], pd.cap, P["head_dim"], [P["prefix"]], P["dtype"])
+    D = P["head_dim"]
+    for k, (active, steps, length, got) in seen.items():
+        done = [b for st in want_trace[:k] for b in st["committed"]]
+        assert length == P["prefix"] + sum(sizes[b] for b in done)
+        ck = np.concatenate([pk[0, :, :P["prefix"]]] + [_qkv32(b, last[b])[1][0] for b in done], axis=1)
+        cv = np.concatenate([pv[0, :, :P["prefix"]]] + [_qkv32(b, last[b])[2][0] for b in done], axis=1)
+        h = [_qkv32(b, s) for b, s in zip(active, steps)]
+        assert [want_trace[k]["active"], [sum(1 for x in want_trace[:k] if b in x["active"]) for b in active]] == \
+            [active, steps]
+        q = np.concatenate([x[0] for x in h], axis=1)
+        ka = np.concatenate([x[1] for x in h], axis=2)
+        va = np.concatenate([x[2] for x in h], axis=2)
+        off = np.concatenate([[0], np.cumsum([sizes[b] for b in active])])
+        want = OA.attention_step(q, ck[None], cv[None], [length], ka, va, off, OA.MASK_BIDIR, scale=D ** -0.5)
+        err = np.abs(got[:, :off[-1]] - want).max()
+        assert err <= 1e-2, "step %d attention max-abs %.3g" % (k, err)
+
+    # the cache holds the prefix, then every block's last-step K/V, in block order
+    kc = pd.cache.k.float().cpu().numpy()[0]
+    vc = pd.cache.v.float().cpu().numpy()[0]
+    assert int(pd.length[0]) == pd.cap
+    row = P["prefix"]
+    for b, n in enumerate(sizes):
+        _, kb, vb = _qkv32(b, last[b])
+        assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), b
+        row += n
+    assert np.array_equal(kc[:, :P["prefix"]], pk[0, :, :P["prefix"]])
