@@ -329,8 +329,9 @@ def legs(stream):
     """Secondary measurements on the other workloads of the pages' systems:
     the shared-prefix fork round at N = 4, 16, 64 rollouts (attention there
     is MFMA-bound), the verify scan over N = 64 rollouts' logits (HBM-bound),
-    the large-block decode's attention at batch 16 (HBM-bound), a
-    pipelined-parallel decode of 625 tokens against the same decode without
+    the large-block decode's attention at batch 16 (HBM-bound), the section
+    decode with scaffold rows inside its blocks under block and section
+    visibility, a pipelined-parallel decode of 625 tokens against the same decode without
     overlap, and the duration of a minimal kernel as the launch floor."""
     import torch
     from block_causal_attention_gqa_amd import binding as B
@@ -384,6 +385,18 @@ def legs(stream):
                                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                    "TFLOP_s": round(flops / us / 1e6, 1), "bytes": nbytes}
     del pk, pv, cache, ws
+    # the section decode with the sections' scaffold rows inside the blocks
+    # (404 rows, 280 editable), block and section visibility, each decode
+    # replayed whole as one graph like the headline
+    scf = {}
+    for vis in ("block", "section"):
+        dec = decode.SectionDecode(synth.PRESETS["section_scaffold"], seed=0, device="cuda:0", visibility=vis)
+        us = graph_us(lambda: dec.run(stream), stream, reps=1, replays=5)
+        scf[vis] = {"decode_ms": round(us / 1e3, 3), "tok_s": round(dec.tokens_per_decode / us * 1e6, 1),
+                    "rows": sum(dec.blocks), "units": len(dec.units), "max_unit_rows": max(dec.unit_rows)}
+        del dec
+        torch.cuda.empty_cache()
+    out["section_scaffold"] = scf
     # pipelined parallel decoding of a 625-token output (blocks of 32 and a
     # last of 17 over a 512-token prefix, 16q/2kv heads, vocab 2048): each
     # step's commit counts decide the next step's blocks, so the host reads
@@ -418,35 +431,25 @@ def cpu_baseline(dec, args):
     block), repeated until about --cpu-seconds have passed, in decoded tokens
     per second."""
     import threadpoolctl
-    from oracle import attention as OA, kvcache as OK, unmask as OU
+    from oracle import section as OS
     from block_causal_attention_gqa_amd import synth
 
     seed = args.seed
     (_, _), (k32, v32) = synth.kv_cache(seed, 1, dec.Hkv, dec.cap, dec.D, [dec.prefix], dec.dtype)
     # inputs first (not timed): the same seeded tensors the GPU decode uses
-    inputs = []
+    inputs = {}
     for b, bs in enumerate(dec.blocks):
-        row = []
         for st in range(dec.steps):
             (_, q), (_, k), (_, v) = synth.active_qkv(seed, 1, bs, dec.Hq, dec.Hkv, dec.D, dec.dtype, b, st)
-            row.append((q, k, v, synth.logits(seed, bs, dec.V, dec.sigma, b, st)))
-        inputs.append(row)
+            inputs[(b, st)] = (q, k, v, synth.logits(seed, bs, dec.V, dec.sigma, b, st))
+    n = sum(dec.blocks)
+    units = [[b] for b in range(len(dec.blocks))]
     tokens, reps = 0, 0
     t0 = time.perf_counter()
     while True:
-        cache = OK.new_cache(k32, v32, [dec.prefix])
-        for b, bs in enumerate(dec.blocks):
-            masked = np.ones(bs, np.uint8)
-            toks = np.full(bs, -1, np.int32)
-            for st in range(dec.steps):
-                q, k, v, lg = inputs[b][st]
-                ck, cv = cache[0]
-                OA.attention_step(q, ck[None], cv[None], [ck.shape[1]], k, v, [0, bs], OA.MASK_BIDIR,
-                                  scale=dec.scale)
-                masked, toks, _, _ = OU.unmask_select(lg, [0, bs], [OU.MODE_FULL], [dec.steps - st],
-                                                      np.float32(dec.tau), masked, toks)
-            OK.commit(cache, 0, cache[0][0].shape[1], k[0], v[0])
-            tokens += bs
+        OS.section_decode(k32[0], v32[0], dec.prefix, units, dec.blocks, lambda b, st: inputs[(b, st)], dec.steps,
+                          dec.tau, np.ones(n, np.uint8), np.full(n, -1, np.int32), scale=dec.scale)
+        tokens += n
         reps += 1
         if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
             break
@@ -456,7 +459,7 @@ def cpu_baseline(dec, args):
     return {"value": round(tokens / secs, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": "%d repetitions of the whole section decode (%d tokens, %d denoise steps each) on "
                       "the same inputs; BLAS threads %d, os.cpu_count()=%s"
-                      % (reps, sum(dec.blocks), dec.denoise_steps, threads, os.cpu_count()),
+                      % (reps, n, dec.denoise_steps, threads, os.cpu_count()),
             "seconds": round(secs, 2)}
 
 

@@ -5,10 +5,12 @@ module only owns device buffers and issues the calls in the order the pages
 describe:
 
 * ``SectionDecode`` -- Section Diffusion (Fast-dDrive method summary,
-  sec. 3.2): output blocks are decoded in causal order over a committed
-  prefix; each block takes a fixed number of denoise steps (attention, then
-  confidence unmask with n = steps left), and its K/V are committed to the
-  cache when it completes.  Also the large-block decode at batch > 1 (one
+  sec. 3.1 - 3.2): output blocks are decoded in causal order over a
+  committed prefix; each block takes a fixed number of denoise steps
+  (attention, then confidence unmask with n = steps left), and its K/V are
+  committed to the cache when it completes -- or, with section visibility,
+  when its section does.  Optionally the sections' scaffold rows sit inside
+  the blocks.  Also the large-block decode at batch > 1 (one
   attention call covers every sequence; the unmask call sees one block per
   sequence).
 * ``ForkVerify`` -- shared-prefix fork with scaffold speculative decoding
@@ -34,32 +36,76 @@ from . import synth
 
 
 class SectionDecode:
+    """Section Diffusion (Fast-dDrive method summary sec. 3.1 - 3.2): blocks
+    decoded in causal order over a committed prefix, a fixed number of
+    denoise steps each (attention, then confidence unmask with n = steps
+    left).
+
+    ``visibility`` picks the unit that is bidirectional and committed whole:
+      * "block": a block sees the prefix, earlier blocks and itself, and is
+        committed when it completes;
+      * "section": the blocks of one section see each other, so every row of
+        the section is active in each step of each of its blocks (attention
+        over the section's rows, unmask over the current block's rows) and
+        the section is committed when its last block completes.
+    With a preset that sets ``scaffold``, the blocks hold the sections'
+    scaffold rows among the editable ones (``synth.section_layout``); they
+    start unmasked with their template tokens, so the unmask never counts,
+    ranks or changes them.
+
+    Also the large-block decode at batch > 1 (one attention call covers
+    every sequence; the unmask call sees one block per sequence)."""
+
     def __init__(self, preset, seed=0, n_seq=None, device="cuda:0", logits_pool=None,
-                 planted_frac=0.0, planted_delta=12.0):
+                 planted_frac=0.0, planted_delta=12.0, visibility="block"):
         p = dict(preset)
         self.p = p
         self.S = n_seq or p.get("n_seq", 1)
         self.Hq, self.Hkv, self.D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
         self.dtype = p["dtype"]
-        self.blocks = list(p["blocks"])
         self.steps = p["steps"]
         self.V, self.sigma, self.tau = p["vocab"], p["sigma"], p["threshold"]
         self.prefix = p["prefix"]
-        self.cap = self.prefix + sum(self.blocks)
         self.dev = device
+        editable = None
+        if p.get("scaffold"):
+            lay = synth.section_layout(p.get("layout_seed", 0))
+            self.blocks = [b for sec in lay for b in sec["blocks"]]
+            per_section = [len(sec["blocks"]) for sec in lay]
+            editable = np.concatenate([sec["kinds"] for sec in lay])
+        else:
+            self.blocks = list(p["blocks"])
+            per_section = list(p.get("sections", [len(self.blocks)]))
+        nb = len(self.blocks)
+        if visibility == "block":
+            self.units = [[b] for b in range(nb)]
+        elif visibility == "section":
+            if sum(per_section) != nb:
+                raise ValueError("the preset's sections do not cover its blocks")
+            first = np.concatenate([[0], np.cumsum(per_section)])
+            self.units = [list(range(first[i], first[i + 1])) for i in range(len(per_section))]
+        else:
+            raise ValueError("visibility must be 'block' or 'section'")
+        self.visibility = visibility
+        self.unit_of = {b: u for u, blks in enumerate(self.units) for b in blks}
+        self.unit_rows = [sum(self.blocks[b] for b in blks) for blks in self.units]
+        self.row0 = [0] + [int(x) for x in np.cumsum(self.blocks)]
+        self.cap = self.prefix + sum(self.blocks)
         S, Hkv, D = self.S, self.Hkv, self.D
         tdt = synth.torch_dtype(self.dtype)
         (k, v), _ = synth.kv_cache(seed, S, Hkv, self.cap, D, [self.prefix] * S, self.dtype)
         self.cache = B.KVCache(k.to(device), v.to(device))
         self.len0 = np.full(S, self.prefix, np.int32)
-        # per (block, step) active rows and logits, resident on the device;
-        # with logits_pool = k, k distinct logits tensors are cycled instead
+        # per (block, step) the active rows (those of the block's unit) and
+        # the block's logits, resident on the device; with logits_pool = k,
+        # k distinct logits tensors are cycled instead
         bmax = max(self.blocks)
         self.qkv = []
         for b, bs in enumerate(self.blocks):
+            ur = self.unit_rows[self.unit_of[b]]
             row = []
             for st in range(self.steps):
-                (qt, _), (kt, _), (vt, _) = synth.active_qkv(seed, S, bs, self.Hq, Hkv, D, self.dtype, b, st)
+                (qt, _), (kt, _), (vt, _) = synth.active_qkv(seed, S, ur, self.Hq, Hkv, D, self.dtype, b, st)
                 row.append((qt.to(device), kt.to(device), vt.to(device)))
             self.qkv.append(row)
 
@@ -76,21 +122,35 @@ class SectionDecode:
         else:
             self.logits = [[make_logits(S * bs, b, st) for st in range(self.steps)]
                            for b, bs in enumerate(self.blocks)]
-        self.out = {bs: torch.empty((S, bs, self.Hq, D), dtype=tdt, device=device) for bs in set(self.blocks)}
-        self.masked = torch.ones(S * sum(self.blocks), dtype=torch.uint8, device=device)
-        self.tokens = torch.full((S * sum(self.blocks),), -1, dtype=torch.int32, device=device)
+        self.out = {ur: torch.empty((S, ur, self.Hq, D), dtype=tdt, device=device) for ur in set(self.unit_rows)}
+        n_rows = S * sum(self.blocks)
+        self.masked = torch.ones(n_rows, dtype=torch.uint8, device=device)
+        self.tokens = torch.full((n_rows,), -1, dtype=torch.int32, device=device)
+        # initial state of every block's rows, laid out [block][seq][row]
+        self.masked0 = self.tokens0 = None
+        if editable is not None:
+            tmpl = synth.scaffold_tokens(p.get("layout_seed", 0), len(editable), self.V)
+            m0 = np.concatenate([np.tile(editable[self.row0[b]:self.row0[b + 1]], S) for b in range(nb)])
+            t0 = np.concatenate([np.tile(np.where(editable == 0, tmpl, -1)[self.row0[b]:self.row0[b + 1]], S)
+                                 for b in range(nb)]).astype(np.int32)
+            self.masked0 = torch.from_numpy(m0).to(device)
+            self.tokens0 = torch.from_numpy(t0).to(device)
         self.conf = torch.empty(S * bmax, dtype=torch.float32, device=device)
         self.n_commit = torch.zeros(self.S, dtype=torch.int32, device=device)
-        self.ws_attn = torch.zeros(max(B.bc_attn_workspace_bytes(self.cache, None, (S, bs, self.Hq, D), [0, bs])
-                                       for bs in set(self.blocks)), dtype=torch.uint8, device=device)
+        self.ws_attn = torch.zeros(max(B.bc_attn_workspace_bytes(self.cache, None, (S, ur, self.Hq, D), [0, ur])
+                                       for ur in set(self.unit_rows)), dtype=torch.uint8, device=device)
         self.ws_unmask = torch.zeros(B.bc_unmask_workspace_bytes(S * bmax, self.V), dtype=torch.uint8,
                                      device=device)
         self.scale = 1.0 / np.sqrt(D)
         self.hooks = None   # optional callables around each call: hooks(kind, "pre"/"post")
+        self.after_attn = None   # optional after_attn(b, st, out), called after each attention call
 
     @property
     def tokens_per_decode(self):
-        return self.S * sum(self.blocks)
+        """Decoded (editable) tokens per decode, all sequences."""
+        if self.masked0 is None:
+            return self.S * sum(self.blocks)
+        return int(self.masked0.sum())
 
     @property
     def denoise_steps(self):
@@ -104,30 +164,37 @@ class SectionDecode:
         """One whole decode.  Returns nothing; tokens / masked hold the result."""
         S = self.S
         length = self.len0.copy()
-        off = 0
-        for b, bs in enumerate(self.blocks):
-            masked = self.masked[S * off: S * (off + bs)]
-            tokens = self.tokens[S * off: S * (off + bs)]
-            masked.fill_(1)
-            blk_rows = list(range(0, S * bs + 1, bs))
-            out = self.out[bs]
-            for st in range(self.steps):
-                q, k, v = self.qkv[b][st]
-                self._hook("attn", "pre")
-                B.bc_attn_step(self.cache, length, None, None, q, k, v, [0, bs], B.BC_MASK_BLOCK_BIDIR,
-                               self.scale, out, self.ws_attn, stream=stream)
-                self._hook("attn", "post")
-                self._hook("unmask", "pre")
-                B.bc_unmask_select(self.logits[b][st], blk_rows, [B.BC_UNMASK_FULL] * S,
-                                   [self.steps - st] * S, self.tau, masked, tokens, self.conf[: S * bs],
-                                   self.n_commit[:S], self.ws_unmask, stream=stream)
-                self._hook("unmask", "post")
-            q, k, v = self.qkv[b][self.steps - 1]
+        for u, blks in enumerate(self.units):
+            ur = self.unit_rows[u]
+            out = self.out[ur]
+            for b in blks:
+                bs, off = self.blocks[b], self.row0[b]
+                rows = slice(S * off, S * (off + bs))
+                masked, tokens = self.masked[rows], self.tokens[rows]
+                if self.masked0 is None:
+                    masked.fill_(1)
+                else:
+                    masked.copy_(self.masked0[rows])
+                    tokens.copy_(self.tokens0[rows])
+                blk_rows = list(range(0, S * bs + 1, bs))
+                for st in range(self.steps):
+                    q, k, v = self.qkv[b][st]
+                    self._hook("attn", "pre")
+                    B.bc_attn_step(self.cache, length, None, None, q, k, v, [0, ur], B.BC_MASK_BLOCK_BIDIR,
+                                   self.scale, out, self.ws_attn, stream=stream)
+                    self._hook("attn", "post")
+                    if self.after_attn is not None:
+                        self.after_attn(b, st, out)
+                    self._hook("unmask", "pre")
+                    B.bc_unmask_select(self.logits[b][st], blk_rows, [B.BC_UNMASK_FULL] * S,
+                                       [self.steps - st] * S, self.tau, masked, tokens, self.conf[: S * bs],
+                                       self.n_commit[:S], self.ws_unmask, stream=stream)
+                    self._hook("unmask", "post")
+            q, k, v = self.qkv[blks[-1]][self.steps - 1]
             self._hook("commit", "pre")
             for s in range(S):
-                B.bc_kv_commit(self.cache, length, s, int(length[s]), bs, k[s], v[s], stream=stream)
+                B.bc_kv_commit(self.cache, length, s, int(length[s]), ur, k[s], v[s], stream=stream)
             self._hook("commit", "post")
-            off += bs
 
 
 class ForkVerify:
@@ -138,7 +205,9 @@ class ForkVerify:
 
       1. draft pass: bidirectional attention of the block's rows;
       2. draft argmax: an unmask with threshold 0 and SEMI mode reveals every
-         masked row, token = argmax of its draft logits;
+         masked row, token = argmax of its draft logits; the block's scaffold
+         rows (one template for all rollouts) start unmasked with their
+         template tokens, so only the editable rows are drafted;
       3. verify pass: causal attention of the same rows;
       4. speculative verify of the drafts against the verify logits, scaffold
          rows accepted as they are; with a temperature, the verify samples
@@ -175,8 +244,13 @@ class ForkVerify:
         self.draft_logits = torch.from_numpy(synth.logits(seed, N * R, self.V, self.sigma, 200 + block)).to(device)
         self.verify_logits = torch.from_numpy(
             synth.logits(seed, N * R, self.V, self.sigma, 300 + block)).to(device).view(N, R, self.V)
-        g = synth.rng(seed, "misc", 400 + block)
-        self.fixed = torch.from_numpy((g.random((N, R)) < scaffold_frac).astype(np.uint8)).to(device)
+        # the block's scaffold rows: one prefilled template shared by every
+        # rollout, accepted as they are; only the editable rows are drafted
+        fixed, tmpl = self._scaffold(seed, block, scaffold_frac)
+        self.scaffold_frac = scaffold_frac
+        self.fixed = torch.from_numpy(fixed).to(device)
+        self.masked0 = torch.from_numpy((1 - fixed).reshape(-1)).to(device)
+        self.tokens0 = torch.from_numpy(np.where(fixed == 1, tmpl, -1).astype(np.int32).reshape(-1)).to(device)
         # trajectory-only sampling (method summary sec. 3.3): the verify
         # samples softmax(l / T) through Gumbel-max on per-rollout noise
         self.temperature = temperature
@@ -198,6 +272,12 @@ class ForkVerify:
         self.scale = 1.0 / np.sqrt(D)
         self.blk_rows = list(range(0, N * R + 1, R))
 
+    def _scaffold(self, seed, block, frac):
+        """(fixed [N][R] uint8, template tokens [N][R]) of the block."""
+        g = synth.rng(seed, "misc", 400 + block)
+        fixed = np.tile((g.random(self.R) < frac).astype(np.uint8), (self.N, 1))
+        return fixed, np.tile(synth.scaffold_tokens(seed, self.R, self.V, 400 + block), (self.N, 1))
+
     def host_inputs(self, seed=0, block=0):
         """The float32 host arrays the device tensors were made from (same
         seeded draws), for checks against the CPU oracle."""
@@ -212,10 +292,11 @@ class ForkVerify:
         noise = None
         if self.temperature is not None:
             noise = synth.gumbel(seed, (N, R, self.V), 500 + block)
+        fixed, tmpl = self._scaffold(seed, block, self.scaffold_frac)
         return dict(pk=pk, pv=pv, vk=vk, vv=vv, qkv=qkv, noise=noise,
                     draft_logits=synth.logits(seed, N * R, self.V, self.sigma, 200 + block),
                     verify_logits=synth.logits(seed, N * R, self.V, self.sigma, 300 + block).reshape(N, R, self.V),
-                    fixed=self.fixed.cpu().numpy())
+                    fixed=fixed, tokens0=np.where(fixed == 1, tmpl, -1).astype(np.int32).reshape(-1))
 
     def attention(self, pass_id, stream=None):
         q, k, v = self.qkv[pass_id]
@@ -224,7 +305,8 @@ class ForkVerify:
                        self.scale, self.out, self.ws_attn, stream=stream)
 
     def draft_argmax(self, stream=None):
-        self.masked.fill_(1)
+        self.masked.copy_(self.masked0)
+        self.tokens.copy_(self.tokens0)
         B.bc_unmask_select(self.draft_logits, self.blk_rows, [B.BC_UNMASK_SEMI] * self.N, [1] * self.N, 0.0,
                            self.masked, self.tokens, None, self.n_commit, self.ws_unmask, stream=stream)
 

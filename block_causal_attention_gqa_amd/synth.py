@@ -22,6 +22,7 @@ _TAGS = {
     "prefix_k": 1, "prefix_v": 2, "q": 3, "k": 4, "v": 5, "logits": 6,
     "priv_k": 7, "priv_v": 8, "draft": 9, "peak": 10, "ratio": 11,
     "subset": 12, "commit_k": 13, "commit_v": 14, "misc": 15, "gumbel": 16,
+    "layout": 17, "scaffold": 18,
 }
 
 
@@ -64,6 +65,8 @@ def torch_dtype(dtype):
 #                prefix 2048, 8 blocks of 32, 16 steps per block, batch 1/16
 #   pipelined  : Fast-dVLA, 16q/2kv, D 128, bf16, prefix 512, 3 active blocks
 #                of 7, logits [21 x 2048]; variant 625 tokens in blocks of 32
+#   section_scaffold: the section decode with the sections' scaffold tokens
+#                inside the blocks (404 rows, blocks of <= 32 editable rows)
 #   fork       : shared prefix 3072 + 210, 16q/2kv, D 128, bf16, N rollouts,
 #                trajectory blocks 24/23/23, logits [24 x 151936]
 # ---------------------------------------------------------------------------
@@ -71,6 +74,9 @@ def torch_dtype(dtype):
 SECTION_EDITABLE = {"critical_objects": 12, "explanation": 192,
                     "future_meta_behavior": 6, "trajectory": 70}
 SECTION_ORDER = ["critical_objects", "explanation", "future_meta_behavior", "trajectory"]
+# scaffold (template) tokens of each section, from the same table
+SECTION_SCAFFOLD = {"critical_objects": 80, "explanation": 6,
+                    "future_meta_behavior": 18, "trajectory": 20}
 
 
 def split_sizes(n, d):
@@ -82,6 +88,36 @@ def split_sizes(n, d):
     return sizes
 
 
+def section_layout(seed, d=32):
+    """Output rows of the four sections with their scaffold tokens inside
+    the blocks.  Each section's rows are a seeded interleaving of its
+    editable and scaffold counts (the pages give the counts, not the
+    order); a block ends right after every d-th editable row while editable
+    rows remain, so the last block of a section also takes its trailing
+    scaffold.  Returns one dict per section, in decoding order:
+    ``kinds`` (uint8 [rows], 1 = editable, 0 = scaffold) and ``blocks``
+    (rows per block)."""
+    out = []
+    for i, name in enumerate(SECTION_ORDER):
+        ne, ns = SECTION_EDITABLE[name], SECTION_SCAFFOLD[name]
+        kinds = np.zeros(ne + ns, np.uint8)
+        kinds[rng(seed, "layout", i).permutation(ne + ns)[:ne]] = 1
+        blocks, start, seen = [], 0, 0
+        for r in range(ne + ns):
+            seen += int(kinds[r])
+            if kinds[r] and seen % d == 0 and seen < ne:
+                blocks.append(r + 1 - start)
+                start = r + 1
+        blocks.append(ne + ns - start)
+        out.append(dict(name=name, kinds=kinds, blocks=blocks))
+    return out
+
+
+def scaffold_tokens(seed, n, vocab, *idx):
+    """Token ids of prefilled scaffold rows (uniform over the vocabulary)."""
+    return rng(seed, "scaffold", *idx).integers(0, vocab, size=n).astype(np.int32)
+
+
 PRESETS = {
     "tiny": dict(n_seq=1, n_q_heads=4, n_kv_heads=1, head_dim=64, dtype="f32",
                  prefix=256, blocks=[8], steps=1, vocab=1024, sigma=3.0,
@@ -89,7 +125,13 @@ PRESETS = {
     "section": dict(n_seq=1, n_q_heads=16, n_kv_heads=2, head_dim=128, dtype="bf16",
                     prefix=3072,
                     blocks=sum((split_sizes(SECTION_EDITABLE[s], 32) for s in SECTION_ORDER), []),
+                    sections=[len(split_sizes(SECTION_EDITABLE[s], 32)) for s in SECTION_ORDER],
                     steps=8, vocab=151936, sigma=4.0, threshold=0.9),
+    # the same decode with the scaffold rows inside the blocks (404 rows:
+    # 280 editable, 124 scaffold), the layout drawn once from layout_seed
+    "section_scaffold": dict(n_seq=1, n_q_heads=16, n_kv_heads=2, head_dim=128, dtype="bf16",
+                             prefix=3072, scaffold=True, layout_seed=0, steps=8, vocab=151936,
+                             sigma=4.0, threshold=0.9),
     "large_block": dict(n_seq=1, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
                         prefix=2048, blocks=[32] * 8, steps=16, vocab=151936, sigma=4.0,
                         threshold=0.9),

@@ -36,11 +36,15 @@ def test_fork_verify_round_matches_oracle(N, block, temperature):
         assert np.abs(got - want).max() <= 1e-2, "pass %d" % pass_id
     fv.draft_argmax()
     torch.cuda.synchronize()
-    masked0 = np.ones(N * R, np.uint8)
-    tok0 = np.full(N * R, -1, np.int32)
+    # the scaffold rows start revealed with the template (the same for every
+    # rollout); the draft reveals exactly the editable rows
+    masked0 = (1 - h["fixed"]).reshape(-1).astype(np.uint8)
+    tok0 = h["tokens0"]
+    assert (h["fixed"] == h["fixed"][0]).all() and 0 < h["fixed"].sum() < N * R
     m_want, t_want, n_want, _ = OU.unmask_select(h["draft_logits"], fv.blk_rows, [OU.MODE_SEMI] * N, [1] * N,
                                                  np.float32(0.0), masked0, tok0)
     assert np.array_equal(fv.masked.cpu().numpy(), m_want) and not m_want.any()
+    assert np.array_equal(n_want, masked0.reshape(N, R).sum(axis=1))
     assert np.array_equal(fv.tokens.cpu().numpy(), t_want)
     assert np.array_equal(fv.n_commit.cpu().numpy(), n_want)
     fv.verify()
