@@ -34,12 +34,14 @@
 //
 // Data movement (bf16).  K and V tiles of 64 keys go from HBM straight into
 // LDS with buffer loads that write LDS (no staging registers), 1 KB per wave
-// instruction, double-buffered so the next tile is in flight while the
-// current one is computed; one barrier per tile.  Rows past a segment's end
+// instruction, in two-stage rings of their own so that each load has a whole
+// tile iteration to land; one barrier per tile.  Rows past a segment's end
 // fall outside the buffer's record range and arrive as zeros.  Both tiles
 // stay [key][dim] in LDS with a 16-byte-chunk XOR swizzle per row; K operands
 // are plain 16-byte reads, V^T operands come from the transposing LDS read
 // (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of one dim.
+// Inside a wave the scores of tile j + 1 (MFMA) are computed while the
+// probabilities of tile j (VALU) are formed.
 // fp32 inputs (small configurations) use v_mfma_f32_16x16x4_f32 with
 // register-staged tiles and the same softmax.
 
@@ -84,13 +86,6 @@ __device__ inline float group4_max(float x) {
 // every outstanding global load of the wave, which would stall on the next
 // key tile's prefetch; here only LDS traffic is drained before the barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// 16 bytes per lane from a raw buffer (base, stride 0, `bytes` records):
-// offsets at or past `bytes` read as zero, so a tile running past its
-// segment's end needs no clamping or masking of the loaded values.
-__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map
 // hardware id -> logical id so that consecutive logical ids (the row tiles
@@ -299,7 +294,58 @@ __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&v
 }
 
 // ============================================================ bf16 partial
+// One buffer-to-LDS load (the 16-byte form gfx950 adds): every lane fetches
+// the 16 bytes at byte offset voff of the buffer described by rsrc and
+// writes them to LDS at byte lds + 16 * lane; offsets at or past the
+// buffer's size write zeros.  Inline assembly keeps the load out of the
+// compiler's wait-count bookkeeping, which would otherwise make every LDS
+// read wait for the loads filling the other stages; completion is awaited
+// explicitly by tile_barrier().
+// (M0 holds the LDS address; nothing else in these kernels uses M0, so the
+// compiler's note that it reserves the register is silenced here.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void buffer_load_lds16(u32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// raw buffer descriptor: base, stride 0, num_records bytes
+__device__ inline u32x4 raw_buffer(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kRawBufferWord3};
+}
+
+__device__ inline uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((BC_LDS const uint8_t*)p);
+}
+
+// Barrier after this wave's buffer-to-LDS loads have landed and its LDS
+// reads have returned: once every wave passes it, the stages loaded before
+// it are visible to all waves and the stages read before it may be
+// refilled.  (Encoding: vmcnt 0, lgkmcnt 0, expcnt unconstrained; as a
+// builtin it also tells the compiler that every earlier load, e.g. of the Q
+// operand, has completed.)
+__device__ inline void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // NW waves, each with CT column tiles of 16 query rows.
+//
+// Tile pipeline.  K and V sit in two-stage rings of their own: K(j) in
+// k_st[j & 1], V(j) in v_st[j & 1].  Iteration j
+//   1. starts the loads of K(j + 2) into K(j)'s stage and of V(j + 1) into
+//      V(j - 1)'s stage (both were last read before the previous barrier);
+//   2. takes tile j's maxima (its scores came from the previous iteration)
+//      and, rarely, rescales the accumulator;
+//   3. computes the scores of tile j + 1 (MFMA) while the probabilities of
+//      tile j are formed (VALU): the two are independent, so the matrix and
+//      vector units overlap inside one wave;
+//   4. accumulates O^T += V(j)^T P(j)^T;
+//   5. waits for its loads and meets the other waves at one barrier.
+// Every load has a whole iteration to land.
 template <int D, int NW, int CT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_bf16_kernel(const AttnArgs a) {
@@ -307,17 +353,16 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   constexpr int RB = D * 2;            // bytes per key row
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int TB = KT * RB;          // bytes per tile and tensor
-  constexpr int NT = NW * 64;          // threads
-  static_assert(TB % (NT * 16) == 0, "tile chunks must split evenly over the threads");
-  constexpr int LPT = TB / (NT * 16);  // 16-byte chunks per thread, tile and tensor
+  constexpr int RPL = 1024 / RB;       // key rows per wave-wide 16-byte load
+  static_assert(TB % (NW * 1024) == 0, "a tile must split evenly over the waves' 1 KB loads");
+  constexpr int LPW = TB / (NW * 1024);  // loads per wave, tile and tensor
   constexpr int kWaveRows = 16 * CT;
   constexpr int kTileRows = NW * kWaveRows;
-  // two stages: tile j + 1 is written while tile j is read
   __shared__ __attribute__((aligned(16))) uint8_t k_st0[TB], k_st1[TB], v_st0[TB], v_st1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, jj = lane >> 4;
 
   const Item<bf16_t> it = decode_item<bf16_t>(a, item_of_block(a));
@@ -349,17 +394,17 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- register staging: thread tid moves 16-byte chunks g = tid + NT u
-  // (u < LPT) of each tile, row g / CPR, chunk g % CPR; it reads them in
-  // order from HBM (coalesced) and writes them to their swizzled LDS
-  // positions.  Also the LDS addresses of the operand reads.
-  uint32_t goff[LPT], koff[LPT], voff[LPT];
+  // ---- load i of this wave fills stage bytes (wave LPW + i) 1024 + 16 lane,
+  // i.e. key row (wave LPW + i) RPL + lane / CPR at chunk position
+  // lane % CPR; it fetches the chunk the swizzle puts there (the swizzles
+  // are XORs, so position and chunk map to each other the same way).  Also
+  // the LDS addresses of the operand reads.
+  uint32_t koff[LPW], voff[LPW];
 #pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int g = tid + NT * u, row = g / CPR, c = g % CPR;
-    goff[u] = row * RB + c * 16;
-    koff[u] = row * RB + (c ^ swz_k<D>(row)) * 16;
-    voff[u] = row * RB + (c ^ swz_v<D>(row)) * 16;
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (wave * LPW + i) * RPL + lane / CPR, pos = lane % CPR;
+    koff[i] = row * RB + (pos ^ swz_k<D>(row)) * 16;
+    voff[i] = row * RB + (pos ^ swz_v<D>(row)) * 16;
   }
   uint32_t kaddr[QK], vaddr[D / 16];
   {
@@ -381,43 +426,21 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     if (j < nt0) { kp = it.k0; vp = it.v0; nk = it.n0; kb = j * KT; msk = it.masked0; }
     else { kp = it.k1; vp = it.v1; nk = it.n1; kb = (j - nt0) * KT; msk = true; }
   };
-
-  u32x4 kreg[LPT], vreg[LPT];
-  auto load = [&](int j) __attribute__((always_inline)) {
+  // loads of tile j's K or V into a stage; rows past the segment arrive as zeros
+  auto load = [&](int j, bool is_v, const uint8_t* stage) __attribute__((always_inline)) {
     const bf16_t *kp, *vp;
     int nk, kb;
     bool msk;
     tile_src(j, kp, vp, nk, kb, msk);
-    const int bytes = min(nk - kb, KT) * RB;   // rows past the segment read as zero
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kp + (long long)kb * D), 0, bytes, kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vp + (long long)kb * D), 0, bytes, kRawBufferWord3);
+    const u32x4 r = raw_buffer((is_v ? vp : kp) + (long long)kb * D, min(nk - kb, KT) * RB);
+    const uint32_t dst = lds_offset(stage) + wave * LPW * 1024;
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) kreg[u] = buffer_load16(rk, goff[u]);
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) vreg[u] = buffer_load16(rv, goff[u]);
-  };
-  auto store = [&](auto stage) __attribute__((always_inline)) {
-    uint8_t* kd = decltype(stage)::value ? k_st1 : k_st0;
-    uint8_t* vd = decltype(stage)::value ? v_st1 : v_st0;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) *reinterpret_cast<u32x4*>(kd + koff[u]) = kreg[u];
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) *reinterpret_cast<u32x4*>(vd + voff[u]) = vreg[u];
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(r, dst + i * 1024, is_v ? voff[i] : koff[i]);
   };
 
-  const float sl2 = a.scale_log2;
-  auto compute = [&](auto stage, int j) __attribute__((always_inline)) {
-    const bf16_t *kp, *vp;
-    int nk, kb;
-    bool msk;
-    tile_src(j, kp, vp, nk, kb, msk);
-    const BC_LDS uint8_t* ks = (const BC_LDS uint8_t*)(decltype(stage)::value ? k_st1 : k_st0);
-    const BC_LDS uint8_t* vs = (const BC_LDS uint8_t*)(decltype(stage)::value ? v_st1 : v_st0);
-
-    // ---- S^T = K Q^T for 4 tiles of 16 keys x 2 column tiles
-    f32x4 st[CT][4];
+  // S^T = K Q^T for 4 tiles of 16 keys x CT column tiles
+  auto scores = [&](const uint8_t* stage, f32x4 (&st)[CT][4]) __attribute__((always_inline)) {
+    const BC_LDS uint8_t* ks = (const BC_LDS uint8_t*)stage;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -434,20 +457,85 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
         for (int c = 0; c < CT; ++c)
           st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[c][kk], st[c][t], 0, 0, 0);
     }
+  };
 
-    softmax_tile<true, D, CT>(st, o, m_run, l_run, lim, jj, kb, nk, msk, sl2);
-
-    // ---- O^T += V^T P^T
-    bf16x8 pb[CT][2];
+  // keys of tile j a column may not see get -inf: past the segment's end,
+  // and for the active keys past the column's limit
+  auto mask = [&](int j, f32x4 (&st)[CT][4]) __attribute__((always_inline)) {
+    const bf16_t *kp, *vp;
+    int nk, kb;
+    bool msk;
+    tile_src(j, kp, vp, nk, kb, msk);
+    if (msk || kb + KT > nk) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+      for (int c = 0; c < CT; ++c) {
+        const int thr = (msk ? min(nk, lim[c]) : nk) - kb - key_group_off<true>(jj);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!(key_const_off<true>(t, i) < thr)) st[c][t][i] = kNegInf;
+      }
+    }
+  };
+
+  // Online softmax of one tile's scores (one query column per lane and
+  // column tile), in two parts.  First the tile's maxima: the reference max
+  // m only moves when a column's tile max exceeds it by more than
+  // kRescaleSlack, so after the first tiles the accumulator is almost never
+  // rescaled; returns whether any column of the wave moved, with the
+  // columns' rescale factors and the max the exponents use.
+  auto maxima = [&](const f32x4 (&st)[CT][4], float (&alpha)[CT], float (&muse)[CT]) __attribute__((always_inline)) {
+    const float sl2 = a.scale_log2;
+    bool moved = false;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, st[c][t][i]);
+      tmax = group4_max(tmax);
+      const float tm = tmax * sl2;
+      const bool move = tm > m_run[c] + kRescaleSlack;
+      const float mnew = move ? tm : m_run[c];
+      muse[c] = mnew == kNegInf ? 0.f : mnew;
+      alpha[c] = move ? __builtin_amdgcn_exp2f(m_run[c] - muse[c]) : 1.f;
+      m_run[c] = mnew;
+      moved |= move;
+    }
+    return moved;
+  };
+  // Then the probabilities p = 2^(x scale log2 e - m), their row sums and
+  // their bf16 B operands for the PV product.
+  auto probs = [&](const f32x4 (&st)[CT][4], const float (&alpha)[CT], const float (&muse)[CT],
+                   bf16x8 (&pb)[CT][2]) __attribute__((always_inline)) {
+    const float sl2 = a.scale_log2;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      float p[4][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse[c]));
+          psum += p[t][i];
+        }
+      l_run[c] = l_run[c] * alpha[c] + psum;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[c][s2][e] = (__bf16)st[c][2 * s2][e];
-          pb[c][s2][e + 4] = (__bf16)st[c][2 * s2 + 1][e];
+          pb[c][s2][e] = (__bf16)p[2 * s2][e];
+          pb[c][s2][e + 4] = (__bf16)p[2 * s2 + 1][e];
         }
+    }
+  };
+
+  // O^T += V^T P^T
+  auto accumulate = [&](const uint8_t* stage, const bf16x8 (&pb)[CT][2]) __attribute__((always_inline)) {
+    const BC_LDS uint8_t* vs = (const BC_LDS uint8_t*)stage;
 #pragma unroll
     for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
       bf16x8 va[4][2];
@@ -471,31 +559,72 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- tile pipeline: tile j + 1 is read from HBM into registers while
-  // tile j is computed, and written to the other LDS stage after it.  The
-  // barrier at step j publishes tile j and also tells every wave that all
-  // waves have finished tile j - 1, whose stage tile j + 1 then overwrites.
+  // iteration j (parity fixed per unrolled half): s_cur holds the scores of
+  // tile j, s_nxt receives those of tile j + 1.  The last form has no next
+  // tile: no score pass and no closing barrier.
+  auto step = [&](auto par, auto last, int j, f32x4 (&s_cur)[CT][4], f32x4 (&s_nxt)[CT][4])
+                  __attribute__((always_inline)) {
+    constexpr bool odd = decltype(par)::value;
+    constexpr bool kLast = decltype(last)::value;
+    if constexpr (!kLast) {
+      if (j + 2 < nt) load(j + 2, false, odd ? k_st1 : k_st0);
+      if (j + 1 < nt) load(j + 1, true, odd ? v_st0 : v_st1);
+    }
+    mask(j, s_cur);
+    float alpha[CT], muse[CT];
+    if (__any(maxima(s_cur, alpha, muse))) {   // wave-uniform
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha[c];
+    }
+    // one branch-free block: the scheduler interleaves the score MFMAs of
+    // tile j + 1 with the exponentials of tile j, then the PV MFMAs.  With
+    // two column tiles it runs at raised wave priority, so that of the two
+    // waves sharing a SIMD the one issuing MFMAs is preferred and the
+    // other's vector work fills the gaps.
+    if constexpr (CT > 1) __builtin_amdgcn_s_setprio(1);
+    if constexpr (!kLast) scores(odd ? k_st0 : k_st1, s_nxt);
+    bf16x8 pb[CT][2];
+    probs(s_cur, alpha, muse, pb);
+    accumulate(odd ? v_st1 : v_st0, pb);
+    if constexpr (CT > 1) __builtin_amdgcn_s_setprio(0);
+    if constexpr (!kLast) tile_barrier();
+  };
+
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using More = std::false_type;
+  using Last = std::true_type;
+  f32x4 sa[CT][4], sb[CT][4];
   if (nt > 0) {
-    load(0);
-    store(S0{});
+    load(0, false, k_st0);
+    load(0, true, v_st0);
+    if (nt > 1) load(1, false, k_st1);
   }
-  // Every load so far (Q operand, first tile) has landed on every path into
-  // the loop; with this the compiler's wait bookkeeping does not wait for
-  // the Q loads again inside the loop, where that wait would also drain the
-  // next tile's loads.  (Encoding: vmcnt 0, expcnt and lgkmcnt unconstrained.)
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  for (int j = 0; j < nt; j += 2) {
-    lds_barrier();
-    if (j + 1 < nt) load(j + 1);
-    compute(S0{}, j);
+  tile_barrier();
+  if (nt > 0) scores(k_st0, sa);
+  if (nt > 2) tile_barrier();   // every wave has read K(0) before iteration 0 refills its stage
+  if constexpr (CT == 1) {
+    // few rows, short items: the last iteration gets its own form
+    int j = 0;
+    for (; j + 2 < nt; j += 2) {
+      step(S0{}, More{}, j, sa, sb);
+      step(S1{}, More{}, j + 1, sb, sa);
+    }
     if (j + 1 < nt) {
-      store(S1{});
-      lds_barrier();
-      if (j + 2 < nt) load(j + 2);
-      compute(S1{}, j + 1);
-      if (j + 2 < nt) store(S0{});
+      step(S0{}, More{}, j, sa, sb);
+      step(S1{}, Last{}, j + 1, sb, sa);
+    } else if (j < nt) {
+      step(S0{}, Last{}, j, sa, sb);
+    }
+  } else {
+    // long items: one form only (a second would push the register
+    // allocation past the budget); the last score pass reads a stale stage
+    // and is discarded
+    for (int j = 0; j < nt; j += 2) {
+      step(S0{}, More{}, j, sa, sb);
+      if (j + 1 < nt) step(S1{}, More{}, j + 1, sb, sa);
     }
   }
 
