@@ -272,15 +272,19 @@ __device__ inline void softmax_tile(f32x4 (&st)[CT][4], f32x4 (&o)[CT][D / 16], 
 
 // this item's partial for the lane's columns.  Non-temporal stores: the
 // partials are read once, by the combine, so they are not kept in L2.
-template <int D, int CT>
+// (kGroupSum: l_run holds each lane group's share of the column sum, added
+// up here; otherwise every lane already holds the full sum)
+template <int D, int CT, bool kGroupSum = true>
 __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
                                      const float (&m_run)[CT], const float (&l_run)[CT],
                                      const f32x4 (&o)[CT][D / 16], int jj) {
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     float l = l_run[c];
-    l += wave_xor(l, 16);
-    l += wave_xor(l, 32);
+    if constexpr (kGroupSum) {
+      l += wave_xor(l, 16);
+      l += wave_xor(l, 32);
+    }
     if (!valid[c]) continue;
     const long long prow = (long long)slot * a.rows_total + orow[c];
     if (jj == 0) {
@@ -382,12 +386,15 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
       qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
     }
 
-  float m_run[CT], l_run[CT];
-  f32x4 o[CT][D / 16];
+  // osum: the row sums, accumulated by the matrix core next to o (an
+  // all-ones A operand), so that the normaliser sums exactly the bf16
+  // probabilities the numerator uses; every lane holds its column's full sum
+  float m_run[CT];
+  f32x4 o[CT][D / 16], osum[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     m_run[c] = kNegInf;
-    l_run[c] = 0.f;
+    osum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int c = 0; c < CT; ++c)
@@ -514,15 +521,10 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       float p[4][4];
-      float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse[c]));
-          psum += p[t][i];
-        }
-      l_run[c] = l_run[c] * alpha[c] + psum;
+        for (int i = 0; i < 4; ++i) p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[c][t][i], sl2, -muse[c]));
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -536,6 +538,13 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   // O^T += V^T P^T
   auto accumulate = [&](const uint8_t* stage, const bf16x8 (&pb)[CT][2]) __attribute__((always_inline)) {
     const BC_LDS uint8_t* vs = (const BC_LDS uint8_t*)stage;
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) osum[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][s2], osum[c], 0, 0, 0);
 #pragma unroll
     for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
       bf16x8 va[4][2];
@@ -577,6 +586,8 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha[c];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) osum[c] *= alpha[c];
     }
     // one branch-free block: the scheduler interleaves the score MFMAs of
     // tile j + 1 with the exponentials of tile j, then the PV MFMAs.  With
@@ -628,7 +639,10 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     }
   }
 
-  write_partial<D, CT>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  float l_run[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) l_run[c] = osum[c][0];
+  write_partial<D, CT, false>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // ============================================================ fp32 partial

@@ -107,6 +107,29 @@ def test_fork_sixteen_rollouts_ragged_rows():
     _check(60, 16, 23, 16, 2, 128, "bf16", [3282], [0, 23], CAUSAL, fork=True, priv_len=priv, priv_cap=48)
 
 
+# ---- many rows per KV-head group (>= 2048): the eight-wave kernel whose two
+# wave groups alternate matrix and vector halves
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_fork_sixtyfour_rollouts(mode):
+    # the fork at full size: 64 rollouts x 24 rows x 8 heads per KV head
+    priv = [(11 * s) % 48 for s in range(64)]
+    _check(64, 64, 24, 16, 2, 128, "bf16", [3282], [0, 24], mode, fork=True, priv_len=priv, priv_cap=48)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_many_rows_head_dim_64(mode, splits):
+    # 512 rows x group 4: 2048 rows per group, ragged prefix, uneven blocks
+    _check(70 + splits, 1, 512, 16, 4, 64, "bf16", [1000], [0, 100, 256, 300, 512], mode, n_splits=splits)
+
+
+def test_many_rows_empty_prefix():
+    # no committed keys: the prefix items have no tiles, the active items do all the work
+    _check(75, 1, 1024, 4, 1, 128, "bf16", [0], [0, 512, 1024], CAUSAL)
+
+
 def test_block_size_one_equals_causal():
     # WAM-Diff2 sec. 2.1: B = 1 is causal decoding -- bitwise equal on the GPU
     a, _ = G.attn_case(70, 1, 16, 8, 2, 128, "bf16", [300], list(range(17)), BIDIR)
