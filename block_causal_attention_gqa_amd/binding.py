@@ -188,8 +188,9 @@ def bc_attn_workspace_bytes(prefix, priv, q_shape, blk_off, n_prefix_splits=0):
                                              ctypes.byref(act), int(n_prefix_splits)))
 
 
-def _attn_call(name, prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
-               n_prefix_splits, stream, check):
+def _attn_args(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws, n_prefix_splits, stream):
+    """Checked ctypes arguments of an attention call, and the host objects
+    they point into (kept alive with them)."""
     tdtype = prefix.k.dtype
     act, off_arr = _active(q, k, v, blk_off, tdtype, prefix.n_kv_heads, prefix.head_dim)
     pl_arr, pl_p = _host_i32(prefix_len)
@@ -204,12 +205,48 @@ def _attn_call(name, prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask,
     else:
         vs, vl_arr, vl_p = None, None, None
     _dev(out, "out", tdtype, q.numel())
-    st = getattr(lib(), name)(ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p,
-                              ctypes.byref(act), int(mask), float(scale), int(n_prefix_splits),
-                              out.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    args = (ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p, ctypes.byref(act), int(mask),
+            float(scale), int(n_prefix_splits), out.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(),
+            _stream(stream))
+    return args, (act, off_arr, pl_arr, ps, vs, vl_arr)
+
+
+def _attn_call(name, prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+               n_prefix_splits, stream, check):
+    args, _keep = _attn_args(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                             n_prefix_splits, stream)
+    st = getattr(lib(), name)(*args)
     if check and st != BC_OK:
         raise BcError(st, name)
     return st
+
+
+class Prepared:
+    """One library call whose arguments were checked and marshalled once.
+    Calling it issues the same call again: the same device pointers, and host
+    arrays read afresh at each call (so an int32 length array updated in
+    place by bc_kv_commit is seen).  The tensors and arrays it was made from
+    must stay alive and keep their storage."""
+
+    def __init__(self, name, args, keep):
+        self.name, self.args, self._keep = name, args, keep
+        self.fn = getattr(lib(), name)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != BC_OK:
+            raise BcError(st, self.name)
+
+
+def prepare_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                      n_prefix_splits=0, stream=None):
+    """bc_attn_step as a Prepared call; prefix_len must be a contiguous int32
+    NumPy array (its current contents are passed at each call)."""
+    if not (isinstance(prefix_len, np.ndarray) and prefix_len.dtype == np.int32 and prefix_len.flags.c_contiguous):
+        raise ValueError("prefix_len must be a contiguous int32 NumPy array")
+    args, keep = _attn_args(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
+                            n_prefix_splits, stream)
+    return Prepared("bc_attn_step", args, keep + (prefix_len,))
 
 
 def bc_attn_step(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out, ws,
@@ -271,8 +308,7 @@ def bc_unmask_decide(logits, blk_off, mode, n_div, threshold, masked, tokens, co
                         n_commit, ws, stream, check)
 
 
-def _unmask_call(name, logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
-                 stream, check):
+def _unmask_args(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws, stream):
     R, V = (int(x) for x in logits.shape)
     off_arr, off_p = _host_i32(blk_off)
     n_blk = len(off_arr) - 1
@@ -280,14 +316,27 @@ def _unmask_call(name, logits, blk_off, mode, n_div, threshold, masked, tokens, 
     div_arr, div_p = _host_i32(n_div)
     if len(mode_arr) != n_blk or len(div_arr) != n_blk:
         raise ValueError("mode and n_div need one entry per block")
-    st = getattr(lib(), name)(
-        _dev(logits, "logits", torch.float32, R * V), R, V, off_p, n_blk, mode_p, div_p,
-        float(threshold), _dev(masked, "masked", torch.uint8, R), _dev(tokens, "tokens", torch.int32, R),
-        _dev(conf, "conf", torch.float32, R, allow_none=True), _dev(n_commit, "n_commit", torch.int32, n_blk),
-        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    args = (_dev(logits, "logits", torch.float32, R * V), R, V, off_p, n_blk, mode_p, div_p, float(threshold),
+            _dev(masked, "masked", torch.uint8, R), _dev(tokens, "tokens", torch.int32, R),
+            _dev(conf, "conf", torch.float32, R, allow_none=True), _dev(n_commit, "n_commit", torch.int32, n_blk),
+            _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return args, (off_arr, mode_arr, div_arr)
+
+
+def _unmask_call(name, logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+                 stream, check):
+    args, _keep = _unmask_args(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws, stream)
+    st = getattr(lib(), name)(*args)
     if check and st != BC_OK:
         raise BcError(st, name)
     return st
+
+
+def prepare_unmask_select(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws,
+                          stream=None):
+    """bc_unmask_select as a Prepared call."""
+    args, keep = _unmask_args(logits, blk_off, mode, n_div, threshold, masked, tokens, conf, n_commit, ws, stream)
+    return Prepared("bc_unmask_select", args, keep)
 
 
 def bc_verify_workspace_bytes(n_seq, n_lrows, vocab):

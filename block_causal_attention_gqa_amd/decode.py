@@ -397,6 +397,9 @@ class PipelinedDecode:
         self.length = np.array([self.prefix], np.int32)
         self.keep_inputs = False
         self._resident = {}
+        self._calls = {}
+        # the commit counts come back through pinned host memory
+        self.n_commit_host = torch.zeros(self.window, dtype=torch.int32).pin_memory()
 
     def logits_for(self, b, s):
         x = synth.logits(self.seed, self.blocks[b], self.V, self.sigma, 700 + b, s)
@@ -465,19 +468,36 @@ class PipelinedDecode:
             active = [b for b in range(committed, nb) if state[b] != "wait"]
             off = [0] + [int(x) for x in np.cumsum([self.blocks[b] for b in active])]
             rows = off[-1]
-            q, k, v, lg, blk_kv = self._step_inputs(active, [local[b] for b in active])
-            out = self.out[:, :rows]
-            B.bc_attn_step(self.cache, self.length, None, None, q, k, v, off, B.BC_MASK_BLOCK_BIDIR, self.scale,
-                           out, self.ws_attn, stream=stream)
-            if after_attn is not None:
-                after_attn(len(self.trace), list(active), [local[b] for b in active], int(self.length[0]), out)
-            r0, r1 = self.row0[active[0]], self.row0[active[-1] + 1]
+            steps = [local[b] for b in active]
             modes = [B.BC_UNMASK_FULL if state[b] == "full" else B.BC_UNMASK_SEMI for b in active]
-            divs = [self.n_div if state[b] == "full" else 1 for b in active]
-            nc = self.n_commit[:len(active)]
-            B.bc_unmask_select(lg, off, modes, divs, self.tau, self.masked[r0:r1], self.tokens[r0:r1], None, nc,
-                               self.ws_unmask, stream=stream)
-            counts = [int(x) for x in nc.cpu()]        # the next transitions depend on them
+            key = (tuple(active), tuple(steps), tuple(modes), B._stream(stream))
+            calls = self._calls.get(key)
+            if calls is None:
+                # the step's two library calls, marshalled once (with
+                # resident inputs they are kept and reissued on later runs)
+                q, k, v, lg, blk_kv = self._step_inputs(active, steps)
+                out = self.out[:, :rows]
+                r0, r1 = self.row0[active[0]], self.row0[active[-1] + 1]
+                divs = [self.n_div if state[b] == "full" else 1 for b in active]
+                nc = self.n_commit[:len(active)]
+                calls = (B.prepare_attn_step(self.cache, self.length, None, None, q, k, v, off,
+                                             B.BC_MASK_BLOCK_BIDIR, self.scale, out, self.ws_attn, stream=stream),
+                         B.prepare_unmask_select(lg, off, modes, divs, self.tau, self.masked[r0:r1],
+                                                 self.tokens[r0:r1], None, nc, self.ws_unmask, stream=stream),
+                         blk_kv, out, nc)
+                if self.keep_inputs:
+                    self._calls[key] = calls
+            attn, unmask, blk_kv, out, nc = calls
+            attn()
+            if after_attn is not None:
+                after_attn(len(self.trace), list(active), steps, int(self.length[0]), out)
+            unmask()
+            # the next transitions depend on the counts: copy them to pinned
+            # memory and wait for the stream
+            host = self.n_commit_host[:len(active)]
+            host.copy_(nc, non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+            counts = [int(x) for x in host.tolist()]
             for j, b in enumerate(active):
                 revealed[b] += counts[j]
                 local[b] += 1
