@@ -37,7 +37,8 @@ BC_MAX_SCAN_ROWS = 4096
 
 EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
             "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
-            "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide")
+            "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide",
+            "bc_pipeline_create", "bc_pipeline_destroy", "bc_pipeline_next", "bc_pipeline_report")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -98,6 +99,15 @@ def lib():
     L.bc_spec_verify.restype = ctypes.c_int
     L.bc_spec_verify_sampled.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.bc_spec_verify_sampled.restype = ctypes.c_int
+    L.bc_pipeline_create.argtypes = [_c_i32p, i32, i32, ctypes.c_double, ctypes.c_double, i32,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+    L.bc_pipeline_create.restype = ctypes.c_int
+    L.bc_pipeline_destroy.argtypes = [vp]
+    L.bc_pipeline_destroy.restype = None
+    L.bc_pipeline_next.argtypes = [vp, _c_i32p, _c_i32p, _c_i32p, _c_i32p, _c_i32p, _c_i32p]
+    L.bc_pipeline_next.restype = ctypes.c_int
+    L.bc_pipeline_report.argtypes = [vp, _c_i32p, _c_i32p]
+    L.bc_pipeline_report.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -369,3 +379,54 @@ def bc_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=No
     if check and st != BC_OK:
         raise BcError(st, "bc_spec_verify")
     return st
+
+
+class Pipeline:
+    """The pipelined parallel decoding schedule (bc_pipeline_*): a host state
+    machine, no GPU involved.  plan() returns the next step's (active blocks,
+    local steps, modes, n_div, blk_off, row0), or None when every block is
+    committed; report(n_commit) returns the blocks to commit, in order."""
+
+    def __init__(self, block_sizes, window, add, act, n_div):
+        sizes = np.ascontiguousarray(np.asarray(block_sizes, dtype=np.int32))
+        h = ctypes.c_void_p()
+        st = lib().bc_pipeline_create(sizes.ctypes.data_as(_c_i32p), len(sizes), int(window), float(add),
+                                      float(act), int(n_div), ctypes.byref(h))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_create")
+        self._h = h
+        self.window = int(window)
+        w = self.window
+        self._active, self._local, self._mode, self._div = (np.zeros(w, np.int32) for _ in range(4))
+        self._off = np.zeros(w + 1, np.int32)
+        self._row0 = np.zeros(1, np.int32)
+        self._done = np.zeros(w, np.int32)
+        self._counts = np.zeros(w, np.int32)
+        p = lambda a: a.ctypes.data_as(_c_i32p)
+        self._next_args = (h, p(self._active), p(self._local), p(self._mode), p(self._div), p(self._off),
+                           p(self._row0))
+
+    def plan(self):
+        n = lib().bc_pipeline_next(*self._next_args)
+        if n < 0:
+            raise BcError(n, "bc_pipeline_next")
+        if n == 0:
+            return None
+        return (self._active[:n].tolist(), self._local[:n].tolist(), self._mode[:n].tolist(),
+                self._div[:n].tolist(), self._off[:n + 1].tolist(), int(self._row0[0]))
+
+    def report(self, n_commit):
+        c = np.ascontiguousarray(np.asarray(n_commit, dtype=np.int32))
+        k = lib().bc_pipeline_report(self._h, c.ctypes.data_as(_c_i32p), self._done.ctypes.data_as(_c_i32p))
+        if k < 0:
+            raise BcError(k, "bc_pipeline_report")
+        return self._done[:k].tolist()
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.bc_pipeline_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()

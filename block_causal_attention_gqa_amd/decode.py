@@ -355,8 +355,9 @@ class PipelinedDecode:
       * a block whose tokens are all revealed is committed to the cache, with
         the K/V of its last step, as soon as every earlier block is: strictly
         in order, right after that step.
-    Transitions need each step's commit counts, so the host reads them back
-    after every step: the schedule is data-dependent and host-driven.
+    The schedule is the library's native state machine (``bc_pipeline_*``,
+    host code): it needs each step's commit counts, so the host reads them
+    back after every step; the schedule is data-dependent and host-driven.
 
     Block b's synthetic model outputs at its s-th active step are seeded
     draws: logits (``logits_for``) and the rows' Q/K/V (``qkv_for``)."""
@@ -444,32 +445,17 @@ class PipelinedDecode:
             return self._run(stream, after_attn)
 
     def _run(self, stream, after_attn):
-        nb = len(self.blocks)
-        state = ["wait"] * nb
-        local = [0] * nb
-        revealed = [0] * nb
-        committed = 0
+        sched = B.Pipeline(self.blocks, self.window, self.add, self.act, self.n_div)
         self.length[0] = self.prefix
         self.masked.fill_(1)
         self.tokens.fill_(-1)
         self.trace = []
-        while committed < nb:
-            state[committed] = "full"
-            n_active = sum(1 for x in range(committed, nb) if state[x] != "wait")
-            for b in range(committed + 1, nb):
-                if state[b - 1] == "wait":
-                    break
-                r = revealed[b - 1] / self.blocks[b - 1]
-                if state[b] == "wait" and r >= self.add and n_active < self.window:
-                    state[b] = "semi"
-                    n_active += 1
-                if state[b] == "semi" and r >= self.act:
-                    state[b] = "full"
-            active = [b for b in range(committed, nb) if state[b] != "wait"]
-            off = [0] + [int(x) for x in np.cumsum([self.blocks[b] for b in active])]
+        while True:
+            plan = sched.plan()
+            if plan is None:
+                break
+            active, steps, modes, divs, off, r0 = plan
             rows = off[-1]
-            steps = [local[b] for b in active]
-            modes = [B.BC_UNMASK_FULL if state[b] == "full" else B.BC_UNMASK_SEMI for b in active]
             key = (tuple(active), tuple(steps), tuple(modes), B._stream(stream))
             calls = self._calls.get(key)
             if calls is None:
@@ -477,13 +463,11 @@ class PipelinedDecode:
                 # resident inputs they are kept and reissued on later runs)
                 q, k, v, lg, blk_kv = self._step_inputs(active, steps)
                 out = self.out[:, :rows]
-                r0, r1 = self.row0[active[0]], self.row0[active[-1] + 1]
-                divs = [self.n_div if state[b] == "full" else 1 for b in active]
                 nc = self.n_commit[:len(active)]
                 calls = (B.prepare_attn_step(self.cache, self.length, None, None, q, k, v, off,
                                              B.BC_MASK_BLOCK_BIDIR, self.scale, out, self.ws_attn, stream=stream),
-                         B.prepare_unmask_select(lg, off, modes, divs, self.tau, self.masked[r0:r1],
-                                                 self.tokens[r0:r1], None, nc, self.ws_unmask, stream=stream),
+                         B.prepare_unmask_select(lg, off, modes, divs, self.tau, self.masked[r0:r0 + rows],
+                                                 self.tokens[r0:r0 + rows], None, nc, self.ws_unmask, stream=stream),
                          blk_kv, out, nc)
                 if self.keep_inputs:
                     self._calls[key] = calls
@@ -492,22 +476,19 @@ class PipelinedDecode:
             if after_attn is not None:
                 after_attn(len(self.trace), list(active), steps, int(self.length[0]), out)
             unmask()
-            # the next transitions depend on the counts: copy them to pinned
-            # memory and wait for the stream
+            # the next plan depends on the counts: copy them to pinned memory
+            # and wait for the stream
             host = self.n_commit_host[:len(active)]
             host.copy_(nc, non_blocking=True)
             torch.cuda.current_stream().synchronize()
             counts = [int(x) for x in host.tolist()]
-            for j, b in enumerate(active):
-                revealed[b] += counts[j]
-                local[b] += 1
-            done = []
-            while committed < nb and state[committed] != "wait" and revealed[committed] == self.blocks[committed]:
-                blk_k, blk_v = blk_kv[active.index(committed)]      # K/V of its last step
-                B.bc_kv_commit(self.cache, self.length, 0, int(self.length[0]), self.blocks[committed],
-                               blk_k, blk_v, stream=stream)
-                done.append(committed)
-                committed += 1
-            self.trace.append(dict(active=list(active), modes=[state[b] for b in active], n_commit=counts,
-                                   committed=done))
+            done = sched.report(counts)
+            for b in done:                          # in order, with the K/V of the block's last step
+                blk_k, blk_v = blk_kv[active.index(b)]
+                B.bc_kv_commit(self.cache, self.length, 0, int(self.length[0]), self.blocks[b], blk_k, blk_v,
+                               stream=stream)
+            self.trace.append(dict(active=list(active),
+                                   modes=["full" if m == B.BC_UNMASK_FULL else "semi" for m in modes],
+                                   n_commit=counts, committed=list(done)))
+        sched.close()
         return len(self.trace)

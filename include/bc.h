@@ -279,6 +279,50 @@ int bc_unmask_decide(const float *logits, int32_t n_rows, int32_t vocab,
                      uint8_t *masked, int32_t *tokens, float *conf, int32_t *n_commit,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* ---- Pipelined parallel decoding schedule (host only) --------------------
+ * Fast-dVLA reading notes, key design 4 ("pipelined parallel decoding"):
+ * several consecutive blocks of one sequence are denoised together; the
+ * first uncommitted block is fully active (threshold, plus at least
+ * ceil(remaining / n_div) per step), the block after an active one joins as
+ * semi-active (threshold only) once its predecessor's completion ratio --
+ * revealed rows / block size, compared in double precision with >= -- reaches
+ * `add` and fewer than `window` blocks are active, and turns fully active
+ * once that ratio reaches `act`.  Blocks are committed strictly in order,
+ * right after the step that reveals their last row.
+ *
+ * This is the schedule's state machine only; it runs on the host and touches
+ * no GPU.  Per step the caller asks for the plan (bc_pipeline_next), runs the
+ * step -- bc_attn_step over the active blocks' rows (BC_MASK_BLOCK_BIDIR,
+ * blk_off as planned), the model, bc_unmask_select with the planned modes
+ * and n_div over the same rows -- and reports the step's n_commit
+ * (bc_pipeline_report), which returns the blocks to bc_kv_commit, in order.
+ *
+ * bc_pipeline_create: block_sizes[n_blocks] (each >= 1, n_blocks <= 4096),
+ *   1 <= window <= BC_MAX_BLOCKS, n_div >= 1, add and act finite.  The
+ *   library allocates the state (host memory) and owns it until
+ *   bc_pipeline_destroy.  Errors: BC_ERR_ARG.
+ * bc_pipeline_next: writes, for the n active blocks (n <= window, returned;
+ *   0 once every block is committed), their ids (consecutive, oldest first),
+ *   local_step (how many steps each has been active before this one),
+ *   mode (BC_UNMASK_FULL / BC_UNMASK_SEMI), n_div (n_div for FULL, 1 for
+ *   SEMI) and blk_off[n + 1] (row offsets inside the step; rows are the
+ *   blocks' rows concatenated), and *row0, the first output row of the
+ *   first active block (output rows = all blocks' rows concatenated).
+ *   Calling it twice without a report returns the same plan.  Arrays hold
+ *   at least `window` (+1 for blk_off) entries.  Errors: BC_ERR_ARG.
+ * bc_pipeline_report: n_commit[n] of the planned step (0 <= n_commit[j] <=
+ *   the block's still-masked rows); writes the ids of the blocks that are
+ *   now complete and next in commit order to done[] (room for `window`)
+ *   and returns their count.  Errors: BC_ERR_ORDER without a plan,
+ *   BC_ERR_ARG for counts out of range (the state is left unchanged). */
+typedef struct bc_pipeline bc_pipeline;
+int bc_pipeline_create(const int32_t *block_sizes, int32_t n_blocks, int32_t window, double add,
+                       double act, int32_t n_div, bc_pipeline **out);
+void bc_pipeline_destroy(bc_pipeline *p);
+int bc_pipeline_next(bc_pipeline *p, int32_t *active, int32_t *local_step, int32_t *mode,
+                     int32_t *n_div, int32_t *blk_off, int32_t *row0);
+int bc_pipeline_report(bc_pipeline *p, const int32_t *n_commit, int32_t *done);
+
 /* Human-readable name of a bc_status value (never NULL). */
 const char *bc_status_str(int status);
 

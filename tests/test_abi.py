@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     with open(os.path.join(ROOT, "include", "bc.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(bc_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(bc_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
