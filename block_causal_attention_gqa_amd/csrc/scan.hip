@@ -272,51 +272,65 @@ struct SelectSmem {
   int tok[BC_MAX_BLOCK_ROWS];
   int rank[BC_MAX_BLOCK_ROWS];
   unsigned char st[BC_MAX_BLOCK_ROWS];
+  unsigned long long key[64];        // one-wave path: rank keys of rows 0 .. 63
   double red[kScanThreads];
   int cnt[2][kScanThreads / 64];
   double lohi[2][2 * (kScanThreads / 64)];
-  double cw[64];          // one-wave path: confidence of row i, -inf outside E
-  double cut[2];          // one-wave path: values at ranks k - 1 and k
   int done;
 };
 
+// A double held by lane `lane` (wave-uniform), in every lane.
+__device__ inline double readlane_f64(double v, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // Decisions of a block of at most 64 rows by wave 0 alone, lane i owning
-// row i, when no float64 refine is needed: counts are ballots, the rank is
-// taken against the block's confidences broadcast from LDS, and -- with no
-// refined row in the block, every row carries the same relative error band
-// -- the extreme of (c - e) over the top k and of (c + e) over the rest sit
-// at ranks k - 1 and k.  Returns false, having written nothing, when a row
-// is inside the threshold band or the cut is not certain; the caller then
+// row i, when no float64 refine is needed: counts are ballots; ranks by
+// (confidence desc, row asc) come from 64-bit integer keys, broadcast from
+// LDS and compared once per row -- the float32 confidence's bits (monotone for positive values)
+// above the complemented row index, rows outside E keyed 0 -- and, with no
+// refined row in the block, every row carrying the same relative error band,
+// the extreme of (c - e) over the top k and of (c + e) over the rest sit at
+// ranks k - 1 and k.  Ranking in float32 is exact wherever it is used: the
+// cut is accepted only when the float64 confidences at ranks k - 1 and k
+// differ by more than the band, which dwarfs float32 rounding (rows that
+// round to one float32 are ordered by row, and if they meet at the cut the
+// check fails).  Returns false, having written nothing, when a row is
+// inside the threshold band or the cut is not certain; the caller then
 // takes the workgroup-wide path, which refines.
-__device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, double tau, SelectSmem& sm) {
+__device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, double tau, int mode_b, int div_b,
+                                SelectSmem& sm) {
   const int i = threadIdx.x;
   const bool inE = i < nb && (sm.st[i] & kInE);
   const double c = inE ? sm.cf[i] : -__builtin_huge_val();
   if (__ballot(inE && fabs(c - tau) <= kBand * c)) return false;
-  sm.cw[i] = c;
   const unsigned long long eb = __ballot(inE), ab = __ballot(inE && c > tau);
   const int nE = __popcll(eb), nA = __popcll(ab);
   int k;
-  if (a.mode[b] == BC_UNMASK_SEMI) {
+  if (mode_b == BC_UNMASK_SEMI) {
     k = nA;
   } else {
-    const int fb = (nE + a.n_div[b] - 1) / a.n_div[b];
+    const int fb = (nE + div_b - 1) / div_b;
     k = min(nE, max(nA, fb));
   }
   const int how = k == 0 ? 0 : k == nE ? 1 : k == nA ? 2 : 3;
   int rk = 0;
   if (how == 3) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt 0: cw[] written by every lane
+    const uint32_t kc = inE ? __float_as_uint((float)c) : 0u;
+    const unsigned long long key = ((unsigned long long)kc << 32) | (uint32_t)(63 - i);
+    sm.key[i] = key;
+    __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt 0: every lane's key written
     __builtin_amdgcn_wave_barrier();
-    for (int q = 0; q < nb; ++q) {             // rows outside E hold -inf and never count
-      const double cq = sm.cw[q];
-      rk += cq > c || (cq == c && q < i);
-    }
-    if (inE && rk == k - 1) sm.cut[0] = c;
-    if (inE && rk == k) sm.cut[1] = c;
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    const double lo = sm.cut[0] - kBand * sm.cut[0], hi = sm.cut[1] + kBand * sm.cut[1];
+#pragma unroll 8
+    for (int q = 0; q < nb; ++q) rk += sm.key[q] > key;   // broadcast reads
+    // 1 <= k < nE, so ranks k - 1 and k are both rows of E
+    const unsigned long long at0 = __ballot(inE && rk == k - 1), at1 = __ballot(inE && rk == k);
+    if (!at0 || !at1) return false;
+    const double c0 = readlane_f64(c, __builtin_ctzll(at0)), c1 = readlane_f64(c, __builtin_ctzll(at1));
+    const double lo = c0 - kBand * c0, hi = c1 + kBand * c1;
     if (!(lo > hi)) return false;
   }
   if (inE) {
@@ -341,6 +355,7 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   const int r0 = a.blk_off[b];
   const int nb = a.blk_off[b + 1] - r0;
   const double tau = (double)a.threshold;
+  const int mode_b = a.mode[b], div_b = a.n_div[b];   // read early: their latency overlaps the merge
 
   // The masked flags and the chunk partials of every row are read in one
   // round: partials of revealed rows were not written by the scan and are
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   __syncthreads();
   if (nb <= 64) {
     if (tid < 64) {
-      const bool ok = decide_one_wave(a, b, r0, nb, tau, sm);
+      const bool ok = decide_one_wave(a, b, r0, nb, tau, mode_b, div_b, sm);
       if (tid == 0) sm.done = ok;
     }
     __syncthreads();
@@ -393,10 +408,10 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   const int packed = block_sum(my_e | (my_a << 16), sm.cnt[0]);
   const int nE = packed & 0xffff, nA = packed >> 16;
   int k;
-  if (a.mode[b] == BC_UNMASK_SEMI) {
+  if (mode_b == BC_UNMASK_SEMI) {
     k = nA;
   } else {
-    const int fb = (nE + a.n_div[b] - 1) / a.n_div[b];
+    const int fb = (nE + div_b - 1) / div_b;
     k = min(nE, max(nA, fb));
   }
 
