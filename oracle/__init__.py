@@ -17,6 +17,8 @@ Modules
              and its sampled form (Gumbel-max over supplied noise)
   pipeline   the pipelined parallel decoding schedule (semi / fully active
              blocks, add and activation thresholds, in-order commit)
+  section    the Section Diffusion decode schedule (block or section
+             visibility units, scaffold rows never masked, fixed steps)
 
 Sources (the pages the method is described on):
   * "Fast-dDrive" (Chinese translation of arXiv 2605.23163): abstract, sec. 1
