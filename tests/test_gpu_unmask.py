@@ -122,6 +122,30 @@ def test_rank_cut_near_ties_and_exact_ties():
         compare(x, [0, 8], [FULL], [n], 0.9, np.ones(8, np.uint8), np.zeros(8, np.int32))
 
 
+def test_float32_tied_confidences_around_the_cut():
+    # two-value rows with logits a and the next float32 above it, a ~ 1e-3:
+    # their confidences differ in float64 (by ~1e-10 relative) but round to
+    # one float32, and the larger sits at the higher row, so float32 order
+    # with the row tie-break disagrees with float64 order.  Sweeping n moves
+    # the rank cut onto, beside and away from the tied pairs; decisions must
+    # match the float64 oracle in every case.
+    V = 4096
+    base = [np.float32(1e-3), np.float32(2e-3), np.float32(0.2), np.float32(5e-4)]
+    a = []
+    for v in base:
+        a += [v, np.nextafter(v, np.float32(1.0))]        # lower logit first
+    x = np.stack([_two_value(float(v), V) for v in a])
+    conf = [1.0 / (1.0 + math.exp(-float(v))) for v in a]     # two finite logits: a and 0
+    for j in range(0, 8, 2):
+        assert conf[j] != conf[j + 1] and np.float32(conf[j]) == np.float32(conf[j + 1])
+    for n in range(1, 9):
+        compare(x, [0, 8], [FULL], [n], 0.9, np.ones(8, np.uint8), np.zeros(8, np.int32))
+    # the same rows in a block of 40 with random others around them
+    y = np.concatenate([x, synth.logits(8, 32, V, 4.0, 0)])
+    for n in (3, 5, 8, 13):
+        compare(y, [0, 40], [FULL], [n], 0.9, np.ones(40, np.uint8), np.zeros(40, np.int32))
+
+
 def test_argmax_ties_and_uniform_rows():
     V = 1000
     x = np.zeros((4, V), np.float32)
