@@ -232,3 +232,48 @@ def test_automatic_splits_shrink_to_the_workspace():
                        D ** -0.5, out, ws)
         got = out.float().cpu().numpy()
         assert np.abs(got - want).max() <= TOL["bf16"]
+
+
+# ---- the call limits: BC_MAX_BLOCKS active blocks, BC_MAX_SEQ sequences
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_max_blocks_ragged(mode):
+    # 64 active blocks of 1..9 rows over two ragged prefixes
+    sizes = np.random.default_rng(100).integers(1, 10, B.BC_MAX_BLOCKS)
+    off = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    _check(100 + mode, 2, off[-1], 16, 2, 128, "bf16", [700, 123], off, mode, cap=700)
+
+
+def test_max_sequences_own_prefixes():
+    # 64 sequences, each with its own prefix length (some empty, some one key)
+    lens = [0, 1, 900] + np.random.default_rng(101).integers(0, 901, B.BC_MAX_SEQ - 3).tolist()
+    _check(101, B.BC_MAX_SEQ, 12, 8, 2, 64, "bf16", lens, [0, 5, 12], BIDIR, cap=900)
+
+
+def test_max_sequences_and_max_blocks():
+    # 64 sequences x 64 blocks of one row: block-bidirectional with blocks of
+    # size one is causal decoding, and both masks give the oracle's result
+    lens = np.random.default_rng(102).integers(0, 301, B.BC_MAX_SEQ).tolist()
+    off = list(range(B.BC_MAX_BLOCKS + 1))
+    a = _check(102, B.BC_MAX_SEQ, B.BC_MAX_BLOCKS, 4, 1, 64, "bf16", lens, off, BIDIR, cap=300)
+    b = _check(102, B.BC_MAX_SEQ, B.BC_MAX_BLOCKS, 4, 1, 64, "bf16", lens, [0, B.BC_MAX_BLOCKS], CAUSAL,
+               cap=300)
+    assert np.array_equal(a, b)
+
+
+def test_one_past_the_sequence_and_block_limits_is_unsupported():
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    D, Hq, Hkv = 64, 4, 1
+    for S, R, off in [(B.BC_MAX_SEQ + 1, 2, [0, 2]),
+                      (1, B.BC_MAX_BLOCKS + 1, list(range(B.BC_MAX_BLOCKS + 2)))]:
+        (pk, pv), _ = synth.kv_cache(103, S, Hkv, 16, D, [16] * S, "bf16")
+        (q, _), (k, _), (v, _) = synth.active_qkv(103, S, R, Hq, Hkv, D, "bf16", 0)
+        prefix = B.KVCache(pk.to(G.DEV), pv.to(G.DEV))
+        out = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device=G.DEV)
+        assert B.bc_attn_workspace_bytes(prefix, None, (S, R, Hq, D), off) == 0
+        st = B.bc_attn_step(prefix, [16] * S, None, None, q.to(G.DEV), k.to(G.DEV), v.to(G.DEV), off, BIDIR,
+                            0.125, out, ws, check=False)
+        assert st == B.BC_ERR_UNSUPPORTED

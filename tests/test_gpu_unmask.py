@@ -261,3 +261,60 @@ def test_block_sizes_around_one_wave(sizes):
     masked = (np.random.default_rng(80 + R).random(R) < 0.8).astype(np.uint8)
     nb = len(sizes)
     compare(x, off, [FULL, SEMI, FULL, FULL][:nb], [5, 1, 3, 2][:nb], 0.9, masked, np.zeros(R, np.int32))
+
+
+# ---- the call limits: BC_MAX_SCAN_ROWS rows, BC_MAX_BLOCKS blocks,
+# BC_MAX_BLOCK_ROWS rows in one block, and one past each
+
+
+def test_max_scan_rows_in_max_blocks():
+    # 4096 rows in 64 blocks of 64: alternating modes, divisors 1..8, blocks
+    # fully masked, half masked and not masked at all
+    nb, bs, V = B.BC_MAX_BLOCKS, 64, 4096
+    R = nb * bs
+    assert R == B.BC_MAX_SCAN_ROWS
+    x = synth.logits(90, R, V, 4.0, 0)
+    synth.plant_peaks(x, 90, 0.15, 12.0, 0)
+    rng = np.random.default_rng(90)
+    frac = rng.choice([0.0, 0.5, 1.0], nb)
+    masked = (rng.random(R) < np.repeat(frac, bs)).astype(np.uint8)
+    modes = [FULL if b % 2 else SEMI for b in range(nb)]
+    divs = [1 + b % 8 for b in range(nb)]
+    compare(x, list(range(0, R + 1, bs)), modes, divs, 0.9, masked, np.zeros(R, np.int32))
+
+
+@pytest.mark.parametrize("n_blk", [1, 4])
+def test_blocks_of_max_rows(n_blk):
+    # blocks of 1024 rows (the workgroup decide path at its largest); four of
+    # them fill the scan-row limit
+    bs, V = B.BC_MAX_BLOCK_ROWS, 2048
+    R = n_blk * bs
+    x = synth.logits(91, R, V, 4.0, n_blk)
+    synth.plant_peaks(x, 91, 0.1, 12.0, n_blk)
+    masked = (np.random.default_rng(91 + n_blk).random(R) < 0.9).astype(np.uint8)
+    compare(x, list(range(0, R + 1, bs)), [FULL, SEMI, FULL, FULL][:n_blk], [3, 1, 7, 1024][:n_blk], 0.9,
+            masked, np.zeros(R, np.int32))
+
+
+def test_one_past_each_limit_is_unsupported():
+    V = 8
+
+    def status(R, off):
+        lg = G.to_dev(np.zeros((R, V), np.float32))
+        m = G.to_dev(np.ones(R, np.uint8))
+        t = G.to_dev(np.zeros(R, np.int32))
+        nc = torch.zeros(len(off) - 1, dtype=torch.int32, device=G.DEV)
+        ws = torch.zeros(B.bc_unmask_workspace_bytes(min(R, B.BC_MAX_SCAN_ROWS), V), dtype=torch.uint8,
+                         device=G.DEV)
+        n = len(off) - 1
+        return B.bc_unmask_select(lg, off, [FULL] * n, [1] * n, 0.9, m, t, None, nc, ws, check=False)
+
+    R = B.BC_MAX_SCAN_ROWS + 1
+    assert status(R, [0, 1024, 2048, 3072, 4096, R]) == B.BC_ERR_UNSUPPORTED
+    assert status(B.BC_MAX_BLOCK_ROWS + 1, [0, B.BC_MAX_BLOCK_ROWS + 1]) == B.BC_ERR_UNSUPPORTED
+    nb = B.BC_MAX_BLOCKS + 1
+    assert status(nb, list(range(nb + 1))) == B.BC_ERR_UNSUPPORTED
+    assert B.bc_unmask_workspace_bytes(B.BC_MAX_SCAN_ROWS + 1, V) == 0
+    # the limits themselves are accepted
+    assert status(B.BC_MAX_BLOCK_ROWS, [0, B.BC_MAX_BLOCK_ROWS]) == B.BC_OK
+    assert status(B.BC_MAX_BLOCKS, list(range(B.BC_MAX_BLOCKS + 1))) == B.BC_OK

@@ -131,3 +131,31 @@ def test_sampled_verify_argument_errors():
     st = B.lib().bc_spec_verify_sampled(x.data_ptr(), None, ctypes.c_float(1.0), S, L, V, d.data_ptr(), L, None,
                                         f.data_ptr(), acc.data_ptr(), bon.data_ptr(), ws.data_ptr(), ws.numel(), None)
     assert st == B.BC_ERR_ARG
+
+
+@pytest.mark.parametrize("S,L", [(64, 64), (1, 4096)])
+def test_scan_row_limit(S, L):
+    # S * L = 4096 logit rows, the most one call takes: 64 rollouts of 64 rows,
+    # and one sequence of 4096
+    assert S * L == B.BC_MAX_SCAN_ROWS
+    V = 2048
+    lg = np.empty((S, L, V), np.float32)
+    draft = np.empty((S, L), np.int32)
+    for s in range(S):
+        lg[s], t = synth.argmax_planted_logits(12, L, V, 4.0, 0.5, s)
+        draft[s] = synth.drafts_with_agreement(12, t, 0.97 if S > 1 else 0.999, V, s)
+    fixed = (np.random.default_rng(S).random((S, L)) < 0.1).astype(np.uint8)
+    first = np.random.default_rng(S + 1).integers(0, 8, S)
+    compare(lg, draft, None, np.zeros(S, np.int32))
+    compare(lg, draft, fixed, first)
+
+
+def test_one_past_the_scan_row_limit_is_unsupported():
+    S, L, V = 65, 64, 4
+    lg = G.to_dev(np.zeros((S, L, V), np.float32))
+    d = G.to_dev(np.zeros((S, L), np.int32))
+    f = G.to_dev(np.zeros(S, np.int32))
+    a = torch.zeros(S, dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(B.bc_verify_workspace_bytes(64, L, V), dtype=torch.uint8, device=G.DEV)
+    assert B.bc_verify_workspace_bytes(S, L, V) == 0
+    assert B.bc_spec_verify(lg, d, None, f, a, a.clone(), ws, check=False) == B.BC_ERR_UNSUPPORTED
