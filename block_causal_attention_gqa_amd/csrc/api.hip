@@ -39,6 +39,7 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 // ------------------------------------------------------------ attention plan
 struct Plan {
   int waves, cols, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  bool compact;        // compact split partials (bf16 inputs, many rows)
   size_t o_bytes, ml_bytes, total_bytes;
 };
 
@@ -77,10 +78,10 @@ int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_a
 // 64-key tile with one workgroup per CU and ~2.5 us with two (512
 // co-resident), ~2 us of fixed cost per item (Q load, first tile, partial
 // write), K/V and partial slots streamed at ~5 TB/s.
-int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, int D) {
+int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, double slot_row_bytes) {
   constexpr int kCUs = 256, kSlotsResident = 512;
   constexpr double kTileUs1 = 1.9, kTileUs2 = 2.5, kItemUs = 2.0, kBytesPerUs = 5.0e6;
-  const double slot_us = (double)rows_total * (D * 4.0 + 8.0) * 2.0 / kBytesPerUs;
+  const double slot_us = (double)rows_total * slot_row_bytes * 2.0 / kBytesPerUs;
   const double floor_us = kv_bytes / kBytesPerUs + kItemUs;
   const int most = std::max(1, std::min(256, (maxlen + kAttnKeyTile - 1) / kAttnKeyTile));
   int best = 1;
@@ -105,6 +106,16 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   const int S = a->n_seq, R = a->n_rows, Hq = a->n_q_heads, Hkv = prefix->n_kv_heads;
   const int group = Hq / Hkv, D = prefix->head_dim;
   const bool fork = priv != nullptr;
+  // Split partials: compact (int16 output, 16-byte record) for bf16 inputs
+  // with many output rows, where their write and read-back is a large part
+  // of the call; float32 otherwise.  The extra quantising work sits on every
+  // workgroup's tail, which a latency-bound call with few rows pays for
+  // (measured: +4% at 512 rows, -14% at 1536 rows over a 3282-key prefix).
+  // The choice depends on the shapes only, so the workspace size a call
+  // needs never exceeds the size at full capacity.
+  const bool compact = prefix->dtype == BC_BF16 && S * R * Hq >= kCompactRows;
+  p->compact = compact;
+  const double slot_row_bytes = compact ? D * 2.0 + 16.0 : D * 4.0 + 8.0;
   const int groups = fork ? Hkv : S * Hkv;
   const int rows_group = fork ? S * R * group : R * group;
   // Row tiles of 128 rows (4 waves x 32).  With few row tiles (small
@@ -123,7 +134,7 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
     // K/V bytes of the prefix as streamed from HBM (a shared fork prefix once)
     double kv = 0;
     for (int s = 0; s < prefix->n_seq; ++s) kv += (double)lengths[s] * Hkv * D * 2.0 * elem_bytes(prefix->dtype);
-    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, D);
+    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes);
   }
   p->P = P;
   for (int s = 0; s < prefix->n_seq; ++s) {
@@ -134,8 +145,8 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   p->n_prefix_items = groups * P * p->n_mt_prefix;
   p->n_items = p->n_prefix_items + S * Hkv * p->n_mt_active;
   p->rows_total = S * R * Hq;
-  p->o_bytes = align256((size_t)p->n_slots * p->rows_total * D * sizeof(float));
-  p->ml_bytes = align256((size_t)p->n_slots * p->rows_total * 2 * sizeof(float));
+  p->o_bytes = align256((size_t)p->n_slots * p->rows_total * D * (compact ? 2 : 4));
+  p->ml_bytes = align256((size_t)p->n_slots * p->rows_total * (compact ? 16 : 8));
   p->total_bytes = p->o_bytes + p->ml_bytes;
 }
 
@@ -238,8 +249,9 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   }
   args->ak = a->k;
   args->av = a->v;
-  args->ws_o = static_cast<float*>(ws);
-  args->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.o_bytes);
+  args->ws_o = ws;
+  args->ws_ml = static_cast<char*>(ws) + p.o_bytes;
+  args->compact = p.compact ? 1 : 0;
   args->scale_log2 = scale * 1.4426950408889634f;
   args->S = a->n_seq;
   args->R = a->n_rows;

@@ -59,6 +59,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t bf16_t;   // raw bf16 storage
 
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -270,14 +271,16 @@ __device__ inline void softmax_tile(f32x4 (&st)[CT][4], f32x4 (&o)[CT][D / 16], 
   }
 }
 
-// this item's partial for the lane's columns.  Non-temporal stores: the
-// partials are read once, by the combine, so they are not kept in L2.
-// (kGroupSum: l_run holds each lane group's share of the column sum, added
-// up here; otherwise every lane already holds the full sum)
+// this item's float32 partial for the lane's columns.  Non-temporal
+// stores: the partials are read once, by the combine, so they are not kept
+// in L2.  (kGroupSum: l_run holds each lane group's share of the column
+// sum, added up here; otherwise every lane already holds the full sum)
 template <int D, int CT, bool kGroupSum = true>
-__device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
-                                     const float (&m_run)[CT], const float (&l_run)[CT],
-                                     const f32x4 (&o)[CT][D / 16], int jj) {
+__device__ inline void write_partial_f32(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
+                                         const float (&m_run)[CT], const float (&l_run)[CT],
+                                         const f32x4 (&o)[CT][D / 16], int jj) {
+  float* ws_o = static_cast<float*>(a.ws_o);
+  float2* ws_ml = static_cast<float2*>(a.ws_ml);
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     float l = l_run[c];
@@ -288,12 +291,59 @@ __device__ inline void write_partial(const AttnArgs& a, int slot, const bool (&v
     if (!valid[c]) continue;
     const long long prow = (long long)slot * a.rows_total + orow[c];
     if (jj == 0) {
-      __builtin_nontemporal_store(m_run[c], &a.ws_ml[prow].x);
-      __builtin_nontemporal_store(l, &a.ws_ml[prow].y);
+      __builtin_nontemporal_store(m_run[c], &ws_ml[prow].x);
+      __builtin_nontemporal_store(l, &ws_ml[prow].y);
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      __builtin_nontemporal_store(o[c][dt], reinterpret_cast<f32x4*>(&a.ws_o[prow * D + 16 * dt + 4 * jj]));
+      __builtin_nontemporal_store(o[c][dt], reinterpret_cast<f32x4*>(&ws_o[prow * D + 16 * dt + 4 * jj]));
+  }
+}
+
+// this item's compact partial (bf16 inputs): the unnormalised output of a
+// row is stored as int16 against one power of two per (slot, row),
+//   h_d = rint(o_d 2^(14 - e)),  2^(e - 1) <= max_d |o_d| < 2^e,
+// so |h_d| < 2^14 and o_d = c h_d with c = 2^(e - 14), to within
+// c / 2 <= 2^-14 max_d |o_d|.  After the merge the error is at most 2^-14
+// of the largest |V| element the row attends to, far below the bf16
+// rounding of the output; the bytes per row and slot drop from 520 to 272.
+// Every lane already holds its column's full sum in l_run.  A row's D
+// values sit in the four lanes n, n + 16, n + 32, n + 48: lane group jj
+// holds dims 16 dt + 4 jj + i.  The record is laid out lane-major,
+// position jj D / 4 + 4 dt + i, so each lane writes D / 2 contiguous bytes
+// with 16-byte stores.
+template <int D, int CT>
+__device__ inline void write_partial_q16(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
+                                         const float (&m_run)[CT], const float (&l_run)[CT],
+                                         const f32x4 (&o)[CT][D / 16], int jj) {
+  int16_t* ws_o = static_cast<int16_t*>(a.ws_o);
+  f32x4* ws_ml = static_cast<f32x4*>(a.ws_ml);
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    float mo = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo = fmaxf(mo, fabsf(o[c][dt][i]));
+    mo = group4_max(mo);
+    const int e = mo > 0.f ? __builtin_amdgcn_frexp_expf(mo) : 0;
+    const float up = __builtin_amdgcn_ldexpf(1.f, 14 - e);
+    if (!valid[c]) continue;
+    const long long prow = (long long)slot * a.rows_total + orow[c];
+    if (jj == 0)
+      __builtin_nontemporal_store(f32x4{m_run[c], l_run[c], __builtin_amdgcn_ldexpf(1.f, e - 14), 0.f}, &ws_ml[prow]);
+    u32x4 h[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 x = o[c][dt] * up;
+      const auto lo = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(x[0]), (int)__builtin_rintf(x[1]));
+      const auto hi = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(x[2]), (int)__builtin_rintf(x[3]));
+      h[dt >> 1][2 * (dt & 1)] = __builtin_bit_cast(uint32_t, lo);
+      h[dt >> 1][2 * (dt & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
+    }
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k)
+      __builtin_nontemporal_store(h[k], reinterpret_cast<u32x4*>(&ws_o[prow * D + jj * (D / 4) + 8 * k]));
   }
 }
 
@@ -642,7 +692,8 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   float l_run[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) l_run[c] = osum[c][0];
-  write_partial<D, CT, false>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  if (a.compact) write_partial_q16<D, CT>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  else write_partial_f32<D, CT, false>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // ============================================================ fp32 partial
@@ -755,18 +806,20 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
     }
   }
 
-  write_partial<D, 2>(a, it.slot, valid, orow, m_run, l_run, o, jj);
+  write_partial_f32<D, 2>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
 // w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  D / 4
-// lanes per row take 4 dims (16 bytes) each, so a row's slot is one
-// contiguous read.  SW groups of those lanes split the slots of a row (SW = 1
+// lanes per row take 4 dims each (16 bytes of float32, or 8 bytes of int16
+// scaled by the record's c for bf16 outputs), so a row's slot is one
+// contiguous read; with compact records lane k writes dims
+// 16 (k % (D / 16)) + 4 (k / (D / 16)) + 0..3 of the output.  SW groups of those lanes split the slots of a row (SW = 1
 // for many rows and few slots, 8 for few rows and many slots); each group
 // takes its slots four at a time with every load of the batch issued first,
 // rescaling its running sums when a batch raises the max, and the groups
 // merge through LDS.
-template <typename T, int D, int SW>
+template <typename T, int D, int SW, bool kCompact>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   constexpr int LPR = D / 4;            // lanes per row and slot group
   constexpr int RPB = 256 / (LPR * SW); // rows per workgroup
@@ -776,7 +829,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   const int t = threadIdx.x;
   const int sub = (t / LPR) % SW;
   const int row = blockIdx.x * RPB + t / (LPR * SW);
-  const int d0 = (t % LPR) * 4;
+  const int d0 = (t % LPR) * 4;                 // record position of this lane's 4 values
+  // the dims they hold: the position itself, or for the lane-major compact
+  // record (position jj D / 4 + 4 dt + i) dim 16 dt + 4 jj + i
+  const int dim0 = kCompact ? 16 * ((t % LPR) % (D / 16)) + 4 * ((t % LPR) / (D / 16)) : d0;
   const bool live = row < a.rows_total;
   float wm = kNegInf, wl = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -790,8 +846,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
       ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < a.n_slots) {
         const long long prow = (long long)s * a.rows_total + row;
-        ml[u] = a.ws_ml[prow];
-        ov[u] = *reinterpret_cast<const f32x4*>(&a.ws_o[prow * D + d0]);
+        if constexpr (kCompact) {
+          const f32x4 r = static_cast<const f32x4*>(a.ws_ml)[prow];
+          const u32x2 h = *reinterpret_cast<const u32x2*>(static_cast<const int16_t*>(a.ws_o) + prow * D + d0);
+          ml[u] = float2{r[0], r[1]};
+          ov[u] = f32x4{(float)(int16_t)(h[0] & 0xffffu), (float)(int16_t)(h[0] >> 16),
+                        (float)(int16_t)(h[1] & 0xffffu), (float)(int16_t)(h[1] >> 16)} * r[2];
+        } else {
+          ml[u] = static_cast<const float2*>(a.ws_ml)[prow];
+          ov[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + prow * D + d0);
+        }
       }
     }
     float bm = kNegInf;
@@ -835,7 +899,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   }
   const float inv = wl > 0.f ? 1.f / wl : 0.f;
   acc *= inv;
-  T* out = static_cast<T*>(a.out) + (long long)row * D + d0;
+  T* out = static_cast<T*>(a.out) + (long long)row * D + dim0;
   if constexpr (sizeof(T) == 2) {
     uint16_t h[4];
 #pragma unroll
@@ -870,8 +934,11 @@ hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
 template <typename T, int D, int SW>
 hipError_t launch_combine_sw(const AttnArgs& a, hipStream_t stream) {
   constexpr int rows_per_block = 256 / (D / 4 * SW);
-  hipLaunchKernelGGL((attn_combine_kernel<T, D, SW>), dim3((a.rows_total + rows_per_block - 1) / rows_per_block),
-                     dim3(256), 0, stream, a);
+  const dim3 grid((a.rows_total + rows_per_block - 1) / rows_per_block);
+  if (sizeof(T) == 2 && a.compact)
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, sizeof(T) == 2>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace bc {
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
+constexpr int kCompactRows = 1024;        // bf16 calls with at least this many output rows use compact partials
 
 struct AttnArgs {
   const void* q;       // [S][R][Hq][D]
@@ -23,8 +24,14 @@ struct AttnArgs {
   long long v_seq_stride, v_head_stride;
   const void* ak;      // active K/V [S][Hkv][R][D]
   const void* av;
-  float* ws_o;         // [n_slots][rows_total][D] unnormalised partial outputs
-  float2* ws_ml;       // [n_slots][rows_total] (running max in log2 units, sum)
+  // Split partials, [n_slots][rows_total] records of the unnormalised
+  // output o (D values), the running max m (log2 units) and the sum l:
+  //   float32:  ws_o float [..][D] = o, ws_ml float2 {m, l};
+  //   compact:  ws_o int16 [..][D] = h (lane-major order), ws_ml float4
+  //             {m, l, c, 0}, with o = c h (c a power of two per record).
+  void* ws_o;
+  void* ws_ml;
+  int compact;         // 1: compact partials (bf16 inputs only)
   float scale_log2;    // softmax scale * log2(e)
   int S, R, Hq, Hkv, group, D;
   int waves;           // waves per workgroup (2 or 4)

@@ -253,8 +253,11 @@ int bc_spec_verify_sampled(const float *logits, const float *noise, float inv_te
  *
  * bc_attn_step(args) == bc_attn_partial(args); bc_attn_combine(args).
  *   The partial pass leaves, per key split, the running max, the softmax
- *   denominator and the unnormalised output of every row in the workspace;
- *   the combine pass merges them with log-sum-exp weights into `out`.
+ *   denominator and the unnormalised output of every row in the workspace
+ *   (float32; for bf16 inputs with n_seq * n_rows * n_q_heads >= 1024, int16
+ *   against a power of two per row and split, within 2^-14 of the row's
+ *   largest element); the combine pass merges them with log-sum-exp weights
+ *   into `out`.
  *
  * bc_unmask_select(args) == bc_vocab_scan(logits, n_rows, vocab, masked, 1,
  *   ws, ws_bytes, stream); bc_unmask_decide(args).

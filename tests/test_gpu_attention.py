@@ -277,3 +277,41 @@ def test_one_past_the_sequence_and_block_limits_is_unsupported():
         st = B.bc_attn_step(prefix, [16] * S, None, None, q.to(G.DEV), k.to(G.DEV), v.to(G.DEV), off, BIDIR,
                             0.125, out, ws, check=False)
         assert st == B.BC_ERR_UNSUPPORTED
+
+
+# ---- split partial formats: float32 below 1024 output rows, compact (int16
+# against a power of two per row and slot) from 1024 rows with bf16 inputs
+
+
+@pytest.mark.parametrize("splits", [1, 5, 64])
+def test_compact_partials_with_empty_chunks(splits):
+    # 128 rows x 8 heads = 1024 output rows; most of the forced chunks of a
+    # 97-key prefix are empty
+    _check(111, 1, 128, 8, 2, 128, "bf16", [97], [0, 40, 128], CAUSAL, cap=200, n_splits=splits)
+
+
+@pytest.mark.parametrize("R", [32, 128])   # 512 output rows: float32 partials; 2048: compact
+def test_output_scales_exactly_with_power_of_two_values(R):
+    # Scaling V by a power of two scales every partial, every record's scale
+    # and the merged output by the same power of two, with no new rounding:
+    # the outputs must match bit for bit, and V = 0 must give exactly 0.
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    seed, S, Hq, Hkv, D, L = 112, 1, 16, 2, 128, 1500
+    (pk, pv), _ = synth.kv_cache(seed, S, Hkv, L, D, [L], "bf16")
+    (q, _), (k, _), (v, _) = synth.active_qkv(seed, S, R, Hq, Hkv, D, "bf16", 0)
+    blk = [0, R // 2, R]
+    ws = torch.zeros(B.bc_attn_workspace_bytes(B.KVCache(pk.to(G.DEV), pv.to(G.DEV)), None, (S, R, Hq, D), blk),
+                     dtype=torch.uint8, device=G.DEV)
+    outs = {}
+    for f in (1.0, 2.0 ** 10, 2.0 ** -20, 0.0):
+        prefix = B.KVCache(pk.to(G.DEV), (pv * f).to(G.DEV))
+        out = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+        B.bc_attn_step(prefix, [L], None, None, q.to(G.DEV), k.to(G.DEV), (v * f).to(G.DEV), blk, BIDIR,
+                       D ** -0.5, out, ws)
+        torch.cuda.synchronize()
+        outs[f] = out.float().cpu()
+    assert outs[1.0].abs().max() > 0.1
+    assert torch.equal(outs[2.0 ** 10], outs[1.0] * 2.0 ** 10)
+    assert torch.equal(outs[2.0 ** -20], outs[1.0] * 2.0 ** -20)
+    assert not outs[0.0].any()
