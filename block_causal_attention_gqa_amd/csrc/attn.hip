@@ -649,7 +649,23 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     bf16x8 pb[CT][2];
     probs(s_cur, alpha, muse, pb);
     accumulate(odd ? v_st1 : v_st0, pb);
-    if constexpr (CT > 1) __builtin_amdgcn_s_setprio(0);
+    if constexpr (CT > 1) {
+      // Left alone, the scheduler issues the score MFMAs back to back and
+      // the exponentials after them.  Interleave them: per 16-key tile the
+      // four K operand reads, then each MFMA followed by three vector
+      // instructions (an MFMA occupies the matrix core for 16 cycles and
+      // the issue port for about 6; an exponential costs about three FMAs).
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
     if constexpr (!kLast) tile_barrier();
   };
 
