@@ -61,8 +61,8 @@ hipError_t launch_commit(void* k_cache, void* v_cache, const void* blk_k, const 
 
 // -------------------------------------------------------------- vocab scans
 constexpr int kScanThreads = 256;
-constexpr int kScanVecPerThread = 8;                                // float4 per thread
-constexpr int kScanChunk = kScanThreads * kScanVecPerThread * 4;    // 8192 logits
+constexpr int kScanVecPerThread = 4;                                // float4 per thread
+constexpr int kScanChunk = kScanThreads * kScanVecPerThread * 4;    // 4096 logits
 
 struct ScanPartial { float m; int a; float s; int pad; };
 

@@ -13,7 +13,7 @@
 //     from softmax(l / T)).
 //
 // Two kernels per call.  The scan is one pass over HBM: a (chunk, row) grid
-// where each workgroup reads 8192 logits with 16-byte loads (8 per lane,
+// where each workgroup reads 4096 logits with 16-byte loads (4 per lane,
 // all in flight before any arithmetic), reduces max / argmax / exp-sum inside
 // the wave and across the 4 waves, and leaves one 16-byte partial.  Rows that
 // need no scan (already revealed, or outside the verified range) skip the
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
 }
 
 // Merge the chunk partials of rows r0 .. r0 + nr - 1 that `want(i)`:
-// 8 lanes per row, up to 4 chunks per lane per round, one round of loads for
-// vocabularies up to 32 chunks.  `sink(i, acc)` receives each merged row
+// 8 lanes per row, up to 8 chunks per lane per round, one round of loads for
+// vocabularies up to 64 chunks (262144 logits).  `sink(i, acc)` receives each merged row
 // (called by one lane per row).
 template <typename Want, typename Sink>
 __device__ void merge_rows(const ScanPartial* part, int n_chunks, int r0, int nr, Want want, Sink sink) {
@@ -198,16 +198,16 @@ __device__ void merge_rows(const ScanPartial* part, int n_chunks, int r0, int nr
     const int i = i0 + tid / kLanes;
     const bool use = i < nr && want(i);
     Acc t{kNegInf, INT_MAX, 0.f};
-    for (int c0 = 0; c0 < n_chunks; c0 += 4 * kLanes) {
-      ScanPartial p[4];
+    for (int c0 = 0; c0 < n_chunks; c0 += 8 * kLanes) {
+      ScanPartial p[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int c = c0 + sub + kLanes * u;
         p[u] = ScanPartial{kNegInf, INT_MAX, 0.f, 0};
         if (use && c < n_chunks) p[u] = part[(long long)(r0 + i) * n_chunks + c];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) t = merge(t, Acc{p[u].m, p[u].a, p[u].s});
+      for (int u = 0; u < 8; ++u) t = merge(t, Acc{p[u].m, p[u].a, p[u].s});
     }
     t = lanes_merge<kLanes>(t);
     if (use && sub == 0) sink(i, t);

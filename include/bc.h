@@ -263,7 +263,7 @@ int bc_spec_verify_sampled(const float *logits, const float *noise, float inv_te
  *   ws, ws_bytes, stream); bc_unmask_decide(args).
  *   bc_vocab_scan leaves, for every row r with row_mask == NULL or
  *   row_mask[r] != 0, the max, the lowest argmax and (with_sum != 0) the sum
- *   of exp(l - max) of each 8192-logit chunk of the row in the workspace
+ *   of exp(l - max) of each 4096-logit chunk of the row in the workspace
  *   (sized by bc_unmask_workspace_bytes); bc_unmask_decide merges them and
  *   takes the decisions.  `masked` must not change between the two. */
 int bc_attn_partial(const bc_kv_cache *prefix, const int32_t *prefix_len,
