@@ -209,6 +209,7 @@ def main():
                 "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": partial_bytes / n_attn, "avg_launch_us": round(avg["attn_partial"], 3)}
     kernel_us = {k: round(v, 3) for k, v in avg.items()}
+    cold = cache_states(stream, dec, call_args, masked_before)
 
     tokens = dec.tokens_per_decode
     value = tokens * args.steps / (ms_total * 1e-3)
@@ -237,6 +238,7 @@ def main():
         "unmask": {"scan_us": round(avg["vocab_scan"], 3), "scan_GB_s": round(scan_gbs, 1),
                    "avg_masked_rows": float(np.mean(masked_rows))},
         "kernel_avg_us": kernel_us,
+        "cache_states": cold,
         "roofline": roof,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 2),
@@ -250,6 +252,82 @@ def main():
 
 
 TRAFFIC_SUMMARY = "profiles/attn_partial_section_decode_traffic.md"
+
+
+def cache_states(stream, dec, call_args, masked_before, reps=20, replays=5):
+    """Cold and warm call times at the bs1 shape: the attention call
+    (partial + combine) and the unmask select of the first denoise step of
+    the first 32-row block.  One graph holds reps repetitions of [a 512 MiB
+    write, the call] (cold: the 256 MB MALL and the L2 hold none of the
+    call's data, and are full of dirty lines), another the same writes
+    alone; the call time is their difference / reps.  Warm: the same with a
+    GPU spin that touches no memory in place of the write (the call's data
+    stay where the previous call left them).  Median over the replays."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    b = next(i for i, bs in enumerate(dec.blocks) if bs == 32)
+    off, bs = sum(dec.blocks[:b]), dec.blocks[b]
+    i = b * dec.steps
+    a_args, lg = call_args[i]
+    masked, tokens = dec.masked[off: off + bs], dec.tokens[off: off + bs]
+    saved = masked_before[i]
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dec.masked.device)   # 512 MiB
+
+    def attn():
+        B.bc_attn_step(*a_args, stream=stream)
+
+    def unmask():
+        masked.copy_(saved)
+        B.bc_unmask_select(lg, [0, bs], [B.BC_UNMASK_FULL], [dec.steps], dec.tau, masked, tokens, dec.conf[:bs],
+                           dec.n_commit[:1], dec.ws_unmask, stream=stream)
+
+    def restore():
+        masked.copy_(saved)
+
+    def pre(cold):
+        if cold:
+            flush.fill_(1.0)
+        else:
+            torch.cuda._sleep(100000)
+
+    def graph_ms(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            body()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                body()
+            ts = []
+            for _ in range(replays):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts]))
+
+    out = {"shape": "bs1, 32-row block over a %d-key prefix, vocab %d, %d masked rows"
+                    % (int(a_args[1][0]), dec.V, int(saved.sum().item())),
+           "flush_bytes": flush.numel() * 4, "reps_per_graph": reps}
+    for name, fn, base in (("attn_step_us", attn, lambda: None), ("unmask_select_us", unmask, restore)):
+        out[name] = {}
+        for state, cold in (("cold", True), ("warm", False)):
+            def with_call():
+                for _ in range(reps):
+                    pre(cold)
+                    fn()
+
+            def without():
+                for _ in range(reps):
+                    pre(cold)
+                    base()
+            out[name][state] = round((graph_ms(with_call) - graph_ms(without)) * 1e3 / reps, 3)
+    masked.zero_()
+    b_, _ = attn_bytes_flops(int(a_args[1][0]), bs, dec.Hq, dec.Hkv, dec.D)
+    out["attn_TB_s"] = {k: round(b_ / (v * 1e-6) / 1e12, 4) for k, v in out["attn_step_us"].items()}
+    return out
 
 
 def measured_traffic():
