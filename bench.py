@@ -497,9 +497,12 @@ def legs(stream):
                      "max_active": max(len(st["active"]) for st in pd.trace)}
         del pd
     out["pipelined_625"] = pip
-    # launch floor: a one-element fill kernel
+    # latency floors: a one-element fill kernel, and a copy of 256 floats
+    # (one load and one store per lane)
     x = torch.zeros(1, device="cuda:0")
     out["launch_floor_us"] = round(graph_us(lambda: x.fill_(1.0), stream, reps=50), 3)
+    src, dst = torch.ones(256, device="cuda:0"), torch.empty(256, device="cuda:0")
+    out["load_floor_us"] = round(graph_us(lambda: dst.copy_(src), stream, reps=50), 3)
     return out
 
 
