@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: issue one decode's attention-partial launches and a "
                          "256 MiB device copy (the counters' calibration), print one JSON line, exit")
+    ap.add_argument("--fork-pass", action="store_true",
+                    help="for profiler runs: issue the N = 64 fork round's two attention calls (draft pass, "
+                         "verify pass) 10 times each, print one JSON line, exit")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the secondary measurements (fork round, batch-16 attention, verify scan)")
     return ap.parse_args()
@@ -70,6 +73,9 @@ def main():
     B.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
+    if args.fork_pass:
+        fork_pass()
+        return
     preset = synth.PRESETS["section"]
     t0 = time.time()
     dec = decode.SectionDecode(preset, seed=args.seed, device=dev)
@@ -353,6 +359,26 @@ def measured_traffic():
     if h.hexdigest() != fields["source_sha256"]:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def fork_pass(N=64, reps=10):
+    """The shared-prefix fork round's attention calls at N rollouts (3282
+    shared keys, 24 rows x 16 heads per rollout), each pass issued reps
+    times after one warm call, for kernel traces and MFMA counters."""
+    import torch
+    from block_causal_attention_gqa_amd import decode, synth
+    fv = decode.ForkVerify(N, seed=0, device="cuda:0", block=0, preset=dict(synth.PRESETS["fork"], vocab=1024))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for pass_id in (0, 1):
+            fv.attention(pass_id, stream)
+        torch.cuda.synchronize()
+        for pass_id in (0, 1):
+            for _ in range(reps):
+                fv.attention(pass_id, stream)
+    torch.cuda.synchronize()
+    print(json.dumps({"fork_rollouts": N, "calls_per_pass": reps + 1,
+                      "flops_per_call": [fv.attention_flops(0), fv.attention_flops(1)]}), flush=True)
 
 
 def pmc_pass(dec):
