@@ -826,51 +826,62 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
 }
 
 // Merge the slots of every output row: out = sum_s w_s o_s / sum_s w_s l_s,
-// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  D / 4
-// lanes per row take 4 dims each (16 bytes of float32, or 8 bytes of int16
-// scaled by the record's c for bf16 outputs), so a row's slot is one
-// contiguous read; with compact records lane k writes dims
-// 16 (k % (D / 16)) + 4 (k / (D / 16)) + 0..3 of the output.  SW groups of those lanes split the slots of a row (SW = 1
-// for many rows and few slots, 8 for few rows and many slots); each group
-// takes its slots four at a time with every load of the batch issued first,
-// rescaling its running sums when a batch raises the max, and the groups
-// merge through LDS.
+// w_s = 2^(m_s - max_s m_s); empty slots (m_s = -inf) drop out.  Each lane
+// takes VPL consecutive record positions of a row -- 4 float32 (16 bytes),
+// or 8 int16 of a compact record (16 bytes, scaled by the record's c) --
+// so a row's slot is one contiguous read.  In a compact record, position
+// jj D / 4 + 4 dt + i holds dim 16 dt + 4 jj + i, so a lane's positions
+// p .. p + 7 are the dims of two groups of four.  SW groups of the row's
+// lanes split its slots (SW = 1 for many rows and few slots, 8 for few
+// rows and many slots); each group takes its slots four at a time with
+// every load of the batch issued first, rescaling its running sums when a
+// batch raises the max, and the groups merge through LDS.
 template <typename T, int D, int SW, bool kCompact>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
-  constexpr int LPR = D / 4;            // lanes per row and slot group
-  constexpr int RPB = 256 / (LPR * SW); // rows per workgroup
+  constexpr int VPL = kCompact ? 8 : 4;   // record values per lane
+  constexpr int NV = VPL / 4;              // groups of four
+  constexpr int LPR = D / VPL;             // lanes per row and slot group
+  constexpr int RPB = 256 / (LPR * SW);    // rows per workgroup
   constexpr int B = 4;
   __shared__ float red_m[SW > 1 ? 256 : 1], red_l[SW > 1 ? 256 : 1];
-  __shared__ f32x4 red_o[SW > 1 ? 256 : 1];
+  __shared__ f32x4 red_o[NV][SW > 1 ? 256 : 1];
   const int t = threadIdx.x;
   const int sub = (t / LPR) % SW;
   const int row = blockIdx.x * RPB + t / (LPR * SW);
-  const int d0 = (t % LPR) * 4;                 // record position of this lane's 4 values
-  // the dims they hold: the position itself, or for the lane-major compact
-  // record (position jj D / 4 + 4 dt + i) dim 16 dt + 4 jj + i
-  const int dim0 = kCompact ? 16 * ((t % LPR) % (D / 16)) + 4 * ((t % LPR) / (D / 16)) : d0;
+  const int pos = (t % LPR) * VPL;          // record position of this lane's first value
+  int dim[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int q = pos + 4 * v;
+    dim[v] = kCompact ? 16 * ((q % (D / 4)) / 4) + 4 * (q / (D / 4)) : q;
+  }
   const bool live = row < a.rows_total;
   float wm = kNegInf, wl = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = sub; live && s0 < a.n_slots; s0 += B * SW) {
     float2 ml[B];
-    f32x4 ov[B];
+    f32x4 ov[B][NV];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const int s = s0 + u * SW;
       ml[u] = float2{kNegInf, 0.f};
-      ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NV; ++v) ov[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < a.n_slots) {
         const long long prow = (long long)s * a.rows_total + row;
         if constexpr (kCompact) {
           const f32x4 r = static_cast<const f32x4*>(a.ws_ml)[prow];
-          const u32x2 h = *reinterpret_cast<const u32x2*>(static_cast<const int16_t*>(a.ws_o) + prow * D + d0);
+          const u32x4 h = *reinterpret_cast<const u32x4*>(static_cast<const int16_t*>(a.ws_o) + prow * D + pos);
           ml[u] = float2{r[0], r[1]};
-          ov[u] = f32x4{(float)(int16_t)(h[0] & 0xffffu), (float)(int16_t)(h[0] >> 16),
-                        (float)(int16_t)(h[1] & 0xffffu), (float)(int16_t)(h[1] >> 16)} * r[2];
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            ov[u][v] = f32x4{(float)(int16_t)(h[2 * v] & 0xffffu), (float)(int16_t)(h[2 * v] >> 16),
+                             (float)(int16_t)(h[2 * v + 1] & 0xffffu), (float)(int16_t)(h[2 * v + 1] >> 16)} * r[2];
         } else {
           ml[u] = static_cast<const float2*>(a.ws_ml)[prow];
-          ov[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + prow * D + d0);
+          ov[u][0] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws_o) + prow * D + pos);
         }
       }
     }
@@ -881,51 +892,59 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
     if (nm == kNegInf) continue;
     const float sc = __builtin_amdgcn_exp2f(wm - nm);
     wl *= sc;
-    acc *= sc;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] *= sc;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const float w = ml[u].x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - nm);
       wl += w * ml[u].y;
-      acc += w * ov[u];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] += w * ov[u][v];
     }
     wm = nm;
   }
   if constexpr (SW > 1) {
     red_m[t] = wm;
     red_l[t] = wl;
-    red_o[t] = acc;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) red_o[v][t] = acc[v];
     __syncthreads();
     if (sub != 0 || !live) return;
     float M = kNegInf;
 #pragma unroll
     for (int g = 0; g < SW; ++g) M = fmaxf(M, red_m[t + g * LPR]);
     wl = 0.f;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != kNegInf) {
 #pragma unroll
       for (int g = 0; g < SW; ++g) {
         const float mg = red_m[t + g * LPR];
         const float f = mg == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mg - M);
         wl += f * red_l[t + g * LPR];
-        acc += f * red_o[t + g * LPR];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += f * red_o[v][t + g * LPR];
       }
     }
   } else {
     if (!live) return;
   }
   const float inv = wl > 0.f ? 1.f / wl : 0.f;
-  acc *= inv;
-  T* out = static_cast<T*>(a.out) + (long long)row * D + dim0;
-  if constexpr (sizeof(T) == 2) {
-    uint16_t h[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const __bf16 b = (__bf16)acc[e];
-      h[e] = __builtin_bit_cast(uint16_t, b);
+  for (int v = 0; v < NV; ++v) {
+    const f32x4 x = acc[v] * inv;
+    T* out = static_cast<T*>(a.out) + (long long)row * D + dim[v];
+    if constexpr (sizeof(T) == 2) {
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 b = (__bf16)x[e];
+        h[e] = __builtin_bit_cast(uint16_t, b);
+      }
+      *reinterpret_cast<uint2*>(out) = uint2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+    } else {
+      *reinterpret_cast<f32x4*>(out) = x;
     }
-    *reinterpret_cast<uint2*>(out) = uint2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
-  } else {
-    *reinterpret_cast<f32x4*>(out) = acc;
   }
 }
 
@@ -949,12 +968,15 @@ hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int SW>
 hipError_t launch_combine_sw(const AttnArgs& a, hipStream_t stream) {
-  constexpr int rows_per_block = 256 / (D / 4 * SW);
-  const dim3 grid((a.rows_total + rows_per_block - 1) / rows_per_block);
-  if (sizeof(T) == 2 && a.compact)
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, sizeof(T) == 2>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, false>), grid, dim3(256), 0, stream, a);
+  if (sizeof(T) == 2 && a.compact) {
+    constexpr int rows_per_block = 256 / (D / 8 * SW);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, sizeof(T) == 2>),
+                       dim3((a.rows_total + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream, a);
+  } else {
+    constexpr int rows_per_block = 256 / (D / 4 * SW);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, false>),
+                       dim3((a.rows_total + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
