@@ -302,11 +302,12 @@ __device__ inline void write_partial_f32(const AttnArgs& a, int slot, const bool
 
 // this item's compact partial (bf16 inputs): the unnormalised output of a
 // row is stored as int16 against one power of two per (slot, row),
-//   h_d = rint(o_d 2^(14 - e)),  2^(e - 1) <= max_d |o_d| < 2^e,
-// so |h_d| < 2^14 and o_d = c h_d with c = 2^(e - 14), to within
-// c / 2 <= 2^-14 max_d |o_d|.  After the merge the error is at most 2^-14
-// of the largest |V| element the row attends to, far below the bf16
-// rounding of the output; the bytes per row and slot drop from 520 to 272.
+//   h_d = round(32767 o_d 2^-e),  2^(e - 1) <= max_d |o_d| < 2^e,
+// (v_cvt_pknorm_i16_f32: two values per instruction, rounded to nearest),
+// so o_d = c h_d with c = 2^e / 32767, to within c / 2 <= 2^-15 max_d |o_d|.
+// After the merge the error is at most 2^-15 of the largest |V| element
+// the row attends to, far below the bf16 rounding of the output; the bytes
+// per row and slot drop from 520 to 272.
 // Every lane already holds its column's full sum in l_run.  A row's D
 // values sit in the four lanes n, n + 16, n + 32, n + 48: lane group jj
 // holds dims 16 dt + 4 jj + i.  The record is laid out lane-major,
@@ -327,17 +328,18 @@ __device__ inline void write_partial_q16(const AttnArgs& a, int slot, const bool
       for (int i = 0; i < 4; ++i) mo = fmaxf(mo, fabsf(o[c][dt][i]));
     mo = group4_max(mo);
     const int e = mo > 0.f ? __builtin_amdgcn_frexp_expf(mo) : 0;
-    const float up = __builtin_amdgcn_ldexpf(1.f, 14 - e);
+    const float up = __builtin_amdgcn_ldexpf(1.f, -e);   // |o_d 2^-e| < 1
     if (!valid[c]) continue;
     const long long prow = (long long)slot * a.rows_total + orow[c];
     if (jj == 0)
-      __builtin_nontemporal_store(f32x4{m_run[c], l_run[c], __builtin_amdgcn_ldexpf(1.f, e - 14), 0.f}, &ws_ml[prow]);
+      __builtin_nontemporal_store(f32x4{m_run[c], l_run[c], __builtin_amdgcn_ldexpf(1.f / 32767.f, e), 0.f},
+                                  &ws_ml[prow]);
     u32x4 h[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const f32x4 x = o[c][dt] * up;
-      const auto lo = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(x[0]), (int)__builtin_rintf(x[1]));
-      const auto hi = __builtin_amdgcn_cvt_pk_i16((int)__builtin_rintf(x[2]), (int)__builtin_rintf(x[3]));
+      const auto lo = __builtin_amdgcn_cvt_pknorm_i16(x[0], x[1]);
+      const auto hi = __builtin_amdgcn_cvt_pknorm_i16(x[2], x[3]);
       h[dt >> 1][2 * (dt & 1)] = __builtin_bit_cast(uint32_t, lo);
       h[dt >> 1][2 * (dt & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
     }
