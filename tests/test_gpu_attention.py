@@ -315,3 +315,17 @@ def test_output_scales_exactly_with_power_of_two_values(R):
     assert torch.equal(outs[2.0 ** 10], outs[1.0] * 2.0 ** 10)
     assert torch.equal(outs[2.0 ** -20], outs[1.0] * 2.0 ** -20)
     assert not outs[0.0].any()
+
+
+def test_fp32_many_rows_keeps_float32_partials():
+    # 2 x 64 rows x 8 heads = 1024 output rows: bf16 inputs would take the
+    # compact partials here; float32 inputs keep float32 ones and the 1e-5 bound
+    _check(113, 2, 64, 8, 2, 64, "f32", [500, 257], [0, 30, 64], CAUSAL, cap=500)
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_fork_head_dim_64(mode):
+    # compact partials and the 8-value combine at head_dim 64: 16 rollouts x
+    # 24 rows x 8 heads per KV head
+    priv = [(13 * s) % 48 for s in range(16)]
+    _check(114, 16, 24, 16, 2, 64, "bf16", [1500], [0, 24], mode, fork=True, priv_len=priv, priv_cap=48)
