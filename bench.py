@@ -124,6 +124,22 @@ def main():
     assert int(dec.masked.sum().item()) == 0, "decode left masked rows"
     assert int((dec.tokens < 0).sum().item()) == 0
 
+    # the same decode issued call by call from the host (no graph), for the
+    # graph's gain: host marshalling and launch per call sit between kernels
+    graph_gain = None
+    if graph is not None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(3):
+                dec.run()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / 3
+        graph_gain = {"graph_ms": round(ms_per_step, 4), "eager_ms": round(eager_ms, 4),
+                      "speedup": round(eager_ms / ms_per_step, 2)}
+
     # ---- per-kernel launch duration.  The decode is issued once more
     # through the sub-step entry points, saving the masked rows each scan
     # sees; then every step's launches of one kernel are captured back to
@@ -237,6 +253,7 @@ def main():
                    "global_batch": 1, "seq_len": dec.prefix + sum(dec.blocks), "parallelism": "none (1 GPU)",
                    "mode": args.mode},
         "denoise_step_ms": round(ms_per_step / dec.denoise_steps, 5),
+        "graph_vs_eager": graph_gain,
         "attn": {"avg_us": round(attn_us, 3), "TB_s": round(attn_gbs / 1e3, 4),
                  "TFLOP_s": round(attn_tflops, 3), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 5),
