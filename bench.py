@@ -505,7 +505,18 @@ def legs(stream):
     out["large_block_b16_attn"] = {"attn_us": round(us, 3), "TB_s": round(nbytes / us / 1e6, 3),
                                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                    "TFLOP_s": round(flops / us / 1e6, 1), "bytes": nbytes}
-    del pk, pv, cache, ws
+    # the same call for the first sequence alone (batch 1)
+    cache1 = B.KVCache(cache.k[:1].contiguous(), cache.v[:1].contiguous())
+    q1, k1, v1, o1 = q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), o[:1].contiguous()
+    ws1 = torch.zeros(B.bc_attn_workspace_bytes(cache1, None, (1, R, Hq, D), [0, R]), dtype=torch.uint8,
+                      device="cuda:0")
+    us1 = graph_us(lambda: B.bc_attn_step(cache1, lens[:1], None, None, q1, k1, v1, [0, R], B.BC_MASK_BLOCK_BIDIR,
+                                          D ** -0.5, o1, ws1, stream=stream), stream)
+    nb1, fl1 = attn_bytes_flops(lens[0], R, Hq, Hkv, D)
+    out["large_block_b1_attn"] = {"attn_us": round(us1, 3), "TB_s": round(nb1 / us1 / 1e6, 4),
+                                  "hbm_frac": round(nb1 / us1 / 1e3 / HBM_PEAK_GBS, 4),
+                                  "TFLOP_s": round(fl1 / us1 / 1e6, 1), "bytes": nb1}
+    del pk, pv, cache, ws, cache1, ws1
     # the section decode with the sections' scaffold rows inside the blocks
     # (404 rows, 280 editable), block and section visibility, each decode
     # replayed whole as one graph like the headline
