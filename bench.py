@@ -63,8 +63,7 @@ def attn_bytes_flops(prefix_len, R, Hq, Hkv, D, elem=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md, "
-              "'How the path would shard').", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     from block_causal_attention_gqa_amd import binding as B
