@@ -318,3 +318,13 @@ def test_one_past_each_limit_is_unsupported():
     # the limits themselves are accepted
     assert status(B.BC_MAX_BLOCK_ROWS, [0, B.BC_MAX_BLOCK_ROWS]) == B.BC_OK
     assert status(B.BC_MAX_BLOCKS, list(range(B.BC_MAX_BLOCKS + 1))) == B.BC_OK
+
+
+def test_vocabulary_past_one_merge_round():
+    # more than 64 chunks of 4096 logits: the decide merges each row's chunk
+    # partials in two rounds of loads
+    V = 64 * 4096 + 4097
+    x = synth.logits(93, 6, V, 4.0, 0)
+    synth.plant_peaks(x, 93, 0.5, 14.0, 0)
+    x[2, V - 1] = 40.0          # argmax in the last chunk
+    compare(x, [0, 3, 6], [FULL, SEMI], [2, 1], 0.9, np.ones(6, np.uint8), np.zeros(6, np.int32))

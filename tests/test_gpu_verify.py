@@ -159,3 +159,15 @@ def test_one_past_the_scan_row_limit_is_unsupported():
     ws = torch.zeros(B.bc_verify_workspace_bytes(64, L, V), dtype=torch.uint8, device=G.DEV)
     assert B.bc_verify_workspace_bytes(S, L, V) == 0
     assert B.bc_spec_verify(lg, d, None, f, a, a.clone(), ws, check=False) == B.BC_ERR_UNSUPPORTED
+
+
+def test_vocabulary_past_one_merge_round():
+    # more than 64 chunks of 4096 logits: two merge rounds per row; four
+    # correct drafts over five rows, so the bonus is row 4's argmax, planted
+    # in the last chunk
+    V = 64 * 4096 + 4097
+    lg, _ = synth.argmax_planted_logits(13, 5, V, 4.0, 0.5, 0)
+    lg[4, V - 2] = lg[4].max() + 1.0
+    t = lg.argmax(axis=1).astype(np.int32)
+    ga, gb = compare(lg[None], t[None, :4].copy(), None, [0])
+    assert ga[0] == 4 and gb[0] == V - 2
