@@ -151,3 +151,18 @@ def test_verify_validation(L):
     assert call(ws=0) == B.BC_ERR_WORKSPACE
     assert call(wsb=100) == B.BC_ERR_WORKSPACE
     assert call(S=200, Lr=24, m=24) == B.BC_ERR_UNSUPPORTED   # 4800 rows > BC_MAX_SCAN_ROWS
+
+
+def test_partial_record_sizes_follow_the_row_count(L):
+    # with an explicit split count P the workspace holds (P + 1) records per
+    # output row: 520 bytes (float32) below 1024 output rows or for float32
+    # inputs, 272 bytes (compact int16) from 1024 rows with bf16 inputs
+    def nbytes(dtype, R, Hq=16):
+        act, keep = _active(R=R, Hq=Hq, off=(0, R))
+        return L.bc_attn_workspace_bytes(ctypes.byref(_cache(dtype=dtype, cap=512)), None, ctypes.byref(act), 2)
+
+    def rounded(n):
+        return (n + 255) // 256 * 256
+    for dtype, R, per_row in ((B.BC_BF16, 32, (512, 8)), (B.BC_BF16, 64, (256, 16)), (B.BC_F32, 64, (512, 8))):
+        rows = R * 16
+        assert nbytes(dtype, R) == rounded(3 * rows * per_row[0]) + rounded(3 * rows * per_row[1]), (dtype, R)
