@@ -78,10 +78,16 @@ int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_a
 // 64-key tile with one workgroup per CU and ~2.5 us with two (512
 // co-resident), ~2 us of fixed cost per item (Q load, first tile, partial
 // write), K/V and partial slots streamed at ~5 TB/s.
-int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, double slot_row_bytes) {
+int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, double slot_row_bytes, bool wide) {
   constexpr int kCUs = 256, kSlotsResident = 512;
   constexpr double kTileUs1 = 1.9, kTileUs2 = 2.5, kItemUs = 2.0, kBytesPerUs = 5.0e6;
-  const double slot_us = (double)rows_total * slot_row_bytes * 2.0 / kBytesPerUs;
+  // Slot traffic of two-column-tile calls (many rows, long items) is priced
+  // at an effective ~2 TB/s, fitted to forced split sweeps: the fork at
+  // N = 16 was 28.4-29.1 us at P = 6 against 30.5-32 us at P = 9 (this
+  // model picks 5: 29.2-30.1 us), the large-block batch 16 best at P = 2.
+  // One-column-tile calls (bs1) are launch-bound and keep 5 TB/s, where
+  // P ~ 25 is the measured optimum.
+  const double slot_us = (double)rows_total * slot_row_bytes * 2.0 / (wide ? 2.0e6 : kBytesPerUs);
   const double floor_us = kv_bytes / kBytesPerUs + kItemUs;
   const int most = std::max(1, std::min(256, (maxlen + kAttnKeyTile - 1) / kAttnKeyTile));
   int best = 1;
@@ -134,7 +140,7 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
     // K/V bytes of the prefix as streamed from HBM (a shared fork prefix once)
     double kv = 0;
     for (int s = 0; s < prefix->n_seq; ++s) kv += (double)lengths[s] * Hkv * D * 2.0 * elem_bytes(prefix->dtype);
-    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes);
+    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes, p->cols == 2);
   }
   p->P = P;
   for (int s = 0; s < prefix->n_seq; ++s) {
