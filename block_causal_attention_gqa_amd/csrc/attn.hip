@@ -310,9 +310,10 @@ __device__ inline void write_partial_f32(const AttnArgs& a, int slot, const bool
 // per row and slot drop from 520 to 272.
 // Every lane already holds its column's full sum in l_run.  A row's D
 // values sit in the four lanes n, n + 16, n + 32, n + 48: lane group jj
-// holds dims 16 dt + 4 jj + i.  The record is laid out lane-major,
-// position jj D / 4 + 4 dt + i, so each lane writes D / 2 contiguous bytes
-// with 16-byte stores.
+// holds dims 16 dt + 4 jj + i.  Store k of a lane writes its values of
+// dt = 2k and 2k + 1 (16 bytes) at record position 32 k + 8 jj, so the four
+// lanes of a row fill 64 contiguous bytes per store instruction: position
+// 32 k + 8 jj + 4 (dt & 1) + i holds dim 16 dt + 4 jj + i.
 template <int D, int CT>
 __device__ inline void write_partial_q16(const AttnArgs& a, int slot, const bool (&valid)[CT], const int (&orow)[CT],
                                          const float (&m_run)[CT], const float (&l_run)[CT],
@@ -345,7 +346,7 @@ __device__ inline void write_partial_q16(const AttnArgs& a, int slot, const bool
     }
 #pragma unroll
     for (int k = 0; k < D / 32; ++k)
-      __builtin_nontemporal_store(h[k], reinterpret_cast<u32x4*>(&ws_o[prow * D + jj * (D / 4) + 8 * k]));
+      __builtin_nontemporal_store(h[k], reinterpret_cast<u32x4*>(&ws_o[prow * D + 32 * k + 8 * jj]));
   }
 }
 
@@ -832,8 +833,8 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
 // takes VPL consecutive record positions of a row -- 4 float32 (16 bytes),
 // or 8 int16 of a compact record (16 bytes, scaled by the record's c) --
 // so a row's slot is one contiguous read.  In a compact record, position
-// jj D / 4 + 4 dt + i holds dim 16 dt + 4 jj + i, so a lane's positions
-// p .. p + 7 are the dims of two groups of four.  SW groups of the row's
+// 32 k + 8 jj + 4 e + i holds dim 16 (2 k + e) + 4 jj + i, so a lane's
+// positions p .. p + 7 are the dims of two groups of four.  SW groups of the row's
 // lanes split its slots (SW = 1 for many rows and few slots, 8 for few
 // rows and many slots); each group takes its slots four at a time with
 // every load of the batch issued first, rescaling its running sums when a
@@ -855,7 +856,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int q = pos + 4 * v;
-    dim[v] = kCompact ? 16 * ((q % (D / 4)) / 4) + 4 * (q / (D / 4)) : q;
+    dim[v] = kCompact ? 32 * (q / 32) + 16 * ((q % 8) / 4) + 4 * ((q % 32) / 8) : q;
   }
   const bool live = row < a.rows_total;
   float wm = kNegInf, wl = 0.f;

@@ -27,7 +27,7 @@ struct AttnArgs {
   // Split partials, [n_slots][rows_total] records of the unnormalised
   // output o (D values), the running max m (log2 units) and the sum l:
   //   float32:  ws_o float [..][D] = o, ws_ml float2 {m, l};
-  //   compact:  ws_o int16 [..][D] = h (lane-major order), ws_ml float4
+  //   compact:  ws_o int16 [..][D] = h (the writer's store order), ws_ml float4
   //             {m, l, c, 0}, with o = c h (c a power of two per record).
   void* ws_o;
   void* ws_ml;
