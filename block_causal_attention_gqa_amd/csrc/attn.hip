@@ -427,17 +427,22 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   int orow[CT], lim[CT];
   lane_rows<CT>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
 
-  // ---- Q^T operand, resident for the whole item
+  // ---- Q^T operand, resident for the whole item.  The two-column-tile
+  // form loads it into registers here; the one-column-tile form stages it
+  // through LDS in the prologue (below), so that the first score pass waits
+  // for Q and K(0) only.
   const bf16_t* q = static_cast<const bf16_t*>(a.q);
   constexpr int QK = D / 32;
   bf16x8 qop[CT][QK];
+  if constexpr (CT > 1) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int kk = 0; kk < QK; ++kk) {
-      const bf16x8 z = {};
-      qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
-    }
+      for (int kk = 0; kk < QK; ++kk) {
+        const bf16x8 z = {};
+        qop[c][kk] = valid[c] ? *reinterpret_cast<const bf16x8*>(q + (long long)orow[c] * D + 32 * kk + 8 * jj) : z;
+      }
+  }
 
   // osum: the row sums, accumulated by the matrix core next to o (an
   // all-ones A operand), so that the normaliser sums exactly the bf16
@@ -676,15 +681,54 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   using S1 = std::integral_constant<int, 1>;
   using More = std::false_type;
   using Last = std::true_type;
+  // One-column-tile form: the Q tile (kTileRows rows of RB bytes, the size
+  // of one stage) goes into V(1)'s stage, which iteration 0 refills only
+  // after the barrier that follows the first score pass.  Each wave loads
+  // its own 16 rows; the row a load lane needs is the output row that
+  // lane_rows gave lane (its row within the wave), fetched with a shuffle.
+  // Tile row t lands at t RB with 16-byte chunk c at position c ^ (t mod
+  // CPR), so the 16 lanes reading one chunk of 16 consecutive rows hit
+  // distinct banks.  Rows past the item's rows load the wave's first row
+  // (real data in unused columns); a wave without rows loads zeros.
+  auto load_q = [&](const uint8_t* stage) __attribute__((always_inline)) {
+    const int mine = valid[0] ? orow[0] : -1;
+    const int base = __builtin_amdgcn_readfirstlane(mine);
+    const u32x4 rsrc = raw_buffer(q + (long long)max(base, 0) * D, base >= 0 ? 0x7ffffff0 : 0);
+    const uint32_t dst = lds_offset(stage) + wave * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int src = i * RPL + lane / CPR, pos = lane % CPR;   // row within the wave
+      const int ro = __shfl(mine, src, 64);
+      const uint32_t off = (uint32_t)((ro >= 0 ? ro - base : 0) * RB + (pos ^ (src % CPR)) * 16);
+      buffer_load_lds16(rsrc, dst + i * 1024, off);
+    }
+  };
+
   f32x4 sa[CT][4], sb[CT][4];
   if (nt > 0) {
+    if constexpr (CT == 1) load_q(v_st1);
     load(0, false, k_st0);
     load(0, true, v_st0);
     if (nt > 1) load(1, false, k_st1);
   }
-  tile_barrier();
+  if constexpr (CT == 1) {
+    // Q and K(0) have landed once no more than the loads issued after K(0)
+    // (V(0), and K(1) when there is a second tile) are outstanding
+    if (nt > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+    const BC_LDS uint8_t* qs = (const BC_LDS uint8_t*)v_st1;
+    const int t = wave * kWaveRows + n;
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk)
+      qop[0][kk] = *(const BC_LDS bf16x8*)(qs + t * RB + ((4 * kk + jj) ^ (t % CPR)) * 16);
+  } else {
+    tile_barrier();
+  }
   if (nt > 0) scores(k_st0, sa);
-  if (nt > 2) tile_barrier();   // every wave has read K(0) before iteration 0 refills its stage
+  // every wave has read K(0) (and, one-column-tile form, the Q tile) before
+  // iteration 0 refills those stages; V(0) and K(1) have landed
+  if (CT == 1 ? nt > 0 : nt > 2) tile_barrier();
   if constexpr (CT == 1) {
     // few rows, short items: the last iteration gets its own form
     int j = 0;
