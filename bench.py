@@ -550,12 +550,13 @@ def legs(stream):
                      "max_active": max(len(st["active"]) for st in pd.trace)}
         del pd
     out["pipelined_625"] = pip
-    # latency floors: a one-element fill kernel, and a copy of 256 floats
-    # (one load and one store per lane)
+    # latency floors: a one-element fill kernel, and an in-place add of 256
+    # floats (two loads and one store per lane).  An add, not a copy: a
+    # device-to-device copy is captured as a memcpy node, not a kernel.
     x = torch.zeros(1, device="cuda:0")
     out["launch_floor_us"] = round(graph_us(lambda: x.fill_(1.0), stream, reps=50), 3)
-    src, dst = torch.ones(256, device="cuda:0"), torch.empty(256, device="cuda:0")
-    out["load_floor_us"] = round(graph_us(lambda: dst.copy_(src), stream, reps=50), 3)
+    src, dst = torch.ones(256, device="cuda:0"), torch.zeros(256, device="cuda:0")
+    out["load_floor_us"] = round(graph_us(lambda: dst.add_(src), stream, reps=50), 3)
     return out
 
 
