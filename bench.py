@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--fork-pass", action="store_true",
                     help="for profiler runs: issue the N = 64 fork round's two attention calls (draft pass, "
                          "verify pass) 10 times each, print one JSON line, exit")
+    ap.add_argument("--verify-pass", action="store_true",
+                    help="for profiler runs: issue the N = 64 fork round's verify scan (greedy, then sampled "
+                         "with Gumbel noise) 10 times each and a 256 MiB device copy (the counters' "
+                         "calibration), print one JSON line, exit")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the secondary measurements (fork round, batch-16 attention, verify scan)")
     return ap.parse_args()
@@ -74,6 +78,9 @@ def main():
     dev = "cuda:0"
     if args.fork_pass:
         fork_pass()
+        return
+    if args.verify_pass:
+        verify_pass()
         return
     preset = synth.PRESETS["section"]
     t0 = time.time()
@@ -395,6 +402,33 @@ def fork_pass(N=64, reps=10):
     torch.cuda.synchronize()
     print(json.dumps({"fork_rollouts": N, "calls_per_pass": reps + 1,
                       "flops_per_call": [fv.attention_flops(0), fv.attention_flops(1)]}), flush=True)
+
+
+def verify_pass(N=64, reps=10):
+    """The fork round's verify scan at N rollouts (24 logit rows of 151936
+    per rollout), greedy and then with Gumbel noise, each issued reps times
+    after one warm call; then a 256 MiB device-to-device copy whose
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    stream = torch.cuda.Stream()
+    out = {"fork_rollouts": N, "calls": reps + 1}
+    for temperature in (None, 0.7):
+        fv = decode.ForkVerify(N, seed=0, device="cuda:0", block=0, temperature=temperature)
+        with torch.cuda.stream(stream):
+            for _ in range(reps + 1):
+                fv.verify(stream)
+        torch.cuda.synchronize()
+        out["logit_bytes" if temperature is None else "logit_and_noise_bytes"] = \
+            N * fv.R * fv.V * 4 * (1 if temperature is None else 2)
+        del fv
+        torch.cuda.empty_cache()
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    out["copy_bytes"] = src.numel() * 4
+    print(json.dumps(out), flush=True)
 
 
 def pmc_pass(dec):
