@@ -276,7 +276,7 @@ def main():
     if not args.no_legs:
         result["legs"] = legs(stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dec, args)
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(dec, args)
     print(json.dumps(result), flush=True)
 
 
@@ -613,6 +613,15 @@ def cpu_baseline(dec, args):
             inputs[(b, st)] = (q, k, v, synth.logits(seed, bs, dec.V, dec.sigma, b, st))
     n = sum(dec.blocks)
     units = [[b] for b in range(len(dec.blocks))]
+    # One untimed run with the decision trace: the decoded tokens against the
+    # GPU decode's, and how close the float64 confidences came to each
+    # decision (the GPU scans in float32 and re-takes, in float64, every
+    # decision within a relative 2^-12 of its threshold or rank cut).
+    trace = []
+    ref = OS.section_decode(k32[0], v32[0], dec.prefix, units, dec.blocks, lambda b, st: inputs[(b, st)],
+                            dec.steps, dec.tau, np.ones(n, np.uint8), np.full(n, -1, np.int32), scale=dec.scale,
+                            attend_all=False, trace=trace)
+    check = oracle_check(ref, trace, dec)
     tokens, reps = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -629,7 +638,41 @@ def cpu_baseline(dec, args):
             "sample": "%d repetitions of the whole section decode (%d tokens, %d denoise steps each) on "
                       "the same inputs; BLAS threads %d, os.cpu_count()=%s"
                       % (reps, n, dec.denoise_steps, threads, os.cpu_count()),
-            "seconds": round(secs, 2)}
+            "seconds": round(secs, 2)}, check
+
+
+def oracle_check(ref, trace, dec):
+    """The oracle decode's tokens against the GPU decode's, and the smallest
+    relative float64 margins of its decisions: |conf - tau| / conf over the
+    masked rows of every step, and (c_(k-1) - c_k) / c_(k-1) at every rank
+    cut (steps whose commit count is neither 0, all masked rows nor exactly
+    the rows above tau)."""
+    band = 2.0 ** -12
+    tau = float(np.float32(dec.tau))
+    thr, cut, n_cuts, inside = float("inf"), float("inf"), 0, 0
+    for _, _, conf, k in trace:
+        c = conf[~np.isnan(conf)]
+        if c.size == 0:
+            continue
+        m = float(np.min(np.abs(c - tau) / c))
+        thr = min(thr, m)
+        inside += m <= band
+        n_above = int(np.sum(c > tau))
+        if k not in (0, c.size, n_above):
+            srt = np.sort(c)[::-1]
+            g = float((srt[k - 1] - srt[k]) / srt[k - 1])
+            cut = min(cut, g)
+            n_cuts += 1
+            inside += g <= band
+    import torch
+    dec.run()                # a fresh GPU decode: the legs above reuse its buffers
+    torch.cuda.synchronize()
+    gpu_tokens = dec.tokens.cpu().numpy()
+    return {"tokens_match": bool(np.array_equal(gpu_tokens, ref["tokens"])),
+            "masked_match": bool(np.array_equal(dec.masked.cpu().numpy(), ref["masked"])),
+            "steps": len(trace), "rank_cuts": n_cuts,
+            "min_threshold_margin_rel": thr, "min_rank_cut_gap_rel": cut if n_cuts else None,
+            "band_rel": band, "decisions_inside_band": inside}
 
 
 if __name__ == "__main__":

@@ -37,7 +37,7 @@ from . import attention as OA, kvcache as OK, unmask as OU
 
 
 def section_decode(prefix_k, prefix_v, prefix_len, units, blocks, inputs, steps, tau, masked0, tokens0,
-                   scale=None, keep=(), attend_all=True):
+                   scale=None, keep=(), attend_all=True, trace=None):
     """Decode one sequence.
 
     prefix_k/v [Hkv][>= prefix_len][D]; ``units`` lists the block indices of
@@ -52,7 +52,9 @@ def section_decode(prefix_k, prefix_v, prefix_len, units, blocks, inputs, steps,
     attention {(b, st): float64 [1][unit rows][Hq][D] for (b, st) in keep}).
     The synthetic logits do not depend on the attention outputs, so with
     attend_all False only the kept steps' attention is computed (same
-    results, less work).
+    results, less work).  With ``trace`` a list, every unmask step appends
+    (block, step, float64 confidences of the block's rows with NaN on rows
+    revealed before the step, commit count).
     """
     cache = OK.new_cache(np.asarray(prefix_k)[None], np.asarray(prefix_v)[None], [prefix_len])
     masked = np.array(masked0, np.uint8)
@@ -74,8 +76,10 @@ def section_decode(prefix_k, prefix_v, prefix_len, units, blocks, inputs, steps,
                                           OA.MASK_BIDIR, scale=scale)
                     if (b, st) in keep:
                         kept[(b, st)] = o
-                m, t, n, _ = OU.unmask_select(lg, [0, r1 - r0], [OU.MODE_FULL], [steps - st], np.float32(tau),
-                                              masked[r0:r1], tokens[r0:r1])
+                m, t, n, conf = OU.unmask_select(lg, [0, r1 - r0], [OU.MODE_FULL], [steps - st], np.float32(tau),
+                                                 masked[r0:r1], tokens[r0:r1])
+                if trace is not None:
+                    trace.append((b, st, conf, int(n[0])))
                 masked[r0:r1], tokens[r0:r1] = m, t
                 n_commit[b].append(int(n[0]))
         OK.commit(cache, 0, cache[0][0].shape[1], k[0], v[0])
