@@ -40,6 +40,7 @@ def _layout(preset):
     ("section_scaffold", "section", None),     # full vocabulary
     ("section_scaffold", "block", 32768),
     ("section", "section", 32768),
+    ("section", "block", None),                # the timed shapes, full vocabulary
 ])
 def test_section_decode_matches_oracle(name, visibility, vocab):
     import torch
