@@ -81,6 +81,35 @@ __device__ inline Acc merge_step(Acc x) {
   return merge(x, y);
 }
 
+// Plain butterfly over the 64 lanes of a wave on 32-bit values; `op` is
+// commutative, so every lane ends with the same bits.
+template <typename Op>
+__device__ inline uint32_t wave_allreduce(uint32_t x, Op op) {
+  x = op(x, lane_xchg<0>(x));
+  x = op(x, lane_xchg<1>(x));
+  x = op(x, lane_xchg<2>(x));
+  x = op(x, lane_xchg<3>(x));
+  x = op(x, lane_xchg<4>(x));
+  x = op(x, lane_xchg<5>(x));
+  return x;
+}
+
+__device__ inline float wave_max(float x) {
+  return __builtin_bit_cast(float, wave_allreduce(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
+    return __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, p), __builtin_bit_cast(float, q)));
+  }));
+}
+
+__device__ inline float wave_sum(float x) {
+  return __builtin_bit_cast(float, wave_allreduce(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, p) + __builtin_bit_cast(float, q));
+  }));
+}
+
+__device__ inline int wave_min(int x) {
+  return (int)wave_allreduce((uint32_t)x, [](uint32_t p, uint32_t q) { return (uint32_t)min((int)p, (int)q); });
+}
+
 // Merge over aligned groups of kWidth lanes (8 or 64); every lane of a group
 // ends with the group's result.
 template <int kWidth>
@@ -148,28 +177,49 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
       v[e] = x;
     }
   }
-  Acc acc{kNegInf, INT_MAX, 0.f};
+  // Max first: the chunk max M over the lanes (butterfly) and the waves (one
+  // LDS slot each); then every lane takes its lowest index holding M and its
+  // sum of exp(l - M), and two more butterflies finish them.  No partial
+  // result is ever rescaled, so the exponentials are the 16 per lane.
+  auto index_of = [&](int e) {
+    return kVec ? c0 + 4 * (tid + kScanThreads * (e / 4)) + (e & 3) : c0 + tid + kScanThreads * e;
+  };
+  const int w = tid >> 6;
+  float m = v[0];
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const int idx = kVec ? c0 + 4 * (tid + kScanThreads * (e / 4)) + (e & 3) : c0 + tid + kScanThreads * e;
-    if (v[e] > acc.m) { acc.m = v[e]; acc.a = idx; }
-  }
+  for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[w].m = m;
+  __syncthreads();
+  float M = red[0].m;
+#pragma unroll
+  for (int k = 1; k < kScanThreads / 64; ++k) M = fmaxf(M, red[k].m);
+  int a = INT_MAX;
+#pragma unroll
+  for (int e = NV - 1; e >= 0; --e) a = v[e] == M ? index_of(e) : a;   // indices rise with e
+  a = wave_min(a);
+  float sum = 0.f;
   if constexpr (kSum) {
-    if (acc.m != kNegInf) {
-      float s = 0.f;
+    if (M != kNegInf) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) s += __builtin_amdgcn_exp2f((v[e] - acc.m) * kLog2e);
-      acc.s = s;
+      for (int e = 0; e < NV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
     }
+    sum = wave_sum(sum);
   }
-  acc = lanes_merge<64>(acc);
-  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  if ((tid & 63) == 0) {   // other fields than the maxima the slower waves may still read
+    red[w].a = a;
+    red[w].s = sum;
+  }
   __syncthreads();
   if (tid == 0) {
-    Acc t = red[0];
+    int at = red[0].a;
+    float st = red[0].s;
 #pragma unroll
-    for (int w = 1; w < kScanThreads / 64; ++w) t = merge(t, red[w]);
-    *out = ScanPartial{t.m, t.a, t.s, 0};
+    for (int k = 1; k < kScanThreads / 64; ++k) {
+      at = min(at, red[k].a);
+      st += red[k].s;
+    }
+    *out = ScanPartial{M, at, kSum ? st : 0.f, 0};
   }
 }
 
