@@ -72,58 +72,39 @@ __device__ inline uint32_t lane_xchg(uint32_t x) {
   }
 }
 
-template <int kStep>
-__device__ inline Acc merge_step(Acc x) {
-  Acc y;
-  y.m = __builtin_bit_cast(float, lane_xchg<kStep>(__builtin_bit_cast(uint32_t, x.m)));
-  y.a = (int)lane_xchg<kStep>((uint32_t)x.a);
-  y.s = __builtin_bit_cast(float, lane_xchg<kStep>(__builtin_bit_cast(uint32_t, x.s)));
-  return merge(x, y);
-}
-
-// Plain butterfly over the 64 lanes of a wave on 32-bit values; `op` is
-// commutative, so every lane ends with the same bits.
-template <typename Op>
-__device__ inline uint32_t wave_allreduce(uint32_t x, Op op) {
+// Butterfly over aligned groups of kWidth lanes (8 or 64) on 32-bit values;
+// `op` is commutative, so every lane of a group ends with the same bits.
+template <int kWidth, typename Op>
+__device__ inline uint32_t lanes_allreduce(uint32_t x, Op op) {
+  static_assert(kWidth == 8 || kWidth == 64, "group width");
   x = op(x, lane_xchg<0>(x));
   x = op(x, lane_xchg<1>(x));
   x = op(x, lane_xchg<2>(x));
-  x = op(x, lane_xchg<3>(x));
-  x = op(x, lane_xchg<4>(x));
-  x = op(x, lane_xchg<5>(x));
+  if constexpr (kWidth == 64) {
+    x = op(x, lane_xchg<3>(x));
+    x = op(x, lane_xchg<4>(x));
+    x = op(x, lane_xchg<5>(x));
+  }
   return x;
 }
 
-__device__ inline float wave_max(float x) {
-  return __builtin_bit_cast(float, wave_allreduce(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
+template <int kWidth>
+__device__ inline float lanes_max(float x) {
+  return __builtin_bit_cast(float, lanes_allreduce<kWidth>(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
     return __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, p), __builtin_bit_cast(float, q)));
   }));
 }
 
-__device__ inline float wave_sum(float x) {
-  return __builtin_bit_cast(float, wave_allreduce(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
+template <int kWidth>
+__device__ inline float lanes_sum(float x) {
+  return __builtin_bit_cast(float, lanes_allreduce<kWidth>(__builtin_bit_cast(uint32_t, x), [](uint32_t p, uint32_t q) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, p) + __builtin_bit_cast(float, q));
   }));
 }
 
-__device__ inline int wave_min(int x) {
-  return (int)wave_allreduce((uint32_t)x, [](uint32_t p, uint32_t q) { return (uint32_t)min((int)p, (int)q); });
-}
-
-// Merge over aligned groups of kWidth lanes (8 or 64); every lane of a group
-// ends with the group's result.
 template <int kWidth>
-__device__ inline Acc lanes_merge(Acc x) {
-  static_assert(kWidth == 8 || kWidth == 64, "group width");
-  x = merge_step<0>(x);
-  x = merge_step<1>(x);
-  x = merge_step<2>(x);
-  if constexpr (kWidth == 64) {
-    x = merge_step<3>(x);
-    x = merge_step<4>(x);
-    x = merge_step<5>(x);
-  }
-  return x;
+__device__ inline int lanes_min(int x) {
+  return (int)lanes_allreduce<kWidth>((uint32_t)x, [](uint32_t p, uint32_t q) { return (uint32_t)min((int)p, (int)q); });
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -188,7 +169,7 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
   float m = v[0];
 #pragma unroll
   for (int e = 1; e < NV; ++e) m = fmaxf(m, v[e]);
-  m = wave_max(m);
+  m = lanes_max<64>(m);
   if ((tid & 63) == 0) red[w].m = m;
   __syncthreads();
   float M = red[0].m;
@@ -197,14 +178,14 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
   int a = INT_MAX;
 #pragma unroll
   for (int e = NV - 1; e >= 0; --e) a = v[e] == M ? index_of(e) : a;   // indices rise with e
-  a = wave_min(a);
+  a = lanes_min<64>(a);
   float sum = 0.f;
   if constexpr (kSum) {
     if (M != kNegInf) {
 #pragma unroll
       for (int e = 0; e < NV; ++e) sum += __builtin_amdgcn_exp2f((v[e] - M) * kLog2e);
     }
-    sum = wave_sum(sum);
+    sum = lanes_sum<64>(sum);
   }
   if ((tid & 63) == 0) {   // other fields than the maxima the slower waves may still read
     red[w].a = a;
@@ -267,11 +248,24 @@ __device__ void merge_rows(const ScanPartial* part, int n_chunks, int r0, int nr
         p[u] = ScanPartial{kNegInf, INT_MAX, 0.f, 0};
         if (use && c < n_chunks) p[u] = part[(long long)(r0 + i) * n_chunks + c];
       }
+      // max first over the lane's partials, then index and rescaled sums
+      Acc r{p[0].m, INT_MAX, 0.f};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t = merge(t, Acc{p[u].m, p[u].a, p[u].s});
+      for (int u = 1; u < 8; ++u) r.m = fmaxf(r.m, p[u].m);
+      if (r.m != kNegInf) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (p[u].m == r.m) r.a = min(r.a, p[u].a);
+          if (p[u].m != kNegInf) r.s += p[u].s * __builtin_amdgcn_exp2f((p[u].m - r.m) * kLog2e);
+        }
+      }
+      t = c0 == 0 ? r : merge(t, r);   // one round for up to 64 chunks
     }
-    t = lanes_merge<kLanes>(t);
-    if (use && sub == 0) sink(i, t);
+    // the same across the row's lanes
+    const float M = lanes_max<kLanes>(t.m);
+    const int a_row = lanes_min<kLanes>(t.m == M ? t.a : INT_MAX);
+    const float s_row = lanes_sum<kLanes>(t.m == kNegInf ? 0.f : t.s * __builtin_amdgcn_exp2f((t.m - M) * kLog2e));
+    if (use && sub == 0) sink(i, Acc{M, a_row, s_row});
   }
 }
 
