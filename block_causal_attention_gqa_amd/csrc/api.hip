@@ -281,6 +281,13 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   for (int s = 0; s < prefix->n_seq; ++s) args->prefix_len[s] = prefix_len[s];
   if (priv)
     for (int s = 0; s < a->n_seq; ++s) args->priv_len[s] = priv_len[s];
+  // every divisor is >= 1 and every dividend below 2^31 (rows < 2^26)
+  args->dv_mt_prefix = make_fastdiv(p.n_mt_prefix);
+  args->dv_splits = make_fastdiv(p.P);
+  args->dv_hkv = make_fastdiv(args->Hkv);
+  args->dv_mt_active = make_fastdiv(p.n_mt_active);
+  args->dv_rows = make_fastdiv(args->R * args->group);
+  args->dv_group = make_fastdiv(args->group);
   return BC_OK;
 }
 

@@ -150,13 +150,18 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
   it.n1 = 0;
   it.masked0 = false;
   if (item < a.n_prefix_items) {
-    it.mt = item % a.n_mt_prefix;
-    const int rest = item / a.n_mt_prefix;
-    it.slot = rest % a.n_splits;
-    const int grp = rest / a.n_splits;
+    const int rest = fast_div(item, a.dv_mt_prefix);
+    it.mt = item - rest * a.n_mt_prefix;
+    const int grp = fast_div(rest, a.dv_splits);
+    it.slot = rest - grp * a.n_splits;
     int ps;
     if (a.fork) { it.g = grp; it.s_item = -1; ps = 0; it.rows_in_group = a.S * a.R * a.group; }
-    else { it.g = grp % a.Hkv; it.s_item = grp / a.Hkv; ps = it.s_item; it.rows_in_group = a.R * a.group; }
+    else {
+      it.s_item = fast_div(grp, a.dv_hkv);
+      it.g = grp - it.s_item * a.Hkv;
+      ps = it.s_item;
+      it.rows_in_group = a.R * a.group;
+    }
     const int key_begin = it.slot * a.chunk[ps];
     const int key_end = min(a.prefix_len[ps], key_begin + a.chunk[ps]);
     const long long off = ps * a.p_seq_stride + it.g * a.p_head_stride + (long long)key_begin * a.D;
@@ -165,10 +170,10 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
     it.n0 = max(0, key_end - key_begin);
   } else {
     const int i2 = item - a.n_prefix_items;
-    it.mt = i2 % a.n_mt_active;
-    const int rest = i2 / a.n_mt_active;
-    it.g = rest % a.Hkv;
-    it.s_item = rest / a.Hkv;
+    const int rest = fast_div(i2, a.dv_mt_active);
+    it.mt = i2 - rest * a.n_mt_active;
+    it.s_item = fast_div(rest, a.dv_hkv);
+    it.g = rest - it.s_item * a.Hkv;
     it.slot = a.n_splits;
     it.rows_in_group = a.R * a.group;
     const int lv = a.fork ? a.priv_len[it.s_item] : 0;
@@ -203,8 +208,8 @@ __device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0,
     const int m = row0 + c * 16 + n;
     valid[c] = m < it.rows_in_group;
     int s = it.s_item, rem = m;
-    if (it.s_item < 0) { s = m / (a.R * a.group); rem = m - s * (a.R * a.group); }
-    const int r = rem / a.group, hh = rem - r * a.group;
+    if (it.s_item < 0) { s = fast_div(m, a.dv_rows); rem = m - s * (a.R * a.group); }
+    const int r = fast_div(rem, a.dv_group), hh = rem - r * a.group;
     orow[c] = valid[c] ? (s * a.R + r) * a.Hq + it.g * a.group + hh : 0;
     int l = r + 1;
     if (!a.causal) {

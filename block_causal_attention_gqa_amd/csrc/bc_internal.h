@@ -9,6 +9,26 @@
 
 namespace bc {
 
+// Division by a launch-invariant divisor d >= 1 with one multiply-high: for
+// 0 <= n < 2^31, n / d = (umulhi(n, mul) + n) >> shift, with shift =
+// ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1 (division by
+// invariant integers using multiplication, Granlund and Montgomery 1994).
+// The kernels split item and row indices this way instead of through the
+// long integer-division sequence, which sits before their first loads.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  return FastDiv{(uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1), s};
+}
+
+__device__ inline int fast_div(int n, FastDiv f) {
+  return (int)((__umulhi((uint32_t)n, f.mul) + (uint32_t)n) >> f.shift);
+}
+
 // ---------------------------------------------------------------- attention
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 constexpr int kCompactRows = 1024;        // bf16 calls with at least this many output rows use compact partials
@@ -50,6 +70,8 @@ struct AttnArgs {
   int prefix_len[BC_MAX_SEQ];
   int chunk[BC_MAX_SEQ];     // prefix keys per chunk (multiple of kAttnKeyTile)
   int priv_len[BC_MAX_SEQ];
+  // n_mt_prefix, n_splits, Hkv, n_mt_active, R * group and group as FastDiv
+  FastDiv dv_mt_prefix, dv_splits, dv_hkv, dv_mt_active, dv_rows, dv_group;
 };
 
 hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream);
