@@ -727,13 +727,15 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 
   f32x4 sa[CT][4], sb[CT][4];
   if (nt > 0) {
-    if constexpr (CT == 1) load_q(v_st1);
+    // K(0) first: its loads need only the item, while the Q tile's wait for
+    // the row shuffles (measured: bs1 partial 5.83 -> 5.76 us)
     load(0, false, k_st0);
+    if constexpr (CT == 1) load_q(v_st1);
     load(0, true, v_st0);
     if (nt > 1) load(1, false, k_st1);
   }
   if constexpr (CT == 1) {
-    // Q and K(0) have landed once no more than the loads issued after K(0)
+    // K(0) and Q have landed once no more than the loads issued after them
     // (V(0), and K(1) when there is a second tile) are outstanding
     if (nt > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
