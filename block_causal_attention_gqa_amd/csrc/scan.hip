@@ -419,9 +419,11 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
                "s"(a.threshold));
   const int mode_b = a.mode[b], div_b = a.n_div[b];
 
-  // The masked flags and the chunk partials of every row are read in one
-  // round: partials of revealed rows were not written by the scan and are
-  // dropped below.
+  // The masked flags go to LDS, then every row's chunk partials are merged
+  // (the flag stores wait for their loads first; holding the flags in
+  // registers across the merge to share one round of loads measured slower).
+  // Partials of revealed rows were not written by the scan and are dropped
+  // below.
   for (int i = tid; i < nb; i += kScanThreads) sm.st[i] = a.masked[r0 + i] != 0 ? kInE : 0;
   merge_rows(a.part, a.n_chunks, r0, nb, [](int) { return true; },
              [&](int i, const Acc& t) {
