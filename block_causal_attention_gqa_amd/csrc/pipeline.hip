@@ -6,10 +6,12 @@
 // active (threshold plus the ceil(remaining / n) fallback).  Before each
 // step the states move: the oldest uncommitted block is fully active; walking
 // forward while the predecessor is active, a waiting block joins as
-// semi-active once its predecessor's completion ratio reaches `add` (and
+// semi-active once its predecessor's completion ratio exceeds `add` (and
 // fewer than `window` blocks are active), and a semi-active block becomes
-// fully active once that ratio reaches `act`.  After the step the reported
-// counts are added and completed blocks are committed strictly in order.
+// fully active once that ratio exceeds `act`.  "Exceeds" is strict, as for
+// the confidence threshold: the notes use the one word for all three.
+// After the step the reported counts are added and completed blocks are
+// committed strictly in order.
 
 #include <cmath>
 #include <new>
@@ -28,8 +30,8 @@ namespace {
 
 enum : int { kWait = 0, kSemi = 1, kFull = 2 };
 
-// revealed / size, rounded once (double), so that a threshold the exact
-// ratio meets compares as met
+// revealed / size, rounded once (double): a ratio equal to a threshold
+// stays equal to it and so does not exceed it
 double ratio(const bc_pipeline& p, int b) { return (double)p.revealed[b] / (double)p.size[b]; }
 
 void transitions(bc_pipeline& p) {
@@ -40,11 +42,11 @@ void transitions(bc_pipeline& p) {
   for (int b = p.committed + 1; b < n; ++b) {
     if (p.state[b - 1] == kWait) break;   // blocks join in order
     const double r = ratio(p, b - 1);
-    if (p.state[b] == kWait && r >= p.add && n_active < p.window) {
+    if (p.state[b] == kWait && r > p.add && n_active < p.window) {
       p.state[b] = kSemi;
       ++n_active;
     }
-    if (p.state[b] == kSemi && r >= p.act) p.state[b] = kFull;
+    if (p.state[b] == kSemi && r > p.act) p.state[b] = kFull;
   }
 }
 

@@ -345,10 +345,10 @@ class PipelinedDecode:
       * the first uncommitted block is fully active;
       * the block after an active one joins as semi-active (threshold-only
         commits) once its predecessor's completion ratio -- revealed tokens /
-        block size, in double precision -- reaches ``add``, if fewer than
-        ``window`` blocks are active; it becomes fully active (threshold plus
-        at least ceil(remaining / n_div) per step) once the ratio reaches
-        ``act``;
+        block size, in double precision -- exceeds ``add`` (strictly), if
+        fewer than ``window`` blocks are active; it becomes fully active
+        (threshold plus at least ceil(remaining / n_div) per step) once the
+        ratio exceeds ``act``;
       * every step runs one attention call over the committed cache with all
         active blocks (bidirectional inside a block, causal across) and one
         unmask call with a mode per block;

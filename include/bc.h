@@ -288,9 +288,10 @@ int bc_unmask_decide(const float *logits, int32_t n_rows, int32_t vocab,
  * first uncommitted block is fully active (threshold, plus at least
  * ceil(remaining / n_div) per step), the block after an active one joins as
  * semi-active (threshold only) once its predecessor's completion ratio --
- * revealed rows / block size, compared in double precision with >= -- reaches
- * `add` and fewer than `window` blocks are active, and turns fully active
- * once that ratio reaches `act`.  Blocks are committed strictly in order,
+ * revealed rows / block size in double precision -- exceeds `add` (strictly,
+ * like the confidence threshold) and fewer than `window` blocks are active,
+ * and turns fully active once that ratio exceeds `act`.  With add = act = 1
+ * no block starts before its predecessor is committed.  Blocks are committed strictly in order,
  * right after the step that reveals their last row.
  *
  * This is the schedule's state machine only; it runs on the host and touches

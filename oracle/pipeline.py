@@ -19,11 +19,13 @@ What is scheduled (restated from the Fast-dVLA notes, key design 4, and its
 Readings where the notes are silent or their figure is garbled:
   * the first block has no predecessor and is fully active from the start;
     a committed predecessor counts as complete (ratio 1);
-  * thresholds compare with >= on the ratio, computed as
-    revealed / size in double precision; the add and activation
-    thresholds, the confidence threshold and n are parameters (the notes
-    give 0.5 as one model's semi-active confidence threshold and no value for
-    the others);
+  * the notes use one word, "exceeds", for the add threshold, the
+    activation threshold and the confidence threshold, so all three compare
+    strictly (``exceeds``); the ratio is revealed / size in double
+    precision; the add and activation thresholds, the confidence threshold
+    and n are parameters (the notes give 0.5 as one model's semi-active
+    confidence threshold and no value for the others).  With add = act = 1 a
+    block never joins before its predecessor is committed (no overlap);
   * at most `window` blocks are active at once; blocks join in order;
   * transitions are evaluated before each step from the ratios the previous
     steps left; a block that has revealed every token stays in the active set
@@ -41,6 +43,12 @@ import numpy as np
 from . import unmask as OU
 
 WAIT, SEMI, FULL = "wait", "semi", "full"
+
+
+def exceeds(ratio, threshold):
+    """A completion ratio passes a threshold only when it is strictly
+    above it (the notes' "exceeds")."""
+    return ratio > threshold
 
 
 def pipelined_decode(block_sizes, logits_for, add, act, tau, n_div, window):
@@ -61,8 +69,8 @@ def pipelined_decode(block_sizes, logits_for, add, act, tau, n_div, window):
     def ratio(b):
         if b < committed:
             return 1.0
-        # the exact ratio, rounded once, so that a threshold it meets exactly
-        # compares as met
+        # revealed / size rounded once: a ratio equal to a threshold stays
+        # equal, so it does not exceed it
         return (block_sizes[b] - int(masked[b].sum())) / block_sizes[b]
 
     while committed < nb:
@@ -76,9 +84,9 @@ def pipelined_decode(block_sizes, logits_for, add, act, tau, n_div, window):
             r = ratio(b - 1)
             if state[b] == WAIT:
                 n_active = sum(1 for x in range(committed, nb) if state[x] != WAIT)
-                if r >= add and n_active < window:
+                if exceeds(r, add) and n_active < window:
                     state[b] = SEMI
-            if state[b] == SEMI and r >= act:
+            if state[b] == SEMI and exceeds(r, act):
                 state[b] = FULL
         active = [b for b in range(committed, nb) if state[b] != WAIT]
 

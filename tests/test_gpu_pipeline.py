@@ -38,7 +38,7 @@ def _qkv32(b, s):
     (0.5, 0.9, 0.5, 4, 3),     # three blocks in flight, semi phase
     (0.25, 0.5, 0.5, 8, 3),    # early joins, slow full blocks
     (1.0, 1.0, 0.5, 4, 3),     # no overlap: plain block-by-block decoding
-    (0.0, 0.0, 0.9, 2, 2),     # successor always full at once, window 2
+    (0.0, 0.0, 0.9, 2, 2),     # successor full once its predecessor reveals a row, window 2
 ])
 def test_pipelined_625_matches_oracle(add, act, tau, n_div, window):
     import torch

@@ -71,6 +71,16 @@ def test_native_schedule_matches_oracle(sizes, add, act, n_div, window):
         assert np.array_equal(a, b)
 
 
+def test_native_schedule_hand_worked():
+    # the schedule worked out by hand from the rule (ratios equal to add and
+    # to act, a join capped by the window), planned by the native state
+    # machine
+    from tests.test_oracle_pipeline import (HAND_ACT, HAND_ADD, HAND_N, HAND_SIZES, HAND_TAU, HAND_TRACE,
+                                            HAND_WINDOW, hand_logits)
+    _, trace = _drive(HAND_SIZES, hand_logits, HAND_ADD, HAND_ACT, HAND_TAU, HAND_N, HAND_WINDOW)
+    assert trace == HAND_TRACE
+
+
 def test_argument_and_order_errors():
     with pytest.raises(B.BcError):
         B.Pipeline([4, 0, 3], 3, 0.5, 0.9, 4)          # empty block
