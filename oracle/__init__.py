@@ -19,6 +19,9 @@ Modules
              blocks, add and activation thresholds, in-order commit)
   section    the Section Diffusion decode schedule (block or section
              visibility units, scaffold rows never masked, fixed steps)
+  trajectory the shared-prefix fork decoding a whole trajectory section with
+             scaffold speculative rounds (draft, verify, bonus, finished
+             rollouts leaving, private commits)
 
 Sources (the pages the method is described on):
   * "Fast-dDrive" (Chinese translation of arXiv 2605.23163): abstract, sec. 1

@@ -1,15 +1,18 @@
-"""Captured HIP graphs of whole decodes replay exactly what the eager calls
-compute.  The bench times the section decode as one captured graph, so every
-launch's arguments (cache lengths, block offsets, workspace) must be baked in
-correctly and nothing may depend on state that only the eager run sets up.
-Each replay follows eager work that scrambles the outputs, the cache rows the
-decode commits and the workspaces, with synchronisations in between, and must
-match the eager result bit for bit."""
+"""Captured HIP graphs of whole decodes against the float64 oracle and
+against the eager calls.  The bench times the section decode as one captured
+graph, so every launch's arguments (cache lengths, block offsets, workspace)
+must be baked in correctly and nothing may depend on state that only the
+eager run sets up.  Each replay follows eager work that scrambles the
+outputs, the cache rows the decode commits and the workspaces, with
+synchronisations in between; every replay's tokens, masks and committed cache
+must equal the oracle's section decode on the same seeded inputs (the bench's
+own workload among them, full vocabulary) and the eager run bit for bit."""
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import section as OS
 from tests import gpu_util as G
 from block_causal_attention_gqa_amd import decode, synth
 
@@ -34,16 +37,50 @@ def _capture(fn, stream):
     return g
 
 
-def test_section_decode_graph_replays_match_eager():
-    p = dict(synth.PRESETS["section"], vocab=32768)
-    print("graph: section decode, %d blocks, vocab %d" % (len(p["blocks"]), p["vocab"]), flush=True)
-    dec = decode.SectionDecode(p, seed=5, device=G.DEV)
+def oracle_section(p, seed, planted_frac=0.0):
+    """The oracle's block-visibility section decode of one sequence on the
+    inputs SectionDecode(p, seed, planted_frac=...) draws (attention outputs
+    are not needed: the synthetic logits do not depend on them)."""
+    blocks = list(p["blocks"])
+    n = sum(blocks)
+    Hq, Hkv, D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
+
+    def inputs(b, st):
+        (_, q), (_, k), (_, v) = synth.active_qkv(seed, 1, blocks[b], Hq, Hkv, D, p["dtype"], b, st)
+        lg = synth.logits(seed, blocks[b], p["vocab"], p["sigma"], b, st)
+        if planted_frac:
+            synth.plant_peaks(lg, seed, planted_frac, 12.0, b, st)
+        return q, k, v, lg
+
+    _, (pk, pv) = synth.kv_cache(seed, 1, Hkv, p["prefix"] + n, D, [p["prefix"]], p["dtype"])
+    return OS.section_decode(pk[0], pv[0], p["prefix"], [[b] for b in range(len(blocks))], blocks, inputs,
+                             p["steps"], p["threshold"], np.ones(n, np.uint8), np.full(n, -1, np.int32),
+                             scale=D ** -0.5, attend_all=False)
+
+
+def _check_oracle(dec, want, what):
+    assert np.array_equal(dec.tokens.cpu().numpy(), want["tokens"]), "%s: tokens differ from the oracle" % what
+    assert np.array_equal(dec.masked.cpu().numpy(), want["masked"]), "%s: masks differ from the oracle" % what
+    assert np.array_equal(dec.cache.k[0].float().cpu().numpy(), want["cache_k"]), "%s: cache k" % what
+    assert np.array_equal(dec.cache.v[0].float().cpu().numpy(), want["cache_v"]), "%s: cache v" % what
+
+
+@pytest.mark.parametrize("seed,vocab,planted", [(5, 32768, 0.2), (0, None, 0.0)])
+def test_section_decode_graph_replays_match_oracle_and_eager(seed, vocab, planted):
+    # (0, full vocabulary, no planted rows) is the bench's own workload
+    p = dict(synth.PRESETS["section"])
+    if vocab:
+        p["vocab"] = vocab
+    print("graph: section decode, %d blocks, vocab %d, seed %d" % (len(p["blocks"]), p["vocab"], seed), flush=True)
+    want_oracle = oracle_section(p, seed, planted)
+    dec = decode.SectionDecode(p, seed=seed, device=G.DEV, planted_frac=planted)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         dec.run()
     torch.cuda.synchronize()
     want = [t.clone() for t in (dec.tokens, dec.masked, dec.cache.k, dec.cache.v)]
     assert not want[1].any()
+    _check_oracle(dec, want_oracle, "eager decode")
     g = _capture(dec.run, stream)
     len0 = int(dec.len0[0])
     gen = torch.Generator(device=G.DEV).manual_seed(0)
@@ -59,6 +96,7 @@ def test_section_decode_graph_replays_match_eager():
         with torch.cuda.stream(stream):
             g.replay()
         torch.cuda.synchronize()
+        _check_oracle(dec, want_oracle, "replay %d" % i)
         got = (dec.tokens, dec.masked, dec.cache.k, dec.cache.v)
         for name, a, b in zip(("tokens", "masked", "cache k", "cache v"), got, want):
             assert torch.equal(a, b), "replay %d: %s differs from the eager decode" % (i, name)
