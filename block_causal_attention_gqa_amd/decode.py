@@ -54,10 +54,16 @@ class SectionDecode:
     ranks or changes them.
 
     Also the large-block decode at batch > 1 (one attention call covers
-    every sequence; the unmask call sees one block per sequence)."""
+    every sequence; the unmask call sees one block per sequence).
+
+    ``mask`` is the in-block mode of the attention calls (bidirectional by
+    default; causal gives the AR form of the same schedule).  With
+    ``logits_pool`` / ``qkv_pool`` = k, k distinct seeded logits / Q-K-V sets
+    are drawn and cycled over the (block, step) pairs instead of one per
+    pair, which bounds the host time and memory of long, wide decodes."""
 
     def __init__(self, preset, seed=0, n_seq=None, device="cuda:0", logits_pool=None,
-                 planted_frac=0.0, planted_delta=12.0, visibility="block"):
+                 planted_frac=0.0, planted_delta=12.0, visibility="block", mask=None, qkv_pool=None):
         p = dict(preset)
         self.p = p
         self.S = n_seq or p.get("n_seq", 1)
@@ -100,13 +106,19 @@ class SectionDecode:
         # the block's logits, resident on the device; with logits_pool = k,
         # k distinct logits tensors are cycled instead
         bmax = max(self.blocks)
+        self.mask = B.BC_MASK_BLOCK_BIDIR if mask is None else mask
+        self.qkv_pool = qkv_pool
+        drawn = {}
         self.qkv = []
         for b, bs in enumerate(self.blocks):
             ur = self.unit_rows[self.unit_of[b]]
             row = []
             for st in range(self.steps):
-                (qt, _), (kt, _), (vt, _) = synth.active_qkv(seed, S, ur, self.Hq, Hkv, D, self.dtype, b, st)
-                row.append((qt.to(device), kt.to(device), vt.to(device)))
+                key = self.qkv_index(b, st)
+                if key not in drawn:
+                    (qt, _), (kt, _), (vt, _) = synth.active_qkv(seed, S, ur, self.Hq, Hkv, D, self.dtype, *key)
+                    drawn[key] = (qt.to(device), kt.to(device), vt.to(device))
+                row.append(drawn[key])
             self.qkv.append(row)
 
         def make_logits(rows, *idx):
@@ -145,6 +157,12 @@ class SectionDecode:
         self.hooks = None   # optional callables around each call: hooks(kind, "pre"/"post")
         self.after_attn = None   # optional after_attn(b, st, out), called after each attention call
 
+    def qkv_index(self, b, st):
+        """Seed indices of block b's step-st Q/K/V draw."""
+        if not self.qkv_pool:
+            return (b, st)
+        return (2000 + self.unit_rows[self.unit_of[b]], (b * self.steps + st) % self.qkv_pool)
+
     @property
     def tokens_per_decode(self):
         """Decoded (editable) tokens per decode, all sequences."""
@@ -180,7 +198,7 @@ class SectionDecode:
                 for st in range(self.steps):
                     q, k, v = self.qkv[b][st]
                     self._hook("attn", "pre")
-                    B.bc_attn_step(self.cache, length, None, None, q, k, v, [0, ur], B.BC_MASK_BLOCK_BIDIR,
+                    B.bc_attn_step(self.cache, length, None, None, q, k, v, [0, ur], self.mask,
                                    self.scale, out, self.ws_attn, stream=stream)
                     self._hook("attn", "post")
                     if self.after_attn is not None:
@@ -334,6 +352,238 @@ class ForkVerify:
             base = self.prefix + self.priv_len[s]
             vis += R * base + (R * R if pass_id == 0 else R * (R + 1) // 2)
         return 4 * self.D * self.Hq * vis
+
+
+class ForkTrajectory:
+    """Shared-prefix fork decoding a whole trajectory section with scaffold
+    speculative rounds (Fast-dDrive method summary sec. 3.2 "Scaffold
+    Speculative Decoding", sec. 3.3).
+
+    N rollouts share one prefix cache and decode the section's blocks in
+    order.  A block is decoded in rounds; a round runs, for the rollouts that
+    have not completed the block, in slot order (the active rollouts, lowest
+    first):
+      1. draft pass: bidirectional attention of the block's rows over the
+         shared prefix and each rollout's private cache;
+      2. draft argmax: an unmask with threshold 0 (SEMI) reveals every
+         unverified row with the argmax of its draft logits;
+      3. verify pass: causal attention of the same rows;
+      4. speculative verify from each rollout's first unverified row: the
+         accept length and the bonus token.
+    The host reads the accept lengths, bonuses and drafts back (one
+    synchronisation per round), advances each rollout's first unverified row
+    and drops the rollouts that completed the block; their private caches are
+    compacted into slot order for the next round.  When every rollout has
+    completed the block, each commits it to its private cache with
+    bc_kv_commit (the K/V of its last verify pass) and the next block starts.
+
+    The synthetic model outputs of a round (block b, round r):
+      * Q/K/V of both passes: seeded draws per (b, r mod ``pool``, pass), one
+        slice per slot;
+      * logits: a seeded clipped-normal base per kind (draft / verify), whose
+        first (active rollouts x rows) rows are the round's logits, with a
+        planted argmax per row (value 7 sigma + margin): the verify targets
+        t = ``synth.round_targets`` per (b, r, rollout) and the drafts
+        ``synth.drafts_with_agreement`` of t at rate ``p_agree``.  The planted
+        values are written before the round and restored after it."""
+
+    def __init__(self, n_rollouts, p_agree, seed=0, device="cuda:0", preset=None, pool=2):
+        p = dict(preset or synth.PRESETS["fork"])
+        self.N, self.p_agree, self.seed, self.pool, self.dev = int(n_rollouts), float(p_agree), seed, pool, device
+        self.Hq, self.Hkv, self.D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
+        self.dtype, self.prefix = p["dtype"], p["prefix"]
+        self.V, self.sigma = p["vocab"], p["sigma"]
+        self.peak = np.float32(7.0 * self.sigma + p.get("margin", 1.0))
+        self.blocks = list(p["blocks"])
+        N, Hq, Hkv, D, V = self.N, self.Hq, self.Hkv, self.D, self.V
+        self.Rmax = Rmax = max(self.blocks)
+        self.cap = sum(self.blocks)
+        (pk, pv), _ = synth.kv_cache(seed, 1, Hkv, self.prefix, D, [self.prefix], self.dtype)
+        self.shared = B.KVCache(pk.to(device), pv.to(device))
+        tdt = synth.torch_dtype(self.dtype)
+        z = lambda: torch.zeros((N, Hkv, self.cap, D), dtype=tdt, device=device)
+        self.priv = B.KVCache(z(), z())
+        self.sub = B.KVCache(z(), z())            # active rollouts' private caches, slot order
+        self.priv_len = np.zeros(N, np.int32)
+        self.qkv = {}
+        for b, R in enumerate(self.blocks):
+            for k in range(pool):
+                for pass_id in (0, 1):
+                    (q, _), (kk, _), (v, _) = synth.active_qkv(seed, N, R, Hq, Hkv, D, self.dtype, 100 + b,
+                                                               pass_id, k)
+                    self.qkv[(b, k, pass_id)] = (q.to(device), kk.to(device), v.to(device))
+        n_logits = N * Rmax * V
+        self.base = {kind: torch.from_numpy(synth.clipped_logits(seed, n_logits, self.sigma, 600 + i)).to(device)
+                     for i, kind in enumerate(("draft", "verify"))}
+        self.out = torch.empty(N * Rmax * Hq * D, dtype=tdt, device=device)
+        self.masked = torch.zeros(N * Rmax, dtype=torch.uint8, device=device)
+        self.tokens = torch.full((N * Rmax,), -1, dtype=torch.int32, device=device)
+        self.first = torch.zeros(N, dtype=torch.int32, device=device)
+        self.accept_len = torch.zeros(N, dtype=torch.int32, device=device)
+        self.bonus = torch.zeros(N, dtype=torch.int32, device=device)
+        self.n_commit = torch.zeros(N, dtype=torch.int32, device=device)
+        self.last_k = torch.zeros((N, Hkv * Rmax * D), dtype=tdt, device=device)
+        self.last_v = torch.zeros_like(self.last_k)
+        ws = 0
+        for R in set(self.blocks):
+            for n in range(1, N + 1):
+                ws = max(ws, B.bc_attn_workspace_bytes(self.shared, B.KVCache(self.sub.k[:n], self.sub.v[:n]),
+                                                       (n, R, Hq, D), [0, R]))
+        self.ws_attn = torch.zeros(ws, dtype=torch.uint8, device=device)
+        self.ws_unmask = torch.zeros(B.bc_unmask_workspace_bytes(N * Rmax, V), dtype=torch.uint8, device=device)
+        self.ws_verify = torch.zeros(B.bc_verify_workspace_bytes(N, Rmax, V), dtype=torch.uint8, device=device)
+        self.scale = 1.0 / np.sqrt(D)
+        # host staging through pinned memory
+        pin = lambda n, dt: torch.zeros(n, dtype=dt).pin_memory()
+        self.h_masked, self.h_tokens = pin(N * Rmax, torch.uint8), pin(N * Rmax, torch.int32)
+        self.h_first, self.h_acc, self.h_bonus = pin(N, torch.int32), pin(N, torch.int32), pin(N, torch.int32)
+        self.h_drafts = pin(N * Rmax, torch.int32)
+        self.h_idx = {k: pin(N * Rmax, torch.int64) for k in ("draft", "verify")}
+        self.d_idx = {k: torch.zeros(N * Rmax, dtype=torch.int64, device=device) for k in ("draft", "verify")}
+        self.saved = {k: torch.zeros(N * Rmax, dtype=torch.float32, device=device) for k in ("draft", "verify")}
+        self.trace, self.rounds = [], []
+        self.result = None
+
+    def targets(self, b, r, s):
+        """(verify argmax targets, drafts) [R_b] of rollout s in round r."""
+        R = self.blocks[b]
+        t = synth.round_targets(self.seed, self.V, R, 600 + b, r, s)
+        return t, synth.drafts_with_agreement(self.seed, t, self.p_agree, self.V, 600 + b, r, s)
+
+    def host_logits(self, kind, b, r, active, base):
+        """The round's float32 logits [len(active)][R_b][V] on the host, from
+        the host copy ``base`` of the kind's clipped base (flat)."""
+        R, V, n = self.blocks[b], self.V, len(active)
+        x = base[: n * R * V].reshape(n, R, V).copy()
+        for j, s in enumerate(active):
+            t, d = self.targets(b, r, s)
+            x[j, np.arange(R), t if kind == "verify" else d] = self.peak
+        return x
+
+    def host_qkv(self, b, r, pass_id):
+        """float32 host arrays (q, k, v) of the pool entry round r reads."""
+        (_, q), (_, k), (_, v) = synth.active_qkv(self.seed, self.N, self.blocks[b], self.Hq, self.Hkv, self.D,
+                                                  self.dtype, 100 + b, pass_id, r % self.pool)
+        return q, k, v
+
+    def _plant(self, b, r, active):
+        R, V, n = self.blocks[b], self.V, len(active)
+        for kind in ("draft", "verify"):
+            h = self.h_idx[kind]
+            for j, s in enumerate(active):
+                t, d = self.targets(b, r, s)
+                tok = t if kind == "verify" else d
+                h[j * R:(j + 1) * R] = torch.from_numpy((j * R + np.arange(R)) * V + tok.astype(np.int64))
+            idx = self.d_idx[kind][: n * R]
+            idx.copy_(h[: n * R], non_blocking=True)
+            flat = self.base[kind]
+            torch.index_select(flat, 0, idx, out=self.saved[kind][: n * R])
+            flat.index_fill_(0, idx, float(self.peak))
+
+    def _restore(self, n_rows):
+        for kind in ("draft", "verify"):
+            self.base[kind].index_copy_(0, self.d_idx[kind][:n_rows], self.saved[kind][:n_rows])
+
+    def run(self, stream=None, after_pass=None):
+        """Decode the whole section for every rollout.  Returns the decoded
+        tokens [N][sum(blocks)] (also in ``self.result``); ``self.trace``
+        holds one dict per round (block, round, active, first, accept,
+        bonus), ``self.rounds`` the rounds per block.  ``after_pass(b, r,
+        pass_id, active, out)`` is called after each attention pass.  All
+        device work is issued on ``stream`` (a torch stream, or None for the
+        current one)."""
+        if stream is None:
+            return self._run(None, after_pass)
+        with torch.cuda.stream(stream):
+            return self._run(stream, after_pass)
+
+    def _run(self, stream, after_pass):
+        N, Hq, Hkv, D, V = self.N, self.Hq, self.Hkv, self.D, self.V
+        self.priv_len[:] = 0
+        result = np.full((N, self.cap), -1, np.int32)
+        self.trace, self.rounds = [], []
+        row0 = 0
+        for b, R in enumerate(self.blocks):
+            first = np.zeros(N, np.int64)
+            verified = np.full((N, R), -1, np.int32)
+            active, compacted = list(range(N)), None
+            pl = int(self.priv_len[0])
+            r = 0
+            while active:
+                n = len(active)
+                if n == N:
+                    priv = self.priv
+                else:
+                    if active != compacted and pl > 0:
+                        idx = torch.tensor(active, dtype=torch.int64, device=self.dev)
+                        for src, dst in ((self.priv.k, self.sub.k), (self.priv.v, self.sub.v)):
+                            dst[:n, :, :pl] = src.index_select(0, idx)[:, :, :pl]
+                    compacted = active
+                    priv = B.KVCache(self.sub.k[:n], self.sub.v[:n])
+                # the round's state: verified rows unmasked with their tokens
+                hm, ht = self.h_masked[: n * R].numpy(), self.h_tokens[: n * R].numpy()
+                for j, s in enumerate(active):
+                    hm[j * R:(j + 1) * R] = np.arange(R) >= first[s]
+                    ht[j * R:(j + 1) * R] = verified[s]
+                self.h_first[:n] = torch.from_numpy(first[active].astype(np.int32))
+                masked, tokens, first_d = self.masked[: n * R], self.tokens[: n * R], self.first[:n]
+                masked.copy_(self.h_masked[: n * R], non_blocking=True)
+                tokens.copy_(self.h_tokens[: n * R], non_blocking=True)
+                first_d.copy_(self.h_first[:n], non_blocking=True)
+                self._plant(b, r, active)
+                out = self.out[: n * R * Hq * D].view(n, R, Hq, D)
+                qkv = [self.qkv[(b, r % self.pool, pass_id)] for pass_id in (0, 1)]
+                q, k, v = (x[:n] for x in qkv[0])
+                B.bc_attn_step(self.shared, [self.prefix], priv, [pl] * n, q, k, v, [0, R], B.BC_MASK_BLOCK_BIDIR,
+                               self.scale, out, self.ws_attn, stream=stream)
+                if after_pass is not None:
+                    after_pass(b, r, 0, list(active), out)
+                dlg = self.base["draft"][: n * R * V].view(n * R, V)
+                B.bc_unmask_select(dlg, list(range(0, n * R + 1, R)), [B.BC_UNMASK_SEMI] * n, [1] * n, 0.0, masked,
+                                   tokens, None, self.n_commit[:n], self.ws_unmask, stream=stream)
+                q, k, v = (x[:n] for x in qkv[1])
+                B.bc_attn_step(self.shared, [self.prefix], priv, [pl] * n, q, k, v, [0, R], B.BC_MASK_BLOCK_CAUSAL,
+                               self.scale, out, self.ws_attn, stream=stream)
+                if after_pass is not None:
+                    after_pass(b, r, 1, list(active), out)
+                vlg = self.base["verify"][: n * R * V].view(n, R, V)
+                B.bc_spec_verify(vlg, tokens.view(n, R), None, first_d, self.accept_len[:n], self.bonus[:n],
+                                 self.ws_verify, stream=stream)
+                self._restore(n * R)
+                self.h_acc[:n].copy_(self.accept_len[:n], non_blocking=True)
+                self.h_bonus[:n].copy_(self.bonus[:n], non_blocking=True)
+                self.h_drafts[: n * R].copy_(tokens, non_blocking=True)
+                torch.cuda.current_stream().synchronize()
+                acc, bon = self.h_acc[:n].tolist(), self.h_bonus[:n].tolist()
+                drafts = self.h_drafts[: n * R].numpy().reshape(n, R)
+                self.trace.append(dict(block=b, round=r, active=list(active),
+                                       first=[int(first[s]) for s in active], accept=acc, bonus=bon))
+                still = []
+                for j, s in enumerate(active):
+                    f, a = int(first[s]), acc[j]
+                    verified[s, f:f + a] = drafts[j, f:f + a]
+                    if bon[j] >= 0:
+                        verified[s, f + a] = bon[j]
+                    first[s] = f + a + (1 if bon[j] >= 0 else 0)
+                    if first[s] < R:
+                        still.append(s)
+                    else:
+                        # the K/V of this (its last) verify pass are what it commits
+                        n_kv = Hkv * R * D
+                        self.last_k[s, :n_kv].view(Hkv, R, D).copy_(k[j])
+                        self.last_v[s, :n_kv].view(Hkv, R, D).copy_(v[j])
+                active = still
+                r += 1
+            self.rounds.append(r)
+            result[:, row0:row0 + R] = verified
+            n_kv = Hkv * R * D
+            for s in range(N):
+                B.bc_kv_commit(self.priv, self.priv_len, s, int(self.priv_len[s]), R,
+                               self.last_k[s, :n_kv].view(Hkv, R, D), self.last_v[s, :n_kv].view(Hkv, R, D),
+                               stream=stream)
+            row0 += R
+        self.result = result
+        return result
 
 
 class PipelinedDecode:

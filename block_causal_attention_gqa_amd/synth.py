@@ -68,7 +68,8 @@ def torch_dtype(dtype):
 #   section_scaffold: the section decode with the sections' scaffold tokens
 #                inside the blocks (404 rows, blocks of <= 32 editable rows)
 #   fork       : shared prefix 3072 + 210, 16q/2kv, D 128, bf16, N rollouts,
-#                trajectory blocks 24/23/23, logits [24 x 151936]
+#                trajectory blocks 24/23/23, logits [24 x 151936]; a planted
+#                argmax 1.0 above the 7 sigma clip in the trajectory rounds
 # ---------------------------------------------------------------------------
 
 SECTION_EDITABLE = {"critical_objects": 12, "explanation": 192,
@@ -142,8 +143,22 @@ PRESETS = {
                           prefix=512, blocks=split_sizes(625, 32), window=3, vocab=2048,
                           sigma=4.0, threshold=0.9),
     "fork": dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype="bf16",
-                 prefix=3072 + 210, blocks=[24, 23, 23], vocab=151936, sigma=4.0),
+                 prefix=3072 + 210, blocks=[24, 23, 23], vocab=151936, sigma=4.0, margin=1.0),
 }
+
+
+def large_block_preset(block_size, n_seq=1, vocab=None):
+    """The WAM-Diff2-shaped large-block decode at block size B: 256 output
+    tokens in 256 / B blocks of B, min(16, B) denoise steps per block."""
+    p = dict(PRESETS["large_block"], n_seq=n_seq)
+    p["blocks"] = [block_size] * (256 // block_size)
+    p["steps"] = min(16, block_size)
+    if vocab:
+        p["vocab"] = vocab
+    return p
+
+
+LARGE_BLOCK_SIZES = (1, 4, 8, 16, 32)
 
 
 def kv_cache(seed, n_seq, n_kv_heads, capacity, head_dim, lengths, dtype, purpose=("prefix_k", "prefix_v")):
@@ -199,6 +214,20 @@ def argmax_planted_logits(seed, n_rows, vocab, sigma, margin, *idx):
     t = g.integers(0, vocab, size=n_rows).astype(np.int32)
     x[np.arange(n_rows), t] = np.float32(7.0 * sigma + margin)
     return x, t
+
+
+def clipped_logits(seed, n, sigma, *idx):
+    """float32 N(0, sigma^2) draws clipped to [-7 sigma, 7 sigma], flat [n]:
+    the base of logits whose row argmax is then planted above 7 sigma."""
+    x = rng(seed, "logits", *idx).standard_normal(n, dtype=np.float32)
+    x *= np.float32(sigma)
+    np.clip(x, np.float32(-7.0 * sigma), np.float32(7.0 * sigma), out=x)
+    return x
+
+
+def round_targets(seed, vocab, n_rows, *idx):
+    """Seeded token ids [n_rows] planted as the row argmaxes of one round."""
+    return rng(seed, "peak", *idx).integers(0, vocab, size=n_rows).astype(np.int32)
 
 
 def drafts_with_agreement(seed, target, p_agree, vocab, *idx):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import section as OS
+from oracle import attention as OA, section as OS, unmask as OU, verify as OV
 from tests import gpu_util as G
 from block_causal_attention_gqa_amd import decode, synth
 
@@ -102,12 +102,32 @@ def test_section_decode_graph_replays_match_oracle_and_eager(seed, vocab, plante
             assert torch.equal(a, b), "replay %d: %s differs from the eager decode" % (i, name)
 
 
+def oracle_fork_round(fv, seed, block):
+    """The oracle's fork round on ForkVerify's inputs: the verify pass's
+    attention, the draft tokens and masks, the accept lengths and bonuses."""
+    h = fv.host_inputs(seed=seed, block=block)
+    N, R = fv.N, fv.R
+    q, k, v = h["qkv"][1]
+    attn = OA.attention_step(q, h["pk"], h["pv"], [fv.prefix], k, v, [0, R], OA.MASK_CAUSAL, scale=fv.scale,
+                             priv_k=h["vk"], priv_v=h["vv"], priv_len=fv.priv_len)
+    masked0 = (1 - h["fixed"]).reshape(-1).astype(np.uint8)
+    m, t, _, _ = OU.unmask_select(h["draft_logits"], fv.blk_rows, [OU.MODE_SEMI] * N, [1] * N, np.float32(0.0),
+                                  masked0, h["tokens0"])
+    if fv.temperature is None:
+        acc, bon = OV.spec_verify(h["verify_logits"], t.reshape(N, R), h["fixed"], np.zeros(N, np.int32))
+    else:
+        acc, bon = OV.spec_verify_sampled(h["verify_logits"], h["noise"], 1.0 / fv.temperature, t.reshape(N, R),
+                                          h["fixed"], np.zeros(N, np.int32))
+    return attn, t, m, acc, bon
+
+
 @pytest.mark.parametrize("temperature", [None, 0.7])
-def test_fork_round_graph_replays_match_eager(temperature):
+def test_fork_round_graph_replays_match_oracle_and_eager(temperature):
     N = 16
     print("graph: fork round N=%d temperature=%s" % (N, temperature), flush=True)
     fv = decode.ForkVerify(N, seed=6, device=G.DEV, block=0, temperature=temperature,
                            preset=dict(synth.PRESETS["fork"], vocab=20000))
+    w_attn, w_tok, w_masked, w_acc, w_bon = oracle_fork_round(fv, 6, 0)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         fv.run()
@@ -129,4 +149,8 @@ def test_fork_round_graph_replays_match_eager(temperature):
         got = (fv.out, fv.tokens, fv.masked, fv.accept_len, fv.bonus)
         for name, a, b in zip(("attention out", "tokens", "masked", "accept_len", "bonus"), got, want):
             assert torch.equal(a, b), "replay %d: %s differs from the eager round" % (i, name)
+        err = np.abs(fv.out.float().cpu().numpy() - w_attn).max()
+        assert err <= 1e-2, "replay %d: verify-pass attention max-abs %.3g against the oracle" % (i, err)
+        assert np.array_equal(fv.tokens.cpu().numpy(), w_tok) and np.array_equal(fv.masked.cpu().numpy(), w_masked)
+        assert np.array_equal(fv.accept_len.cpu().numpy(), w_acc) and np.array_equal(fv.bonus.cpu().numpy(), w_bon)
     assert np.all(fv.accept_len.cpu().numpy() >= 0)

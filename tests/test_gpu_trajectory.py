@@ -1,0 +1,88 @@
+"""The shared-prefix fork decoding a whole trajectory section with scaffold
+speculative rounds, on the GPU, against the float64 trajectory oracle on the
+same seeded inputs (Fast-dDrive method summary sec. 3.2 "Scaffold Speculative
+Decoding", sec. 3.3): N rollouts, blocks 24/23/23 over a 3282-key shared
+prefix, draft agreement 0.5 / 0.8 / 1.0.  Round by round the active
+rollouts, their first unverified rows, accept lengths and bonus tokens must
+be equal; then the decoded tokens and every rollout's private cache (bit for
+bit), and sampled attention passes within 1e-2 of the oracle."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as OA, trajectory as OT
+from tests import gpu_util as G
+from block_causal_attention_gqa_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SEED = 13
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.require_lib()
+
+
+CASES = [(N, p, 2048) for N in (1, 4, 16, 64) for p in (0.5, 0.8, 1.0)] + [(4, 0.8, None)]
+
+
+@pytest.mark.parametrize("N,p_agree,vocab", CASES)
+def test_trajectory_matches_oracle(N, p_agree, vocab):
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("trajectory N=%d p=%.1f vocab=%s" % (N, p_agree, vocab), flush=True)
+    preset = dict(synth.PRESETS["fork"])
+    if vocab:
+        preset["vocab"] = vocab
+    tr = decode.ForkTrajectory(N, p_agree, seed=SEED, device=G.DEV, preset=preset)
+    seen = {}
+    sample_rounds = {0, 2} if N >= 16 else {0, 1, 2, 5}
+
+    def after_pass(b, r, pass_id, active, out):
+        if r in sample_rounds and (N < 16 or b == 1):
+            torch.cuda.synchronize()
+            seen[(b, r, pass_id)] = (list(active), out.float().cpu().numpy())
+
+    got = tr.run(after_pass=after_pass)
+    torch.cuda.synchronize()
+
+    base = {kind: synth.clipped_logits(SEED, N * tr.Rmax * tr.V, tr.sigma, 600 + i)
+            for i, kind in enumerate(("draft", "verify"))}
+    want = OT.fork_trajectory(
+        tr.blocks, N,
+        lambda b, r, act: tr.host_logits("draft", b, r, act, base["draft"]),
+        lambda b, r, act, tok: tr.host_logits("verify", b, r, act, base["verify"]),
+        lambda b, r, j: tuple(x[j] for x in tr.host_qkv(b, r, 1)[1:]),
+        priv_shape=(tr.Hkv, tr.D))
+    assert tr.rounds == want["rounds"]
+    assert len(tr.trace) == len(want["trace"])
+    for k, (a, w) in enumerate(zip(tr.trace, want["trace"])):
+        assert a == w, "round %d: %s != %s" % (k, a, w)
+    assert np.array_equal(got, want["tokens"])
+    if p_agree == 1.0:
+        assert tr.rounds == [1, 1, 1]
+    # every rollout's private cache: its blocks' last verify K/V, in order
+    kc = tr.priv.k.float().cpu().numpy()
+    vc = tr.priv.v.float().cpu().numpy()
+    assert list(tr.priv_len) == [tr.cap] * N
+    for s in range(N):
+        assert np.array_equal(kc[s], want["priv_k"][s]) and np.array_equal(vc[s], want["priv_v"][s]), s
+
+    # sampled attention passes against the oracle's attention
+    _, (pk, pv) = synth.kv_cache(SEED, 1, tr.Hkv, tr.prefix, tr.D, [tr.prefix], tr.dtype)
+    assert seen
+    for (b, r, pass_id), (active, out) in seen.items():
+        R, n = tr.blocks[b], len(active)
+        pl = sum(tr.blocks[:b])
+        priv_k = np.zeros((n, tr.Hkv, max(pl, 1), tr.D), np.float32)
+        priv_v = np.zeros_like(priv_k)
+        for j, s in enumerate(active):
+            priv_k[j, :, :pl] = want["priv_k"][s][:, :pl]
+            priv_v[j, :, :pl] = want["priv_v"][s][:, :pl]
+        q, k, v = (x[:n] for x in tr.host_qkv(b, r, pass_id))
+        mode = OA.MASK_BIDIR if pass_id == 0 else OA.MASK_CAUSAL
+        ref = OA.attention_step(q, pk, pv, [tr.prefix], k, v, [0, R], mode, scale=tr.scale,
+                                priv_k=priv_k, priv_v=priv_v, priv_len=[pl] * n)
+        err = np.abs(out - ref).max()
+        assert err <= 1e-2, "block %d round %d pass %d: max-abs %.3g" % (b, r, pass_id, err)
