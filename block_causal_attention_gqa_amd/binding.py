@@ -23,6 +23,8 @@ BC_ERR_CAPACITY = -3
 BC_ERR_ORDER = -4
 BC_ERR_WORKSPACE = -5
 BC_ERR_HIP = -6
+BC_ERR_SCRATCH = -7
+BC_STATIC_SCRATCH_BYTES = 32 << 20
 
 BC_F32 = 0
 BC_BF16 = 1
@@ -38,7 +40,8 @@ BC_MAX_SCAN_ROWS = 4096
 EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
             "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
             "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide",
-            "bc_pipeline_create", "bc_pipeline_destroy", "bc_pipeline_next", "bc_pipeline_report")
+            "bc_pipeline_create", "bc_pipeline_destroy", "bc_pipeline_next", "bc_pipeline_report",
+            "bc_attn_step_static")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -85,6 +88,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [cp, _c_i32p, cp, _c_i32p, ap, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    L.bc_attn_step_static.argtypes = [cp, _c_i32p, cp, _c_i32p, ap, i32, ctypes.c_float, i32, vp, vp]
+    L.bc_attn_step_static.restype = ctypes.c_int
     L.bc_unmask_workspace_bytes.argtypes = [i32, i32]
     L.bc_unmask_workspace_bytes.restype = sz
     for name in ("bc_unmask_select", "bc_unmask_decide"):
@@ -275,6 +280,31 @@ def bc_attn_combine(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, 
                     n_prefix_splits=0, stream=None, check=True):
     return _attn_call("bc_attn_combine", prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale,
                       out, ws, n_prefix_splits, stream, check)
+
+
+def bc_attn_step_static(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, mask, scale, out,
+                        n_prefix_splits=0, stream=None, check=True):
+    """bc_attn_step without a workspace: the library's static scratch holds
+    the split partials (nothing is allocated)."""
+    tdtype = prefix.k.dtype
+    act, _off = _active(q, k, v, blk_off, tdtype, prefix.n_kv_heads, prefix.head_dim)
+    pl_arr, pl_p = _host_i32(prefix_len)
+    if len(pl_arr) != prefix.n_seq:
+        raise ValueError("prefix_len needs one entry per prefix sequence")
+    ps = prefix.struct()
+    vs, vl_arr, vl_p = None, None, None
+    if priv is not None:
+        vs = priv.struct()
+        vl_arr, vl_p = _host_i32(priv_len)
+        if len(vl_arr) != act.n_seq:
+            raise ValueError("priv_len needs one entry per rollout")
+    _dev(out, "out", tdtype, q.numel())
+    st = lib().bc_attn_step_static(ctypes.byref(ps), pl_p, ctypes.byref(vs) if vs else None, vl_p,
+                                   ctypes.byref(act), int(mask), float(scale), int(n_prefix_splits),
+                                   out.data_ptr(), _stream(stream))
+    if check and st != BC_OK:
+        raise BcError(st, "bc_attn_step_static")
+    return st
 
 
 def bc_kv_commit(cache, length, seq, start, n_rows, blk_k, blk_v, stream=None, check=True):

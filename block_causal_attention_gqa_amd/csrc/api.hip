@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "bc_internal.h"
 
@@ -169,6 +170,8 @@ const char* bc_status_str(int status) {
     case BC_ERR_ORDER: return "BC_ERR_ORDER: commit does not start at the current length";
     case BC_ERR_WORKSPACE: return "BC_ERR_WORKSPACE: workspace missing or too small";
     case BC_ERR_HIP: return "BC_ERR_HIP: the HIP runtime rejected a launch";
+    case BC_ERR_SCRATCH:
+      return "BC_ERR_SCRATCH: the call needs more than the static scratch (BC_STATIC_SCRATCH_BYTES) holds";
     default: return "unknown bc_status";
   }
 }
@@ -209,10 +212,10 @@ size_t bc_attn_workspace_bytes(const bc_kv_cache* prefix, const bc_kv_cache* pri
 
 namespace {
 
-// Validate an attention call and fill the kernel arguments; BC_OK or an error.
-int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
-                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale, int32_t n_prefix_splits,
-                 void* out, void* ws, size_t ws_bytes, AttnArgs* args) {
+// Every check of an attention call's arguments except the workspace.
+int validate_attn_call(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                       const int32_t* priv_len, const bc_active* a, int32_t mask, float scale,
+                       int32_t n_prefix_splits, const void* out) {
   int st = validate_attn(prefix, priv, a, n_prefix_splits);
   if (st) return st;
   if (!prefix_len || !out || (priv && !priv_len)) return BC_ERR_ARG;
@@ -223,6 +226,15 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   if (priv)
     for (int s = 0; s < a->n_seq; ++s)
       if (priv_len[s] < 0 || priv_len[s] > priv->capacity) return BC_ERR_ARG;
+  return BC_OK;
+}
+
+// Validate an attention call and fill the kernel arguments; BC_OK or an error.
+int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                 const int32_t* priv_len, const bc_active* a, int32_t mask, float scale, int32_t n_prefix_splits,
+                 void* out, void* ws, size_t ws_bytes, AttnArgs* args) {
+  int st = validate_attn_call(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out);
+  if (st) return st;
 
   std::memset(args, 0, sizeof(*args));
   if (!ws) return BC_ERR_WORKSPACE;
@@ -394,6 +406,60 @@ int bc_attn_step(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   AttnArgs args;
   const int st = prepare_attn(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out, ws,
                               ws_bytes, &args);
+  if (st) return st;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_attn_partial(args, prefix->dtype, s) != hipSuccess) return BC_ERR_HIP;
+  if (launch_attn_combine(args, prefix->dtype, s) != hipSuccess) return BC_ERR_HIP;
+  return BC_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free attention
+// The split partials of bc_attn_step_static live in this array.  In host code
+// its name is only the host-side stand-in of the device variable: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever handed to a kernel.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[BC_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices] = {};
+
+// The current device's scratch address; BC_OK or an error.
+int scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return BC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BC_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return BC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bc_attn_step_static(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,
+                        const int32_t* priv_len, const bc_active* a, int32_t mask, float scale,
+                        int32_t n_prefix_splits, void* out, void* stream) {
+  // validate before touching the device, so that bad arguments enqueue nothing
+  int st = validate_attn_call(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out);
+  if (st) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  AttnArgs args;
+  st = prepare_attn(prefix, prefix_len, priv, priv_len, a, mask, scale, n_prefix_splits, out, ws,
+                    BC_STATIC_SCRATCH_BYTES, &args);
+  if (st == BC_ERR_WORKSPACE) return BC_ERR_SCRATCH;
   if (st) return st;
   (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -54,7 +54,8 @@ typedef enum {
   BC_ERR_CAPACITY = -3,     /* a commit would grow a sequence past its capacity */
   BC_ERR_ORDER = -4,        /* a commit that does not start at the current length */
   BC_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the query says */
-  BC_ERR_HIP = -6           /* the HIP runtime rejected a launch */
+  BC_ERR_HIP = -6,          /* the HIP runtime rejected a launch */
+  BC_ERR_SCRATCH = -7       /* the call needs more than the static scratch holds */
 } bc_status;
 
 typedef enum { BC_F32 = 0, BC_BF16 = 1 } bc_dtype;
@@ -326,6 +327,32 @@ void bc_pipeline_destroy(bc_pipeline *p);
 int bc_pipeline_next(bc_pipeline *p, int32_t *active, int32_t *local_step, int32_t *mode,
                      int32_t *n_div, int32_t *blk_off, int32_t *row0);
 int bc_pipeline_report(bc_pipeline *p, const int32_t *n_commit, int32_t *done);
+
+/* ------------------------------------------------------------------------ */
+/* Attention without allocation or workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.
+ *
+ * Exactly bc_attn_step (same arguments, same kernels, same results), except
+ * that the split partials live in the library's own scratch: one static
+ * device array of BC_STATIC_SCRATCH_BYTES per GPU, which that GPU holds until
+ * the process ends.  The call allocates nothing.  The first call on a device
+ * looks the array's address up (with that device current); later calls reuse
+ * it.  With n_prefix_splits == 0 the automatic split count is reduced to what
+ * the scratch holds; a call that needs more than BC_STATIC_SCRATCH_BYTES even
+ * with one split, or whose explicit split count does not fit, returns
+ * BC_ERR_SCRATCH with nothing enqueued.  At most 64 devices.
+ *
+ * Every call on one GPU shares that GPU's array, and it keeps the last
+ * call's contents (nothing in it needs to start at zero).  Calls that may
+ * overlap on one GPU -- on different streams, or from different host threads
+ * without ordering -- race on the array and give wrong results: issue them
+ * on one stream, or use bc_attn_step with separate workspaces. */
+#define BC_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int bc_attn_step_static(const bc_kv_cache *prefix, const int32_t *prefix_len,
+                        const bc_kv_cache *priv, const int32_t *priv_len,
+                        const bc_active *a, int32_t mask, float scale, int32_t n_prefix_splits,
+                        void *out, void *stream);
 
 /* Human-readable name of a bc_status value (never NULL). */
 const char *bc_status_str(int status);

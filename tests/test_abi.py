@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert B.bc_status_str(st).startswith("BC_")
     assert B.bc_status_str(-99) == "unknown bc_status"
 
@@ -95,6 +95,22 @@ def test_attention_validation(L):
     assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=2), priv_len=_lens(0, 65)) == B.BC_ERR_ARG
     assert attn(L, _cache(S=1), _lens(8), f_act, priv=_cache(S=2, dtype=B.BC_F32),
                 priv_len=_lens(0, 0)) == B.BC_ERR_UNSUPPORTED
+
+
+def test_static_attention_validation(L):
+    # the allocation-free entry point validates like bc_attn_step, before it
+    # looks up its scratch on the device
+    def call(cache, lens, act, mask=0, splits=0, out=1):
+        return L.bc_attn_step_static(ctypes.byref(cache), lens, None, None, ctypes.byref(act), mask, 0.1, splits,
+                                     out, None)
+    act, keep = _active()
+    assert call(_cache(D=96), _lens(8), act) == B.BC_ERR_UNSUPPORTED
+    assert call(_cache(k=0), _lens(8), act) == B.BC_ERR_ARG
+    assert call(_cache(), _lens(65), act) == B.BC_ERR_ARG
+    assert call(_cache(), _lens(8), act, mask=2) == B.BC_ERR_ARG
+    assert call(_cache(), _lens(8), act, splits=257) == B.BC_ERR_ARG
+    assert call(_cache(), _lens(8), act, out=0) == B.BC_ERR_ARG
+    assert "static scratch" in B.bc_status_str(B.BC_ERR_SCRATCH)
 
 
 def test_workspace_queries(L):
