@@ -129,6 +129,9 @@ def main():
     # sanity: the decode finished every block
     assert int(dec.masked.sum().item()) == 0, "decode left masked rows"
     assert int((dec.tokens < 0).sum().item()) == 0
+    # what the last timed replay left, for the oracle check
+    timed_out = {"tokens": dec.tokens.cpu().numpy(), "masked": dec.masked.cpu().numpy(),
+                 "cache_k": dec.cache.k[0].float().cpu().numpy(), "cache_v": dec.cache.v[0].float().cpu().numpy()}
 
     # the same decode issued call by call from the host (no graph), for the
     # graph's gain: host marshalling and launch per call sit between kernels
@@ -276,7 +279,7 @@ def main():
     if not args.no_legs:
         result["legs"] = legs(stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(dec, args)
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(dec, args, timed_out)
     print(json.dumps(result), flush=True)
 
 
@@ -479,14 +482,190 @@ def graph_us(fn, stream, reps=10, replays=5):
     return e0.elapsed_time(e1) * 1e3 / (replays * reps)
 
 
+def cold_warm_us(stream, fn, flush, reps=20, replays=5):
+    """(cold, warm) duration of one fn() on `stream`: one graph holds reps
+    repetitions of [pre, fn()], another the same pre alone, and the call time
+    is their difference / reps.  Cold: pre writes `flush` (>= 512 MiB), which
+    leaves the 256 MB MALL and the L2 holding none of the call's data; warm:
+    pre is a GPU spin that touches no memory.  Median over the replays."""
+    import torch
+
+    def graph_ms(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            body()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                body()
+            ts = []
+            for _ in range(replays):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts]))
+
+    res = []
+    for cold in (True, False):
+        def pre():
+            if cold:
+                flush.fill_(1.0)
+            else:
+                torch.cuda._sleep(100000)
+
+        def with_call():
+            for _ in range(reps):
+                pre()
+                fn()
+
+        def without():
+            for _ in range(reps):
+                pre()
+        res.append((graph_ms(with_call) - graph_ms(without)) * 1e3 / reps)
+    return res
+
+
+def trajectory_legs(stream):
+    """The shared-prefix fork decoding the whole 70-token trajectory section
+    (blocks 24/23/23, 3282 shared keys, vocab 151936) with scaffold
+    speculative rounds, at N = 1, 4, 16, 64 rollouts and draft agreement 0.5,
+    0.8, 1.0.  Rounds are data dependent (the host reads each round's accept
+    lengths), so a decode is timed whole on the wall clock with its inputs
+    resident: median of 3 after one warm decode."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    rows = []
+    for N in (1, 4, 16, 64):
+        tr = decode.ForkTrajectory(N, 1.0, seed=0, device="cuda:0")
+        for p in (0.5, 0.8, 1.0):
+            tr.p_agree = p
+            tr.run(stream)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                tr.run(stream)
+                torch.cuda.synchronize()
+                ts.append(time.perf_counter() - t0)
+            ms = float(np.median(ts)) * 1e3
+            n_rounds = sum(tr.rounds)
+            rows.append({"N": N, "p_agree": p, "rounds": list(tr.rounds), "ms": round(ms, 3),
+                         "round_us": round(ms * 1e3 / n_rounds, 1), "tokens": N * tr.cap,
+                         "tok_s": round(N * tr.cap / ms * 1e3, 1)})
+        del tr
+        torch.cuda.empty_cache()
+    return rows
+
+
+def large_block_legs(stream):
+    """The WAM-Diff2-shaped large-block decode (32q/8kv heads, head_dim 128,
+    2048-token prefix, 256 output tokens, vocab 151936) at block sizes
+    B = 1, 4, 8, 16, 32 (min(16, B) steps per block), batch 1 and 16 with
+    independent prefixes, each decode replayed whole as one graph (four
+    distinct logits / Q-K-V sets cycled over its steps); and the attention
+    call of the middle block's first step timed back to back, cold and warm."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    from block_causal_attention_gqa_amd import decode, synth
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")     # 512 MiB
+    rows = []
+    for S in (1, 16):
+        for Bsz in synth.LARGE_BLOCK_SIZES:
+            p = synth.large_block_preset(Bsz, n_seq=S)
+            dec = decode.SectionDecode(p, seed=0, n_seq=S, device="cuda:0", logits_pool=4, qkv_pool=4)
+            us = graph_us(lambda: dec.run(stream), stream, reps=1, replays=3)
+            rec = {"B": Bsz, "batch": S, "denoise_steps": dec.denoise_steps, "decode_ms": round(us / 1e3, 3),
+                   "step_us": round(us / dec.denoise_steps, 2), "tok_s": round(S * 256 / us * 1e6, 1)}
+            b = len(dec.blocks) // 2
+            L = p["prefix"] + b * Bsz
+            q, k, v = dec.qkv[b][0]
+            lens = [L] * S
+
+            def call():
+                B.bc_attn_step(dec.cache, lens, None, None, q, k, v, [0, Bsz], B.BC_MASK_BLOCK_BIDIR, dec.scale,
+                               dec.out[Bsz], dec.ws_attn, stream=stream)
+            b2b = graph_us(call, stream)
+            cold, warm = cold_warm_us(stream, call, flush)
+            nbytes, flops = (S * x for x in attn_bytes_flops(L, Bsz, dec.Hq, dec.Hkv, dec.D))
+            rec["attn"] = {"prefix": L, "bytes": nbytes, "us_back_to_back": round(b2b, 3),
+                           "us_cold": round(cold, 3), "us_warm": round(warm, 3),
+                           "TB_s_back_to_back": round(nbytes / b2b / 1e6, 3), "TB_s_cold": round(nbytes / cold / 1e6, 3),
+                           "TB_s_warm": round(nbytes / warm / 1e6, 3),
+                           "hbm_frac_cold": round(nbytes / cold / 1e3 / HBM_PEAK_GBS, 4),
+                           "TFLOP_s_back_to_back": round(flops / b2b / 1e6, 1)}
+            rows.append(rec)
+            del dec
+            torch.cuda.empty_cache()
+    return rows
+
+
+def tiny_leg(stream):
+    """The tiny configuration: one denoise step of 8 rows over a 256-token
+    prefix (4q/1kv heads, head_dim 64, float32), the unmask over [8 x 1024]
+    logits, and the commit, replayed as one graph."""
+    from block_causal_attention_gqa_amd import decode, synth
+    dec = decode.SectionDecode(synth.PRESETS["tiny"], seed=0, device="cuda:0")
+    us = graph_us(lambda: dec.run(stream), stream)
+    return {"step_us": round(us, 3), "tokens": dec.tokens_per_decode}
+
+
+def window_leg(stream):
+    """One pipelined step with three active 7-token blocks (21 rows: the
+    oldest fully active, the others semi-active; seeded completion ratios)
+    over a 512-token prefix, 16q/2kv heads, head_dim 128, bf16, logits
+    [21 x 2048]: the attention call and the unmask (with the masks restored
+    before it, a 21-byte copy), each timed back to back."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    from block_causal_attention_gqa_amd import synth
+    p = synth.PRESETS["pipelined"]
+    Hq, Hkv, D, L = p["n_q_heads"], p["n_kv_heads"], p["head_dim"], p["prefix"]
+    (pk, pv), _ = synth.kv_cache(0, 1, Hkv, L, D, [L], "bf16")
+    (q, _), (k, _), (v, _) = synth.active_qkv(0, 1, 21, Hq, Hkv, D, "bf16", 0)
+    cache = B.KVCache(pk.to("cuda:0"), pv.to("cuda:0"))
+    q, k, v = q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0")
+    off = [0, 7, 14, 21]
+    out = torch.empty((1, 21, Hq, D), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.zeros(B.bc_attn_workspace_bytes(cache, None, (1, 21, Hq, D), off), dtype=torch.uint8,
+                     device="cuda:0")
+    g = synth.rng(0, "ratio", 0)
+    m0 = np.ones(21, np.uint8)
+    for blk in range(3):
+        m0[7 * blk + g.choice(7, size=int(g.random() * 7), replace=False)] = 0
+    masked0 = torch.from_numpy(m0).to("cuda:0")
+    masked = masked0.clone()
+    tokens = torch.full((21,), -1, dtype=torch.int32, device="cuda:0")
+    lg = torch.from_numpy(synth.logits(0, 21, p["vocab"], p["sigma"], 0)).to("cuda:0")
+    nc = torch.zeros(3, dtype=torch.int32, device="cuda:0")
+    wsu = torch.zeros(B.bc_unmask_workspace_bytes(21, p["vocab"]), dtype=torch.uint8, device="cuda:0")
+    a_us = graph_us(lambda: B.bc_attn_step(cache, [L], None, None, q, k, v, off, B.BC_MASK_BLOCK_BIDIR, D ** -0.5,
+                                           out, ws, stream=stream), stream)
+
+    def unmask():
+        masked.copy_(masked0)
+        B.bc_unmask_select(lg, off, [B.BC_UNMASK_FULL, B.BC_UNMASK_SEMI, B.BC_UNMASK_SEMI], [1 << 30, 1, 1],
+                           p["threshold"], masked, tokens, None, nc, wsu, stream=stream)
+    u_us = graph_us(unmask, stream)
+    nbytes = 2 * Hkv * (L + 21) * D * 2 + 2 * 21 * Hq * D * 2
+    return {"attn_us": round(a_us, 3), "unmask_us_with_mask_copy": round(u_us, 3),
+            "step_us": round(a_us + u_us, 3), "attn_bytes": nbytes, "attn_TB_s": round(nbytes / a_us / 1e6, 4),
+            "masked_rows": int(m0.sum())}
+
+
 def legs(stream):
     """Secondary measurements on the other workloads of the pages' systems:
     the shared-prefix fork round at N = 4, 16, 64 rollouts (attention there
-    is MFMA-bound), the verify scan over N = 64 rollouts' logits (HBM-bound),
-    the large-block decode's attention at batch 16 (HBM-bound), the section
-    decode with scaffold rows inside its blocks under block and section
-    visibility, a pipelined-parallel decode of 625 tokens against the same decode without
-    overlap, and the duration of a minimal kernel as the launch floor."""
+    is MFMA-bound) with the verify scan over N = 64 rollouts' logits
+    (HBM-bound); the whole fork trajectory with speculative rounds per N and
+    draft agreement; the large-block decode per block size and batch with its
+    attention cold and warm; the tiny float32 step; one three-block pipelined
+    step; the section decode with scaffold rows inside its blocks under block
+    and section visibility; a pipelined-parallel decode of 625 tokens against
+    the same decode without overlap; and the duration of a minimal kernel as
+    the launch floor."""
     import torch
     from block_causal_attention_gqa_amd import binding as B
     from block_causal_attention_gqa_amd import decode, synth
@@ -518,38 +697,10 @@ def legs(stream):
         torch.cuda.empty_cache()
     out["fork_round"] = fork
 
-    # large-block decode attention at batch 16: 32q/8kv, D 128, prefixes
-    # 2048 .. 2288, one block of 32 rows per sequence
-    p = synth.PRESETS["large_block"]
-    S, R, Hq, Hkv, D = 16, 32, p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
-    cap = p["prefix"] + sum(p["blocks"])
-    lens = [p["prefix"] + 16 * s for s in range(S)]
-    (pk, pv), _ = synth.kv_cache(0, S, Hkv, cap, D, lens, "bf16")
-    (q, _), (k, _), (v, _) = synth.active_qkv(0, S, R, Hq, Hkv, D, "bf16", 0)
-    cache = B.KVCache(pk.to("cuda:0"), pv.to("cuda:0"))
-    q, k, v = q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0")
-    o = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device="cuda:0")
-    ws = torch.zeros(B.bc_attn_workspace_bytes(cache, None, (S, R, Hq, D), [0, R]), dtype=torch.uint8,
-                     device="cuda:0")
-    us = graph_us(lambda: B.bc_attn_step(cache, lens, None, None, q, k, v, [0, R], B.BC_MASK_BLOCK_BIDIR,
-                                         D ** -0.5, o, ws, stream=stream), stream)
-    nbytes = sum(attn_bytes_flops(L, R, Hq, Hkv, D)[0] for L in lens)
-    flops = sum(attn_bytes_flops(L, R, Hq, Hkv, D)[1] for L in lens)
-    out["large_block_b16_attn"] = {"attn_us": round(us, 3), "TB_s": round(nbytes / us / 1e6, 3),
-                                   "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                                   "TFLOP_s": round(flops / us / 1e6, 1), "bytes": nbytes}
-    # the same call for the first sequence alone (batch 1)
-    cache1 = B.KVCache(cache.k[:1].contiguous(), cache.v[:1].contiguous())
-    q1, k1, v1, o1 = q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), o[:1].contiguous()
-    ws1 = torch.zeros(B.bc_attn_workspace_bytes(cache1, None, (1, R, Hq, D), [0, R]), dtype=torch.uint8,
-                      device="cuda:0")
-    us1 = graph_us(lambda: B.bc_attn_step(cache1, lens[:1], None, None, q1, k1, v1, [0, R], B.BC_MASK_BLOCK_BIDIR,
-                                          D ** -0.5, o1, ws1, stream=stream), stream)
-    nb1, fl1 = attn_bytes_flops(lens[0], R, Hq, Hkv, D)
-    out["large_block_b1_attn"] = {"attn_us": round(us1, 3), "TB_s": round(nb1 / us1 / 1e6, 4),
-                                  "hbm_frac": round(nb1 / us1 / 1e3 / HBM_PEAK_GBS, 4),
-                                  "TFLOP_s": round(fl1 / us1 / 1e6, 1), "bytes": nb1}
-    del pk, pv, cache, ws, cache1, ws1
+    out["trajectory"] = trajectory_legs(stream)
+    out["large_block"] = large_block_legs(stream)
+    out["tiny_step"] = tiny_leg(stream)
+    out["pipelined_3x7"] = window_leg(stream)
     # the section decode with the sections' scaffold rows inside the blocks
     # (404 rows, 280 editable), block and section visibility, each decode
     # replayed whole as one graph like the headline
@@ -594,7 +745,7 @@ def legs(stream):
     return out
 
 
-def cpu_baseline(dec, args):
+def cpu_baseline(dec, args, timed_out):
     """The float64 oracle on the host cores: the whole section decode (same
     seeded inputs, 88 denoise steps: attention + unmask each, commit per
     block), repeated until about --cpu-seconds have passed, in decoded tokens
@@ -621,7 +772,7 @@ def cpu_baseline(dec, args):
     ref = OS.section_decode(k32[0], v32[0], dec.prefix, units, dec.blocks, lambda b, st: inputs[(b, st)],
                             dec.steps, dec.tau, np.ones(n, np.uint8), np.full(n, -1, np.int32), scale=dec.scale,
                             attend_all=False, trace=trace)
-    check = oracle_check(ref, trace, dec)
+    check = oracle_check(ref, trace, dec, timed_out)
     tokens, reps = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -641,12 +792,13 @@ def cpu_baseline(dec, args):
             "seconds": round(secs, 2)}, check
 
 
-def oracle_check(ref, trace, dec):
-    """The oracle decode's tokens against the GPU decode's, and the smallest
-    relative float64 margins of its decisions: |conf - tau| / conf over the
-    masked rows of every step, and (c_(k-1) - c_k) / c_(k-1) at every rank
-    cut (steps whose commit count is neither 0, all masked rows nor exactly
-    the rows above tau)."""
+def oracle_check(ref, trace, dec, timed_out):
+    """The oracle decode against the output of the last timed graph replay
+    (tokens, masks and the committed cache), and the smallest relative
+    float64 margins of its decisions: |conf - tau| / conf over the masked
+    rows of every step, and (c_(k-1) - c_k) / c_(k-1) at every rank cut
+    (steps whose commit count is neither 0, all masked rows nor exactly the
+    rows above tau)."""
     band = 2.0 ** -12
     tau = float(np.float32(dec.tau))
     thr, cut, n_cuts, inside = float("inf"), float("inf"), 0, 0
@@ -664,12 +816,11 @@ def oracle_check(ref, trace, dec):
             cut = min(cut, g)
             n_cuts += 1
             inside += g <= band
-    import torch
-    dec.run()                # a fresh GPU decode: the legs above reuse its buffers
-    torch.cuda.synchronize()
-    gpu_tokens = dec.tokens.cpu().numpy()
-    return {"tokens_match": bool(np.array_equal(gpu_tokens, ref["tokens"])),
-            "masked_match": bool(np.array_equal(dec.masked.cpu().numpy(), ref["masked"])),
+    return {"compared": "last timed graph replay",
+            "tokens_match": bool(np.array_equal(timed_out["tokens"], ref["tokens"])),
+            "masked_match": bool(np.array_equal(timed_out["masked"], ref["masked"])),
+            "cache_match": bool(np.array_equal(timed_out["cache_k"], ref["cache_k"])
+                                and np.array_equal(timed_out["cache_v"], ref["cache_v"])),
             "steps": len(trace), "rank_cuts": n_cuts,
             "min_threshold_margin_rel": thr, "min_rank_cut_gap_rel": cut if n_cuts else None,
             "band_rel": band, "decisions_inside_band": inside}

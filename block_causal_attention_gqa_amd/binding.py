@@ -36,6 +36,7 @@ BC_MAX_SEQ = 64
 BC_MAX_BLOCKS = 64
 BC_MAX_BLOCK_ROWS = 1024
 BC_MAX_SCAN_ROWS = 4096
+BC_ALL_SEQ = -1
 
 EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmask_workspace_bytes",
             "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
@@ -308,10 +309,14 @@ def bc_attn_step_static(prefix, prefix_len, priv, priv_len, q, k, v, blk_off, ma
 
 
 def bc_kv_commit(cache, length, seq, start, n_rows, blk_k, blk_v, stream=None, check=True):
-    """``length`` is a host int32 NumPy array [n_seq], updated in place."""
+    """``length`` is a host int32 NumPy array [n_seq], updated in place.
+    seq = BC_ALL_SEQ commits blk_k / blk_v [n_seq][Hkv][n_rows][D] to every
+    sequence."""
     if not (isinstance(length, np.ndarray) and length.dtype == np.int32 and length.flags.c_contiguous):
         raise ValueError("length must be a contiguous int32 NumPy array")
-    n = cache.n_kv_heads * int(n_rows) * cache.head_dim
+    if len(length) != cache.n_seq:
+        raise ValueError("length needs one entry per sequence")
+    n = cache.n_kv_heads * int(n_rows) * cache.head_dim * (cache.n_seq if seq == BC_ALL_SEQ else 1)
     kp = _dev(blk_k, "blk_k", cache.k.dtype, n)
     vp = _dev(blk_v, "blk_v", cache.k.dtype, n)
     cs = cache.struct()

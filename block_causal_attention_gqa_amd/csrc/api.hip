@@ -181,19 +181,25 @@ int bc_kv_commit(const bc_kv_cache* cache, int32_t* len, int32_t seq, int32_t st
   int st = check_cache(cache);
   if (st) return st;
   if (!len || !blk_k || !blk_v) return BC_ERR_ARG;
-  if (seq < 0 || seq >= cache->n_seq || n_rows < 1) return BC_ERR_ARG;
-  if (start != len[seq]) return BC_ERR_ORDER;
+  const bool all = seq == BC_ALL_SEQ;
+  if ((!all && (seq < 0 || seq >= cache->n_seq)) || n_rows < 1) return BC_ERR_ARG;
+  const int s0 = all ? 0 : seq, n_seq = all ? cache->n_seq : 1;
+  for (int s = s0; s < s0 + n_seq; ++s)
+    if (start != len[s]) return BC_ERR_ORDER;
   if ((long long)start + n_rows > cache->capacity) return BC_ERR_CAPACITY;
   const int D = cache->head_dim, Hkv = cache->n_kv_heads, eb = elem_bytes(cache->dtype);
   const long long head_stride = (long long)cache->capacity * D;
   const long long seq_stride = head_stride * Hkv;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  char* kdst = static_cast<char*>(cache->k) + seq * seq_stride * eb;
-  char* vdst = static_cast<char*>(cache->v) + seq * seq_stride * eb;
-  if (launch_commit(kdst, vdst, blk_k, blk_v, cache->dtype, Hkv, D, head_stride, start, n_rows, s) != hipSuccess)
+  // sequences are consecutive runs of Hkv heads at the same head stride, so
+  // a commit of every sequence is one copy over n_seq * Hkv heads
+  char* kdst = static_cast<char*>(cache->k) + s0 * seq_stride * eb;
+  char* vdst = static_cast<char*>(cache->v) + s0 * seq_stride * eb;
+  if (launch_commit(kdst, vdst, blk_k, blk_v, cache->dtype, n_seq * Hkv, D, head_stride, start, n_rows, strm) !=
+      hipSuccess)
     return BC_ERR_HIP;
-  len[seq] = start + n_rows;
+  for (int s = s0; s < s0 + n_seq; ++s) len[s] = start + n_rows;
   return BC_OK;
 }
 

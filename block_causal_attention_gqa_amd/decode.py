@@ -210,8 +210,8 @@ class SectionDecode:
                     self._hook("unmask", "post")
             q, k, v = self.qkv[blks[-1]][self.steps - 1]
             self._hook("commit", "pre")
-            for s in range(S):
-                B.bc_kv_commit(self.cache, length, s, int(length[s]), ur, k[s], v[s], stream=stream)
+            # every sequence has the same length: one commit of all of them
+            B.bc_kv_commit(self.cache, length, B.BC_ALL_SEQ, int(length[0]), ur, k, v, stream=stream)
             self._hook("commit", "post")
 
 
@@ -443,12 +443,20 @@ class ForkTrajectory:
         self.saved = {k: torch.zeros(N * Rmax, dtype=torch.float32, device=device) for k in ("draft", "verify")}
         self.trace, self.rounds = [], []
         self.result = None
+        # the synthetic model's per-round draws, kept once drawn (a decode
+        # repeated with the same agreement rate reads them from here)
+        self._targets, self._plant_idx = {}, {}
 
     def targets(self, b, r, s):
         """(verify argmax targets, drafts) [R_b] of rollout s in round r."""
-        R = self.blocks[b]
-        t = synth.round_targets(self.seed, self.V, R, 600 + b, r, s)
-        return t, synth.drafts_with_agreement(self.seed, t, self.p_agree, self.V, 600 + b, r, s)
+        key = (b, r, s, self.p_agree)
+        hit = self._targets.get(key)
+        if hit is None:
+            R = self.blocks[b]
+            t = synth.round_targets(self.seed, self.V, R, 600 + b, r, s)
+            hit = self._targets[key] = (t, synth.drafts_with_agreement(self.seed, t, self.p_agree, self.V,
+                                                                       600 + b, r, s))
+        return hit
 
     def host_logits(self, kind, b, r, active, base):
         """The round's float32 logits [len(active)][R_b][V] on the host, from
@@ -468,12 +476,20 @@ class ForkTrajectory:
 
     def _plant(self, b, r, active):
         R, V, n = self.blocks[b], self.V, len(active)
+        key = (b, r, tuple(active), self.p_agree)
+        flat_idx = self._plant_idx.get(key)
+        if flat_idx is None:
+            flat_idx = {}
+            for kind in ("draft", "verify"):
+                x = np.empty(n * R, np.int64)
+                for j, s in enumerate(active):
+                    t, d = self.targets(b, r, s)
+                    x[j * R:(j + 1) * R] = (j * R + np.arange(R)) * V + (t if kind == "verify" else d)
+                flat_idx[kind] = torch.from_numpy(x)
+            self._plant_idx[key] = flat_idx
         for kind in ("draft", "verify"):
             h = self.h_idx[kind]
-            for j, s in enumerate(active):
-                t, d = self.targets(b, r, s)
-                tok = t if kind == "verify" else d
-                h[j * R:(j + 1) * R] = torch.from_numpy((j * R + np.arange(R)) * V + tok.astype(np.int64))
+            h[: n * R] = flat_idx[kind]
             idx = self.d_idx[kind][: n * R]
             idx.copy_(h[: n * R], non_blocking=True)
             flat = self.base[kind]

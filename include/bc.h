@@ -111,9 +111,13 @@ typedef struct {
  * Copies blk_k / blk_v [n_kv_heads][n_rows][head_dim] (device, cache dtype)
  * into rows [start, start + n_rows) of sequence `seq` and sets
  * len[seq] = start + n_rows.  `len` is HOST [cache->n_seq], in/out.
- * Errors: BC_ERR_ORDER if start != len[seq]; BC_ERR_CAPACITY if
- * start + n_rows > capacity; BC_ERR_ARG for a bad seq, n_rows < 1 or null
- * pointers.  The copy is bit-exact. */
+ * With seq == BC_ALL_SEQ every sequence commits a block of n_rows at once
+ * (one launch): blk_k / blk_v are [n_seq][n_kv_heads][n_rows][head_dim] and
+ * every len[s] must equal start.
+ * Errors: BC_ERR_ORDER if start != len[seq] (any len[s] with BC_ALL_SEQ);
+ * BC_ERR_CAPACITY if start + n_rows > capacity; BC_ERR_ARG for a bad seq,
+ * n_rows < 1 or null pointers.  The copy is bit-exact. */
+#define BC_ALL_SEQ (-1)
 int bc_kv_commit(const bc_kv_cache *cache, int32_t *len, int32_t seq, int32_t start,
                  int32_t n_rows, const void *blk_k, const void *blk_v, void *stream);
 

@@ -136,6 +136,12 @@ def test_commit_validation(L):
     assert L.bc_kv_commit(ctypes.byref(c), ln, 0, 60, 1, 0, 1, None) == B.BC_ERR_ARG
     assert L.bc_kv_commit(ctypes.byref(_cache(D=80)), ln, 0, 60, 1, 1, 1, None) == B.BC_ERR_UNSUPPORTED
     assert ln[0] == 60
+    c2, ln2 = _cache(S=3, cap=64), _lens(10, 10, 11)
+    assert L.bc_kv_commit(ctypes.byref(c2), ln2, B.BC_ALL_SEQ, 10, 4, 1, 1, None) == B.BC_ERR_ORDER
+    assert L.bc_kv_commit(ctypes.byref(c2), ln2, -2, 10, 4, 1, 1, None) == B.BC_ERR_ARG
+    ln3 = _lens(62, 62, 62)
+    assert L.bc_kv_commit(ctypes.byref(c2), ln3, B.BC_ALL_SEQ, 62, 3, 1, 1, None) == B.BC_ERR_CAPACITY
+    assert list(ln2) == [10, 10, 11] and list(ln3) == [62, 62, 62]
 
 
 def test_unmask_validation(L):

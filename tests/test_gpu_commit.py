@@ -54,3 +54,31 @@ def test_order_and_capacity_errors():
     assert B.bc_kv_commit(cache, length, 0, 60, 5, big, big, check=False) == B.BC_ERR_CAPACITY
     assert B.bc_kv_commit(cache, length, 1, 60, 1, blk, blk, check=False) == B.BC_ERR_ARG
     assert list(length) == [60]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_commit_of_every_sequence_at_once(dtype, D):
+    # seq = BC_ALL_SEQ: one launch commits [S][Hkv][rows][D] to all S
+    # sequences, equal to S in-order single commits
+    S, Hkv, cap = 5, 3, 300
+    lens0 = [200] * S
+    (k_t, v_t), (k32, v32) = synth.kv_cache(14, S, Hkv, cap, D, lens0, dtype)
+    cache = B.KVCache(k_t.to(G.DEV), v_t.to(G.DEV))
+    length = np.array(lens0, np.int32)
+    ocache = OK.new_cache(k32, v32, lens0)
+    for i, rows in enumerate([32, 1, 17]):
+        bk = synth.normal(14, "commit_k", (S, Hkv, rows, D), i)
+        bv = synth.normal(14, "commit_v", (S, Hkv, rows, D), i)
+        bk_t, bk32 = synth.to_dtype(bk, dtype)
+        bv_t, bv32 = synth.to_dtype(bv, dtype)
+        B.bc_kv_commit(cache, length, B.BC_ALL_SEQ, int(length[0]), rows, bk_t.to(G.DEV), bv_t.to(G.DEV))
+        for s in range(S):
+            OK.commit(ocache, s, int(length[s]) - rows, bk32[s], bv32[s], capacity=cap)
+    torch.cuda.synchronize()
+    kw, vw = OK.as_padded(ocache, cap, np.float32)
+    assert list(length) == [250] * S
+    assert np.array_equal(cache.k.float().cpu().numpy(), kw) and np.array_equal(cache.v.float().cpu().numpy(), vw)
+    # unequal lengths: the batched commit is out of order for someone
+    length[2] += 1
+    blk = torch.zeros((S, Hkv, 1, D), dtype=k_t.dtype, device=G.DEV)
+    assert B.bc_kv_commit(cache, length, B.BC_ALL_SEQ, 250, 1, blk, blk, check=False) == B.BC_ERR_ORDER
