@@ -125,24 +125,33 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   const double slot_row_bytes = compact ? D * 2.0 + 16.0 : D * 4.0 + 8.0;
   const int groups = fork ? Hkv : S * Hkv;
   const int rows_group = fork ? S * R * group : R * group;
-  // Row tiles of 128 rows (4 waves x 32).  With few row tiles (small
-  // batch) the tiles halve to 64 rows: bf16 as 4 waves x 16 rows, which
-  // also halves each wave's per-tile dependency chain; fp32 as 2 waves x 32.
-  const bool small = groups * ((rows_group + 127) / 128) < 32;
+  int maxlen = 0;
+  for (int s = 0; s < prefix->n_seq; ++s) maxlen = std::max(maxlen, lengths[s]);
+  // K/V bytes of the prefix as streamed from HBM (a shared fork prefix once)
+  double kv = 0;
+  for (int s = 0; s < prefix->n_seq; ++s) kv += (double)lengths[s] * Hkv * D * 2.0 * elem_bytes(prefix->dtype);
+  // Row tiles of 128 rows (4 waves x 32), or of 64 rows: bf16 as 4 waves x
+  // 16 rows, which also halves each wave's per-tile dependency chain; fp32
+  // as 2 waves x 32.  The 128-row form needs two of its workgroups on a CU
+  // (one wave per SIMD cannot hide its own latencies), so when its prefix
+  // items would give each CU at most one -- few row tiles, or few splits --
+  // the 64-row form, with twice the items, is used.  Measured (call times):
+  // large-block batch 16 38.7 -> 36.8 us and batch 8 27.0 -> 25.1 us (256
+  // items with 128-row tiles); fork N = 16 29.4 -> 26.1 us (240); fork
+  // N = 32 / 48 / 64 (480 / 432 / 384 items) are faster with 128 rows.
+  bool small = groups * ((rows_group + 127) / 128) < 32;
+  int P = n_splits;
+  if (!small && prefix->dtype == BC_BF16) {
+    const int mt2 = (rows_group + 127) / 128;
+    const int P2 = P ? P : auto_splits(groups * mt2, maxlen, kv, S * R * Hq, slot_row_bytes, true);
+    small = (long long)groups * mt2 * P2 <= 256;
+  }
   if (prefix->dtype == BC_BF16) { p->waves = 4; p->cols = small ? 1 : 2; }
   else { p->waves = small ? 2 : 4; p->cols = 2; }
   const int tile_rows = p->waves * p->cols * 16;
   p->n_mt_prefix = (rows_group + tile_rows - 1) / tile_rows;
   p->n_mt_active = (R * group + tile_rows - 1) / tile_rows;
-  int maxlen = 0;
-  for (int s = 0; s < prefix->n_seq; ++s) maxlen = std::max(maxlen, lengths[s]);
-  int P = n_splits;
-  if (P == 0) {
-    // K/V bytes of the prefix as streamed from HBM (a shared fork prefix once)
-    double kv = 0;
-    for (int s = 0; s < prefix->n_seq; ++s) kv += (double)lengths[s] * Hkv * D * 2.0 * elem_bytes(prefix->dtype);
-    P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes, p->cols == 2);
-  }
+  if (P == 0) P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes, p->cols == 2);
   p->P = P;
   for (int s = 0; s < prefix->n_seq; ++s) {
     const int per = (lengths[s] + P - 1) / P;

@@ -422,7 +422,9 @@ class ForkTrajectory:
         self.accept_len = torch.zeros(N, dtype=torch.int32, device=device)
         self.bonus = torch.zeros(N, dtype=torch.int32, device=device)
         self.n_commit = torch.zeros(N, dtype=torch.int32, device=device)
-        self.last_k = torch.zeros((N, Hkv * Rmax * D), dtype=tdt, device=device)
+        # each rollout's K/V of its last verify pass in the current block,
+        # [N][Hkv][R_b][D] at the front of a flat buffer
+        self.last_k = torch.zeros(N * Hkv * Rmax * D, dtype=tdt, device=device)
         self.last_v = torch.zeros_like(self.last_k)
         ws = 0
         for R in set(self.blocks):
@@ -524,6 +526,8 @@ class ForkTrajectory:
             verified = np.full((N, R), -1, np.int32)
             active, compacted = list(range(N)), None
             pl = int(self.priv_len[0])
+            last_k = self.last_k[: N * Hkv * R * D].view(N, Hkv, R, D)
+            last_v = self.last_v[: N * Hkv * R * D].view(N, Hkv, R, D)
             r = 0
             while active:
                 n = len(active)
@@ -574,7 +578,7 @@ class ForkTrajectory:
                 drafts = self.h_drafts[: n * R].numpy().reshape(n, R)
                 self.trace.append(dict(block=b, round=r, active=list(active),
                                        first=[int(first[s]) for s in active], accept=acc, bonus=bon))
-                still = []
+                still, done_slot, done_seq = [], [], []
                 for j, s in enumerate(active):
                     f, a = int(first[s]), acc[j]
                     verified[s, f:f + a] = drafts[j, f:f + a]
@@ -584,19 +588,20 @@ class ForkTrajectory:
                     if first[s] < R:
                         still.append(s)
                     else:
-                        # the K/V of this (its last) verify pass are what it commits
-                        n_kv = Hkv * R * D
-                        self.last_k[s, :n_kv].view(Hkv, R, D).copy_(k[j])
-                        self.last_v[s, :n_kv].view(Hkv, R, D).copy_(v[j])
+                        done_slot.append(j)
+                        done_seq.append(s)
+                if done_seq:
+                    # the K/V of this (their last) verify pass are what they commit
+                    js = torch.tensor(done_slot, dtype=torch.int64, device=self.dev)
+                    ss = torch.tensor(done_seq, dtype=torch.int64, device=self.dev)
+                    last_k.index_copy_(0, ss, k.index_select(0, js))
+                    last_v.index_copy_(0, ss, v.index_select(0, js))
                 active = still
                 r += 1
             self.rounds.append(r)
             result[:, row0:row0 + R] = verified
-            n_kv = Hkv * R * D
-            for s in range(N):
-                B.bc_kv_commit(self.priv, self.priv_len, s, int(self.priv_len[s]), R,
-                               self.last_k[s, :n_kv].view(Hkv, R, D), self.last_v[s, :n_kv].view(Hkv, R, D),
-                               stream=stream)
+            # every rollout holds pl private rows: one commit of all of them
+            B.bc_kv_commit(self.priv, self.priv_len, B.BC_ALL_SEQ, pl, R, last_k, last_v, stream=stream)
             row0 += R
         self.result = result
         return result
