@@ -28,14 +28,33 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose=False):
-    """Compile and link libbc.so (always rebuilds).  Returns the library path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime, or None."""
+    root = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(root)) if os.path.isdir(root) else []:
+        p = os.path.join(root, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return None
+
+
+def build(verbose=False, asan=False, out=None):
+    """Compile and link libbc.so (always rebuilds).  Returns the library path.
+
+    asan=True instruments the host code only (argument validation, split
+    plan, scheduler) with AddressSanitizer; the device code is built as
+    usual.  Such a library is loaded with the runtime from asan_runtime()
+    preloaded.  ``out`` overrides the output path."""
+    lib = out or LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-result",
-           "-I", os.path.join(HERE, "..", "include"),
-           *sources(), "-o", tmp]
+           "-I", os.path.join(HERE, "..", "include")]
+    if asan:
+        cmd += ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                "-shared-libasan"]
+    cmd += [*sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -47,8 +66,8 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed (%d):\n%s" % (proc.returncode, out))
     if out.strip() and verbose:
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
