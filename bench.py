@@ -289,12 +289,14 @@ TRAFFIC_SUMMARY = "profiles/attn_partial_section_decode_traffic.md"
 def cache_states(stream, dec, call_args, masked_before, reps=20, replays=5):
     """Cold and warm call times at the bs1 shape: the attention call
     (partial + combine) and the unmask select of the first denoise step of
-    the first 32-row block.  One graph holds reps repetitions of [a 512 MiB
-    write, the call] (cold: the 256 MB MALL and the L2 hold none of the
-    call's data, and are full of dirty lines), another the same writes
-    alone; the call time is their difference / reps.  Warm: the same with a
-    GPU spin that touches no memory in place of the write (the call's data
-    stay where the previous call left them).  Median over the replays."""
+    the first 32-row block.  One graph holds reps repetitions of [a flush,
+    the call], another the same flushes alone; the call time is their
+    difference / reps.  Cold dirty: the flush writes 512 MiB (the 256 MB
+    MALL and the L2 hold none of the call's data and are full of dirty
+    lines); cold clean: the flush reads 512 MiB (clean lines).  Warm: the
+    same with a GPU spin that touches no memory in place of the flush (the
+    call's data stay where the previous call left them).  Median over the
+    replays."""
     import torch
     from block_causal_attention_gqa_amd import binding as B
     b = next(i for i, bs in enumerate(dec.blocks) if bs == 32)
@@ -303,7 +305,7 @@ def cache_states(stream, dec, call_args, masked_before, reps=20, replays=5):
     a_args, lg = call_args[i]
     masked, tokens = dec.masked[off: off + bs], dec.tokens[off: off + bs]
     saved = masked_before[i]
-    flush = torch.empty(128 << 20, dtype=torch.float32, device=dec.masked.device)   # 512 MiB
+    flush = make_flush(dec.masked.device)
 
     def attn():
         B.bc_attn_step(*a_args, stream=stream)
@@ -316,11 +318,11 @@ def cache_states(stream, dec, call_args, masked_before, reps=20, replays=5):
     def restore():
         masked.copy_(saved)
 
-    def pre(cold):
-        if cold:
-            flush.fill_(1.0)
-        else:
+    def pre(state):
+        if state == "warm":
             torch.cuda._sleep(100000)
+        else:
+            flush[state]()
 
     def graph_ms(body):
         g = torch.cuda.CUDAGraph()
@@ -342,18 +344,18 @@ def cache_states(stream, dec, call_args, masked_before, reps=20, replays=5):
 
     out = {"shape": "bs1, 32-row block over a %d-key prefix, vocab %d, %d masked rows"
                     % (int(a_args[1][0]), dec.V, int(saved.sum().item())),
-           "flush_bytes": flush.numel() * 4, "reps_per_graph": reps}
+           "flush_bytes": flush["bytes"], "reps_per_graph": reps}
     for name, fn, base in (("attn_step_us", attn, lambda: None), ("unmask_select_us", unmask, restore)):
         out[name] = {}
-        for state, cold in (("cold", True), ("warm", False)):
+        for state in ("cold_dirty", "cold_clean", "warm"):
             def with_call():
                 for _ in range(reps):
-                    pre(cold)
+                    pre(state.replace("cold_", ""))
                     fn()
 
             def without():
                 for _ in range(reps):
-                    pre(cold)
+                    pre(state.replace("cold_", ""))
                     base()
             out[name][state] = round((graph_ms(with_call) - graph_ms(without)) * 1e3 / reps, 3)
     masked.zero_()
@@ -482,12 +484,27 @@ def graph_us(fn, stream, reps=10, replays=5):
     return e0.elapsed_time(e1) * 1e3 / (replays * reps)
 
 
+def make_flush(device="cuda:0"):
+    """A 512 MiB buffer that evicts the 256 MB MALL and the L2s, and the
+    two ways of passing it: ("dirty") writing all of it, which leaves every
+    cache full of dirty lines whose write-back the next call pays for; and
+    ("clean") reading one float of every 128-byte line (an elementwise
+    kernel into a 16 MiB output), which leaves them full of clean lines."""
+    import torch
+    buf = torch.empty(128 << 20, dtype=torch.float32, device=device)
+    buf.fill_(1.0)
+    lines = buf.view(-1, 32)[:, 0]
+    small = torch.empty(lines.numel(), dtype=torch.float32, device=device)
+    return {"dirty": lambda: buf.fill_(1.0), "clean": lambda: torch.neg(lines, out=small), "bytes": buf.numel() * 4}
+
+
 def cold_warm_us(stream, fn, flush, reps=20, replays=5):
-    """(cold, warm) duration of one fn() on `stream`: one graph holds reps
-    repetitions of [pre, fn()], another the same pre alone, and the call time
-    is their difference / reps.  Cold: pre writes `flush` (>= 512 MiB), which
-    leaves the 256 MB MALL and the L2 holding none of the call's data; warm:
-    pre is a GPU spin that touches no memory.  Median over the replays."""
+    """(cold dirty, cold clean, warm) duration of one fn() on `stream`: one
+    graph holds reps repetitions of [pre, fn()], another the same pre alone,
+    and the call time is their difference / reps.  Cold: pre is one of the
+    flushes of make_flush(), after which the MALL and the L2 hold none of the
+    call's data; warm: pre is a GPU spin that touches no memory (the call's
+    data stay where the previous call left them).  Median over the replays."""
     import torch
 
     def graph_ms(body):
@@ -509,12 +526,12 @@ def cold_warm_us(stream, fn, flush, reps=20, replays=5):
         return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts]))
 
     res = []
-    for cold in (True, False):
+    for state in ("dirty", "clean", "warm"):
         def pre():
-            if cold:
-                flush.fill_(1.0)
-            else:
+            if state == "warm":
                 torch.cuda._sleep(100000)
+            else:
+                flush[state]()
 
         def with_call():
             for _ in range(reps):
@@ -570,7 +587,7 @@ def large_block_legs(stream):
     import torch
     from block_causal_attention_gqa_amd import binding as B
     from block_causal_attention_gqa_amd import decode, synth
-    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")     # 512 MiB
+    flush = make_flush()
     rows = []
     for S in (1, 16):
         for Bsz in synth.LARGE_BLOCK_SIZES:
@@ -588,13 +605,16 @@ def large_block_legs(stream):
                 B.bc_attn_step(dec.cache, lens, None, None, q, k, v, [0, Bsz], B.BC_MASK_BLOCK_BIDIR, dec.scale,
                                dec.out[Bsz], dec.ws_attn, stream=stream)
             b2b = graph_us(call, stream)
-            cold, warm = cold_warm_us(stream, call, flush)
+            dirty, clean, warm = cold_warm_us(stream, call, flush)
             nbytes, flops = (S * x for x in attn_bytes_flops(L, Bsz, dec.Hq, dec.Hkv, dec.D))
             rec["attn"] = {"prefix": L, "bytes": nbytes, "us_back_to_back": round(b2b, 3),
-                           "us_cold": round(cold, 3), "us_warm": round(warm, 3),
-                           "TB_s_back_to_back": round(nbytes / b2b / 1e6, 3), "TB_s_cold": round(nbytes / cold / 1e6, 3),
+                           "us_cold_clean": round(clean, 3), "us_cold_dirty": round(dirty, 3),
+                           "us_warm": round(warm, 3),
+                           "TB_s_back_to_back": round(nbytes / b2b / 1e6, 3),
+                           "TB_s_cold_clean": round(nbytes / clean / 1e6, 3),
+                           "TB_s_cold_dirty": round(nbytes / dirty / 1e6, 3),
                            "TB_s_warm": round(nbytes / warm / 1e6, 3),
-                           "hbm_frac_cold": round(nbytes / cold / 1e3 / HBM_PEAK_GBS, 4),
+                           "hbm_frac_cold_clean": round(nbytes / clean / 1e3 / HBM_PEAK_GBS, 4),
                            "TFLOP_s_back_to_back": round(flops / b2b / 1e6, 1)}
             rows.append(rec)
             del dec

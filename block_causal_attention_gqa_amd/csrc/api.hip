@@ -40,6 +40,7 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 // ------------------------------------------------------------ attention plan
 struct Plan {
   int waves, cols, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  int xmap, tile_rows, unit_tiles, n_units, units_per_xcd;
   bool compact;        // compact split partials (bf16 inputs, many rows)
   size_t o_bytes, ml_bytes, total_bytes;
 };
@@ -160,6 +161,23 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   p->n_slots = P + 1;
   p->n_prefix_items = groups * P * p->n_mt_prefix;
   p->n_items = p->n_prefix_items + S * Hkv * p->n_mt_active;
+  // Without a fork every row of a row tile gets its records from that tile's
+  // items, so the tile, its splits and the combine of its rows can share an
+  // XCD (measured: a kernel reading 6.8 MB that the previous kernel wrote
+  // on other XCDs took 3.4 us longer than reading what its own XCD wrote).
+  // With a fork the prefix row tiles span rollouts while the active items
+  // tile each rollout's rows, so the fork keeps the key-chunk mapping.  The
+  // placement (workgroup id mod 8) holds for workgroups dispatched while the
+  // GPU has room for them; with more workgroups than are resident at once
+  // (two per CU) the later ones land wherever a CU frees up, so larger grids
+  // keep the key-chunk mapping too (measured: large-block batch 16, 768
+  // workgroups, 36.6 -> 49.4 us with the aligned mapping; bs1, 208, 10.7 ->
+  // 9.8 us).
+  p->tile_rows = tile_rows;
+  p->unit_tiles = groups >= 8 ? p->n_mt_prefix : 1;
+  p->n_units = groups >= 8 ? groups : groups * p->n_mt_prefix;
+  p->units_per_xcd = (p->n_units + 7) / 8;
+  p->xmap = !fork && 8LL * p->units_per_xcd * p->unit_tiles * p->n_slots < 512;
   p->rows_total = S * R * Hq;
   p->o_bytes = align256((size_t)p->n_slots * p->rows_total * D * (compact ? 2 : 4));
   p->ml_bytes = align256((size_t)p->n_slots * p->rows_total * (compact ? 16 : 8));
@@ -315,6 +333,13 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   args->dv_mt_active = make_fastdiv(p.n_mt_active);
   args->dv_rows = make_fastdiv(args->R * args->group);
   args->dv_group = make_fastdiv(args->group);
+  args->xmap = p.xmap;
+  args->tile_rows = p.tile_rows;
+  args->unit_tiles = p.unit_tiles;
+  args->n_units = p.n_units;
+  args->units_per_xcd = p.units_per_xcd;
+  args->dv_slots = make_fastdiv(p.n_slots);
+  args->dv_unit_tiles = make_fastdiv(p.unit_tiles);
   return BC_OK;
 }
 

@@ -105,12 +105,35 @@ template <bool kBf16> constexpr int key_const_off(int t, int i) {
   return kBf16 ? 32 * (t >> 1) + 4 * (t & 1) + i : 16 * t + i;
 }
 
-// Logical item of this workgroup.  Workgroups are dispatched in block-id
-// order, so the (long) prefix items take the lowest ids and start first; the
-// short active items fill in behind them.  Within each class the XCD remap
-// keeps neighbouring items on one XCD.
+// Row tile (group * n_mt_prefix + mt) that local tile jl of XCD x holds
+// under the XCD-aligned mapping, or -1 past the last unit.
+__device__ inline int xmap_tile(const AttnArgs& a, int x, int jl) {
+  const int ju = fast_div(jl, a.dv_unit_tiles);
+  const int unit = x + 8 * ju;
+  if (unit >= a.n_units) return -1;
+  return unit * a.unit_tiles + (jl - ju * a.unit_tiles);
+}
+
+// Logical item of this workgroup, or -1 for a workgroup with none.
+// Key-chunk mapping (fork): workgroups are dispatched in block-id order, so
+// the (long) prefix items take the lowest ids and start first; the short
+// active items fill in behind them.  Within each class the XCD remap keeps
+// neighbouring items -- the row tiles of one key chunk -- on one XCD.
+// XCD-aligned mapping: workgroup 8 k + x is split k % n_slots of local row
+// tile k / n_slots of XCD x (slot P: the active keys).
 __device__ inline int item_of_block(const AttnArgs& a) {
   const int hw = blockIdx.x;
+  if (a.xmap) {
+    const int k = hw >> 3;
+    const int jl = fast_div(k, a.dv_slots);
+    const int slot = k - jl * a.n_slots;
+    const int rt = xmap_tile(a, hw & 7, jl);
+    if (rt < 0) return -1;
+    const int grp = fast_div(rt, a.dv_mt_prefix);
+    const int mt = rt - grp * a.n_mt_prefix;
+    if (slot < a.n_splits) return (grp * a.n_splits + slot) * a.n_mt_prefix + mt;
+    return a.n_prefix_items + grp * a.n_mt_active + mt;
+  }
   if (hw < a.n_prefix_items) return xcd_remap(hw, a.n_prefix_items);
   return a.n_prefix_items + xcd_remap(hw - a.n_prefix_items, a.n_items - a.n_prefix_items);
 }
@@ -128,6 +151,8 @@ __device__ inline void preload_item_args(const AttnArgs& a) {
   asm volatile("" ::"s"(a.dv_mt_prefix.mul), "s"(a.dv_mt_prefix.shift), "s"(a.dv_splits.mul),
                "s"(a.dv_splits.shift), "s"(a.dv_hkv.mul), "s"(a.dv_hkv.shift), "s"(a.dv_group.mul),
                "s"(a.dv_group.shift), "s"(a.chunk[0]), "s"(a.prefix_len[0]));
+  asm volatile("" ::"s"(a.xmap), "s"(a.n_slots), "s"(a.unit_tiles), "s"(a.n_units), "s"(a.dv_slots.mul),
+               "s"(a.dv_slots.shift), "s"(a.dv_unit_tiles.mul), "s"(a.dv_unit_tiles.shift));
 }
 
 // 16-byte chunk swizzles of the bf16 K and V tiles in LDS (row r of a tile,
@@ -443,7 +468,9 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   const int n = lane & 15, jj = lane >> 4;
 
   preload_item_args(a);
-  const Item<bf16_t> it = decode_item<bf16_t>(a, item_of_block(a));
+  const int item = item_of_block(a);
+  if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
+  const Item<bf16_t> it = decode_item<bf16_t>(a, item);
   bool valid[CT];
   int orow[CT], lim[CT];
   lane_rows<CT>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
@@ -801,7 +828,9 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, jj = lane >> 4;
 
-  const Item<float> it = decode_item<float>(a, item_of_block(a));
+  const int item = item_of_block(a);
+  if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
+  const Item<float> it = decode_item<float>(a, item);
   bool valid[2];
   int orow[2], lim[2];
   lane_rows<2>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
@@ -918,9 +947,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   const int t = threadIdx.x;
   // the fields every lane needs, loaded in one burst (as in the partial kernel;
   // measured: section decode +1.4%)
-  asm volatile("" ::"s"(a.rows_total), "s"(a.n_slots), "s"(a.ws_o), "s"(a.ws_ml), "s"(a.out));
+  asm volatile("" ::"s"(a.rows_total), "s"(a.n_slots), "s"(a.ws_o), "s"(a.ws_ml), "s"(a.out), "s"(a.xmap));
   const int sub = (t / LPR) % SW;
-  const int row = blockIdx.x * RPB + t / (LPR * SW);
+  int row;
+  bool live;
+  if (a.xmap) {
+    // workgroup 8 k + x: block k % comb_wpr of local row tile k / comb_wpr of
+    // XCD x, whose records that XCD's partial workgroups wrote
+    const int k = blockIdx.x >> 3;
+    const int jl = fast_div(k, a.dv_comb);
+    const int rt = xmap_tile(a, blockIdx.x & 7, jl);
+    const int grp = rt < 0 ? 0 : fast_div(rt, a.dv_mt_prefix);
+    const int m = (rt - grp * a.n_mt_prefix) * a.tile_rows + (k - jl * a.comb_wpr) * RPB + t / (LPR * SW);
+    live = rt >= 0 && m < a.R * a.group;
+    const int s = fast_div(grp, a.dv_hkv);
+    const int r = fast_div(m, a.dv_group);
+    row = live ? (s * a.R + r) * a.Hq + (grp - s * a.Hkv) * a.group + (m - r * a.group) : 0;
+  } else {
+    row = blockIdx.x * RPB + t / (LPR * SW);
+    live = row < a.rows_total;
+  }
   const int pos = (t % LPR) * VPL;          // record position of this lane's first value
   int dim[NV];
 #pragma unroll
@@ -928,7 +974,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
     const int q = pos + 4 * v;
     dim[v] = kCompact ? 32 * (q / 32) + 16 * ((q % 8) / 4) + 4 * ((q % 32) / 8) : q;
   }
-  const bool live = row < a.rows_total;
   float wm = kNegInf, wl = 0.f;
   f32x4 acc[NV];
 #pragma unroll
@@ -1021,36 +1066,52 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   }
 }
 
+// partial workgroups: one per item, or under the XCD-aligned mapping 8 per
+// (local row tile, slot) with padding
+inline int partial_grid(const AttnArgs& a) {
+  return a.xmap ? 8 * a.units_per_xcd * a.unit_tiles * a.n_slots : a.n_items;
+}
+
 template <int D>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.cols == 1)
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1>), dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 2>), dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 2>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
   if (a.waves == 2)
-    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 2>), dim3(a.n_items), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 2>), dim3(partial_grid(a)), dim3(128), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 4>), dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 4>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int SW, bool kCompact>
+hipError_t launch_combine_rows(const AttnArgs& a, hipStream_t stream) {
+  constexpr int rows_per_block = 256 / (D / (kCompact ? 8 : 4) * SW);
+  if (!a.xmap) {
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, kCompact>),
+                       dim3((a.rows_total + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  // a row tile's rows in whole workgroups (tile_rows is a multiple of the
+  // rows per workgroup)
+  AttnArgs b = a;
+  b.comb_wpr = a.tile_rows / rows_per_block;
+  b.dv_comb = make_fastdiv(b.comb_wpr);
+  hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, kCompact>),
+                     dim3(8 * a.units_per_xcd * a.unit_tiles * b.comb_wpr), dim3(256), 0, stream, b);
   return hipGetLastError();
 }
 
 template <typename T, int D, int SW>
 hipError_t launch_combine_sw(const AttnArgs& a, hipStream_t stream) {
-  if (sizeof(T) == 2 && a.compact) {
-    constexpr int rows_per_block = 256 / (D / 8 * SW);
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, sizeof(T) == 2>),
-                       dim3((a.rows_total + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream, a);
-  } else {
-    constexpr int rows_per_block = 256 / (D / 4 * SW);
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, SW, false>),
-                       dim3((a.rows_total + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
+  if (sizeof(T) == 2 && a.compact) return launch_combine_rows<T, D, SW, sizeof(T) == 2>(a, stream);
+  return launch_combine_rows<T, D, SW, false>(a, stream);
 }
 
 // slot groups per row: with few rows, enough that each group's slots are

@@ -72,6 +72,19 @@ struct AttnArgs {
   int priv_len[BC_MAX_SEQ];
   // n_mt_prefix, n_splits, Hkv, n_mt_active, R * group and group as FastDiv
   FastDiv dv_mt_prefix, dv_splits, dv_hkv, dv_mt_active, dv_rows, dv_group;
+  // XCD-aligned mapping (calls without a fork).  Workgroup h runs on XCD
+  // h % 8.  Row tiles (tile_rows rows, numbered group * n_mt_prefix + mt)
+  // are taken in units of unit_tiles consecutive tiles -- a whole (sequence,
+  // KV head) group when there are at least 8 groups, else one tile -- and
+  // unit u belongs to XCD u % 8: every split of its row tiles (partial
+  // workgroup 8 k + x, k = (local tile) * n_slots + slot) and the combine
+  // workgroups of their rows (8 k + x, k = (local tile) * comb_wpr + block)
+  // run there, so the combine reads records written through its own L2.
+  // Workgroups past the last unit exit at once.
+  int xmap;
+  int tile_rows, unit_tiles, n_units, units_per_xcd;
+  int comb_wpr;        // combine workgroups per row tile (set at launch)
+  FastDiv dv_slots, dv_unit_tiles, dv_comb;
 };
 
 hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream);
