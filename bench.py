@@ -50,6 +50,11 @@ def parse():
                     help="for profiler runs: issue the N = 64 fork round's verify scan (greedy, then sampled "
                          "with Gumbel noise) 10 times each and a 256 MiB device copy (the counters' "
                          "calibration), print one JSON line, exit")
+    ap.add_argument("--batch-pass", action="store_true",
+                    help="for profiler runs: issue the large-block attention call at batch 16 (32q/8kv, a "
+                         "32-row block over a 2176-key prefix) 10 times over 5 distinct caches (765 MB, more "
+                         "than the MALL holds) and a 256 MiB device copy (the counters' calibration), print one "
+                         "JSON line, exit")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the secondary measurements (fork round, batch-16 attention, verify scan)")
     return ap.parse_args()
@@ -81,6 +86,9 @@ def main():
         return
     if args.verify_pass:
         verify_pass()
+        return
+    if args.batch_pass:
+        batch_pass()
         return
     preset = synth.PRESETS["section"]
     t0 = time.time()
@@ -434,6 +442,38 @@ def verify_pass(N=64, reps=10):
     torch.cuda.synchronize()
     out["copy_bytes"] = src.numel() * 4
     print(json.dumps(out), flush=True)
+
+
+def batch_pass(S=16, L=2176, n_caches=5, reps=10):
+    """The large-block decode's attention call at batch 16 (32q/8kv heads,
+    head_dim 128, one 32-row block over a 2176-key prefix per sequence),
+    issued reps times in rotation over n_caches distinct seeded caches (so
+    no call finds its K/V in the MALL), after one warm call; then a 256 MiB
+    device-to-device copy whose FETCH_SIZE / WRITE_SIZE readings calibrate
+    the counters."""
+    import torch
+    from block_causal_attention_gqa_amd import binding as B
+    from block_causal_attention_gqa_amd import synth
+    dev = "cuda:0"
+    R, Hq, Hkv, D = 32, 32, 8, 128
+    caches = []
+    for i in range(n_caches):
+        (pk, pv), _ = synth.kv_cache(i, S, Hkv, L, D, [L] * S, "bf16")
+        caches.append(B.KVCache(pk.to(dev), pv.to(dev)))
+    (q, _), (k, _), (v, _) = synth.active_qkv(0, S, R, Hq, Hkv, D, "bf16", 0)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty((S, R, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(B.bc_attn_workspace_bytes(caches[0], None, (S, R, Hq, D), [0, R]), dtype=torch.uint8, device=dev)
+    for i in range(reps + 1):
+        B.bc_attn_step(caches[i % n_caches], [L] * S, None, None, q, k, v, [0, R], B.BC_MASK_BLOCK_BIDIR, D ** -0.5,
+                       o, ws)
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    nbytes = attn_bytes_flops(L, R, Hq, Hkv, D)[0] * S
+    print(json.dumps({"calls": reps + 1, "bytes_per_call": nbytes, "copy_bytes": src.numel() * 4}), flush=True)
 
 
 def pmc_pass(dec):
