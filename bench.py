@@ -212,6 +212,9 @@ def main():
     avg = {
         "attn_partial": per_launch_us(lambda: [B.bc_attn_partial(*a, stream=stream) for a, _ in call_args]),
         "attn_combine": per_launch_us(lambda: [B.bc_attn_combine(*a, stream=stream) for a, _ in call_args]),
+        # the whole call (partial, then combine) back to back: unlike the sum of
+        # the two above, it includes the combine reading partials just written
+        "attn_call": per_launch_us(lambda: [B.bc_attn_step(*a, stream=stream) for a, _ in call_args]),
         "vocab_scan": per_launch_us(lambda: [B.bc_vocab_scan(lg, m, True, dec.ws_unmask, stream=stream)
                                              for (_, lg), m in zip(call_args, masked_before)]),
     }
@@ -234,7 +237,7 @@ def main():
     scan_bytes = sum(4 * V * r for r in masked_rows)
     n_scan = len(masked_rows)
     scan_gbs = scan_bytes / n_scan / (avg["vocab_scan"] * 1e-6) / 1e9
-    tot = {k: v * n_attn for k, v in avg.items()}
+    tot = {k: v * n_attn for k, v in avg.items() if k != "attn_call"}
     dominant = max(("attn_partial", "vocab_scan"), key=tot.get)
     if dominant == "vocab_scan":
         roof = {"kernel": "scan_kernel (bc_vocab_scan: per-row max/argmax/exp-sum over the vocabulary)",
@@ -271,7 +274,9 @@ def main():
                    "mode": args.mode},
         "denoise_step_ms": round(ms_per_step / dec.denoise_steps, 5),
         "graph_vs_eager": graph_gain,
-        "attn": {"avg_us": round(attn_us, 3), "TB_s": round(attn_gbs / 1e3, 4),
+        "attn": {"avg_us": round(attn_us, 3), "call_us_back_to_back": round(avg["attn_call"], 3),
+                 "TB_s_call": round(attn_bytes / n_attn / avg["attn_call"] / 1e6, 4),
+                 "TB_s": round(attn_gbs / 1e3, 4),
                  "TFLOP_s": round(attn_tflops, 3), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(attn_tflops / BF16_PEAK_TFLOPS, 5),
                  "bytes_per_call": attn_bytes / n_attn, "flops_per_call": attn_flops / n_attn},
