@@ -269,21 +269,59 @@ __device__ void merge_rows(const ScanPartial* part, int n_chunks, int r0, int nr
   }
 }
 
-// float64 sum_v exp(l_v - mx) over one row by the whole workgroup.
-__device__ double row_sum_f64(const float* rowp, int vocab, float mx, double* red) {
+// sum_v exp(l_v - mx) over one row by the whole workgroup, independent of
+// the order of the terms: each float64 term t (in [0, 1]) is cut to
+// floor(t 2^100), held as three 34-bit limbs that add without carries (a
+// limb sum stays below 2^52 for any vocabulary under 2^18), and the total
+// is rounded once to float64.  Two rows whose logits are permutations of
+// each other therefore get the same sum, bit for bit.
+constexpr int kFixBits = 100;
+
+__device__ inline void add_term(double t, unsigned long long (&l)[3]) {
+  const double x = ldexp(t, kFixBits);                 // exact
+  const double h2 = floor(ldexp(x, -68));
+  const double r1 = x - ldexp(h2, 68);                 // exact: the low bits of x
+  const double h1 = floor(ldexp(r1, -34));
+  const double r0 = r1 - ldexp(h1, 34);                // exact
+  l[2] += (unsigned long long)h2;
+  l[1] += (unsigned long long)h1;
+  l[0] += (unsigned long long)r0;                      // r0 >= 0: truncation is floor
+}
+
+// (l0 + l1 2^34 + l2 2^68) 2^-100, rounded once to nearest (ties to even).
+__device__ inline double limbs_to_double(const unsigned long long (&l)[3]) {
+  const unsigned long long lo = l[0] + (l[1] << 34);
+  const unsigned long long hi = (l[1] >> 30) + (l[2] << 4) + (lo < l[0] ? 1ull : 0ull);
+  if (hi == 0) return ldexp((double)lo, -kFixBits);    // u64 -> f64 rounds once
+  const int sh = 64 - __builtin_clzll(hi);             // 1 .. 54: the total is below 2^118
+  unsigned long long top = (hi << (64 - sh)) | (lo >> sh);
+  top |= (lo & ((1ull << sh) - 1)) != 0 ? 1ull : 0ull; // sticky bit, far below the rounding bit
+  return ldexp((double)top, sh - kFixBits);
+}
+
+__device__ double row_sum_f64(const float* rowp, int vocab, float mx, unsigned long long* red) {
   const int tid = threadIdx.x;
   const double m = (double)mx;
-  double s = 0.0;
-  for (int v = tid; v < vocab; v += kScanThreads) s += exp((double)rowp[v] - m);
-  red[tid] = s;
-  __syncthreads();
-  for (int w = kScanThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+  unsigned long long l[3] = {0, 0, 0};
+  for (int v = tid; v < vocab; v += kScanThreads) add_term(exp((double)rowp[v] - m), l);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) l[k] += __shfl_xor(l[k], off, 64);
   }
-  const double total = red[0];
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) red[3 * (tid >> 6) + k] = l[k];
+  }
   __syncthreads();
-  return total;
+  unsigned long long t[3] = {0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) t[k] += red[3 * w + k];
+  }
+  __syncthreads();
+  return limbs_to_double(t);
 }
 
 // Workgroup reductions: wave shuffles, then one LDS slot per wave and a
@@ -328,7 +366,7 @@ struct SelectSmem {
   int rank[BC_MAX_BLOCK_ROWS];
   unsigned char st[BC_MAX_BLOCK_ROWS];
   unsigned long long key[64];        // one-wave path: rank keys of rows 0 .. 63
-  double red[kScanThreads];
+  unsigned long long red[3 * (kScanThreads / 64)];
   int cnt[2][kScanThreads / 64];
   double lohi[2][2 * (kScanThreads / 64)];
   int done;

@@ -14,7 +14,14 @@ What is computed (restated from the pages):
 
 Readings where the pages are silent or vague:
   * confidence = the largest softmax probability of the row at temperature 1,
-    i.e. 1 / sum_j exp(l_j - max_j l_j);
+    i.e. 1 / sum_j exp(l_j - max_j l_j).  The sum is taken exactly, so that it
+    does not depend on the order of the terms: each float64 term
+    exp(l_j - max) (in [0, 1]) is cut to a multiple of 2^-100, the multiples
+    are added as integers, and the total is rounded once to float64.  (Two
+    rows whose logits are permutations of each other then have equal
+    confidences, and their order is the row index, whatever order a sum runs
+    in.  The cut changes each term by less than 2^-100, the sum by less than
+    vocab * 2^-100.)
   * "exceeds" is a strict comparison, conf > tau, with tau the float32
     threshold promoted exactly to float64;
   * FULL commits k = min(|E|, max(|A|, ceil(|E| / n))) rows of the block's
@@ -30,10 +37,34 @@ logits; the sum of exponentials and the confidence are float64.  All
 selection decisions are taken on these float64 confidences.
 """
 
+import math
+
 import numpy as np
 
 MODE_SEMI = 0
 MODE_FULL = 1
+
+
+FIXED_BITS = 100   # the sum's terms are cut to multiples of 2^-FIXED_BITS
+
+
+def exact_sum(terms):
+    """sum(terms) for float64 terms in [0, 1], order-independent: the exact
+    integer sum of floor(t * 2^FIXED_BITS), rounded once to float64, times
+    2^-FIXED_BITS."""
+    t = np.asarray(terms, dtype=np.float64)
+    f, ex = np.frexp(t)                                  # t = f 2^ex, f in [0.5, 1) (0 for t = 0)
+    mant = (f * 2.0 ** 53).astype(np.uint64)             # t = mant 2^(ex - 53), mant < 2^53
+    shift = ex.astype(np.int64) + (FIXED_BITS - 53)      # floor(t 2^FIXED_BITS) = floor(mant 2^shift)
+    total = 0
+    for k in range(4):                                   # 32-bit limbs of the fixed-point value
+        r = 32 * k - shift                               # the limb holds bits r .. r + 31 of mant
+        down = np.right_shift(mant, np.clip(r, 0, 63).astype(np.uint64))
+        up = np.left_shift(mant, np.clip(-r, 0, 63).astype(np.uint64))
+        limb = np.where(r >= 0, down, up) & np.uint64(0xFFFFFFFF)
+        limb = np.where(r >= 64, np.uint64(0), limb)
+        total += int(limb.sum(dtype=np.uint64)) << (32 * k)
+    return math.ldexp(float(total), -FIXED_BITS)         # int -> float rounds to nearest even
 
 
 def row_confidence(row):
@@ -41,7 +72,7 @@ def row_confidence(row):
     row = np.asarray(row, dtype=np.float32)
     m = row.max()
     a = int(np.flatnonzero(row == m)[0])
-    s = float(np.exp(row.astype(np.float64) - np.float64(m)).sum())
+    s = exact_sum(np.exp(row.astype(np.float64) - np.float64(m)))
     return float(m), a, s, 1.0 / s
 
 

@@ -328,3 +328,33 @@ def test_vocabulary_past_one_merge_round():
     synth.plant_peaks(x, 93, 0.5, 14.0, 0)
     x[2, V - 1] = 40.0          # argmax in the last chunk
     compare(x, [0, 3, 6], [FULL, SEMI], [2, 1], 0.9, np.ones(6, np.uint8), np.zeros(6, np.int32))
+
+
+def test_permuted_rows_straddling_the_rank_cut():
+    # rows whose logits are permutations of one row have equal confidences
+    # by definition; the order in which a sum runs must not split them, so
+    # the cut takes the lowest row indexes among them.  Rows 1, 3, 4, 6 are
+    # one row permuted, 0 and 5 above them, 2 and 7 below; n sweeps the cut
+    # across the tied rows.  Then the same rows spread through a block of 64
+    # with random rows in between.
+    rng = np.random.default_rng(31)
+    for V in (4096, 151936):
+        base = (rng.standard_normal(V) * 2.0).astype(np.float32)
+        x = np.empty((8, V), np.float32)
+        for i in (1, 3, 4, 6):
+            x[i] = base[rng.permutation(V)]
+        for i, peak in ((0, 9.0), (5, 8.0)):
+            x[i] = rng.standard_normal(V).astype(np.float32) * 2.0
+            x[i][rng.integers(V)] += np.float32(peak)
+        for i in (2, 7):
+            x[i] = (rng.standard_normal(V) * 0.5).astype(np.float32)
+        for n in (1, 2, 3, 4):
+            gm, _ = compare(x, [0, 8], [FULL], [n], 0.999, np.ones(8, np.uint8), np.zeros(8, np.int32))
+        mk = np.ones(8, np.uint8)
+        mk[[0, 1]] = 0
+        compare(x, [0, 8], [FULL], [2], 0.999, mk, np.zeros(8, np.int32))
+        y = synth.logits(9, 64, V, 1.0, V)
+        at = rng.choice(64, 8, replace=False)
+        y[at] = x
+        for n in (13, 16, 22, 32):          # k = 5, 4, 3, 2: the tied rows rank 3rd to 6th
+            compare(y, [0, 64], [FULL], [n], 0.999, np.ones(64, np.uint8), np.zeros(64, np.int32))

@@ -176,3 +176,67 @@ def test_threshold_comparison_is_strict():
                                      np.ones(2, np.uint8), np.zeros(2, np.int32))
     assert conf[0] == 0.25 and conf[1] > 0.25
     assert list(mo) == [1, 0] and n[0] == 1
+
+
+def test_exact_sum_is_the_rounded_fixed_point_sum():
+    # the definition written out with rationals: sum of floor(t 2^100),
+    # divided by 2^100 and rounded once (Fraction -> float rounds to nearest)
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    cases = [np.exp(rng.standard_normal(n) * s) for n, s in ((1, 1), (7, 3), (64, 0.5), (300, 8))]
+    cases = [c / c.max() for c in cases]
+    cases += [np.array([1.0, 2.0 ** -100, 2.0 ** -101, 5e-324, 0.0]),
+              np.array([1.0, 2.0 ** -53, 2.0 ** -53]),
+              np.array([1.0, 2.0 ** -53, 2.0 ** -100])]
+    for t in cases:
+        want = float(Fraction(sum(math.floor(Fraction(v) * 2 ** 100) for v in t.tolist()), 2 ** 100))
+        assert U.exact_sum(t) == want
+        # within vocab * 2^-100 of the exactly rounded real sum: one ulp at most
+        assert abs(U.exact_sum(t) - math.fsum(t)) <= math.ulp(math.fsum(t))
+
+
+def test_exact_sum_rounds_ties_to_even():
+    # 1 + 2^-53 is halfway between 1 and the next double: ties to even gives 1;
+    # any further bit below breaks the tie upwards
+    assert U.exact_sum(np.array([1.0, 2.0 ** -53])) == 1.0
+    assert U.exact_sum(np.array([1.0, 2.0 ** -53, 2.0 ** -99])) == 1.0 + 2.0 ** -52
+    assert U.exact_sum(np.array([1.0, 2.0 ** -52, 2.0 ** -53])) == 1.0 + 2.0 ** -51
+
+
+def _permuted_rows(seed, vocab):
+    """8 rows over `vocab`: rows 1, 3, 4 and 6 are permutations of one
+    Gaussian row (tied confidences), rows 0 and 5 are more confident, rows 2
+    and 7 less."""
+    rng = np.random.default_rng(seed)
+    base = (rng.standard_normal(vocab) * 2.0).astype(np.float32)
+    rows = np.empty((8, vocab), np.float32)
+    for i in (1, 3, 4, 6):
+        rows[i] = base[rng.permutation(vocab)]
+    for i, peak in ((0, 9.0), (5, 8.0)):
+        rows[i] = rng.standard_normal(vocab).astype(np.float32) * 2.0
+        rows[i][rng.integers(vocab)] += np.float32(peak)
+    for i in (2, 7):
+        rows[i] = (rng.standard_normal(vocab) * 0.5).astype(np.float32)
+    return rows
+
+
+def test_permuted_rows_tie_exactly_and_split_by_row_index():
+    V = 4096
+    x = _permuted_rows(5, V)
+    conf = [U.row_confidence(r)[3] for r in x]
+    assert conf[1] == conf[3] == conf[4] == conf[6]
+    assert min(conf[0], conf[5]) > conf[1] > max(conf[2], conf[7])
+    # a plain float64 sum would not tie these rows: its value depends on the order
+    plain = {float(np.exp(r.astype(np.float64) - float(r.max())).sum()) for r in x[[1, 3, 4, 6]]}
+    assert len(plain) > 1
+    # fully-active block: k = ceil(8 / n) rows by (confidence, row index)
+    for n, want in ((3, {0, 5, 1}), (2, {0, 5, 1, 3}), (4, {0, 5}), (1, set(range(8)))):
+        m, tok, nc, _ = U.unmask_select(x, [0, 8], [U.MODE_FULL], [n], np.float32(0.999),
+                                        np.ones(8, np.uint8), np.full(8, -1, np.int32))
+        assert set(np.flatnonzero(m == 0)) == want, n
+        assert nc[0] == len(want)
+    # with rows 0 and 1 already committed the cut falls between rows 3 and 4
+    mk = np.ones(8, np.uint8)
+    mk[[0, 1]] = 0
+    m, _, nc, _ = U.unmask_select(x, [0, 8], [U.MODE_FULL], [2], np.float32(0.999), mk, np.full(8, -1, np.int32))
+    assert set(np.flatnonzero(m == 0)) == {0, 1, 5, 3, 4} and nc[0] == 3
