@@ -707,18 +707,33 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
     accumulate(odd ? v_st1 : v_st0, pb);
     if constexpr (CT > 1) {
       // Left alone, the scheduler issues the score MFMAs back to back and
-      // the exponentials after them.  Interleave them: per 16-key tile the
-      // four K operand reads, then each MFMA followed by three vector
-      // instructions (an MFMA occupies the matrix core for 16 cycles and
-      // the issue port for about 6; an exponential costs about three FMAs).
+      // the exponentials after them, and each operand read right before
+      // its MFMA, so every MFMA pair waits out an LDS round trip.  Instead:
+      // each score MFMA is followed by three vector instructions (an MFMA
+      // occupies the matrix core for 16 cycles and the issue port for
+      // about 6; an exponential costs about three FMAs); the K operand
+      // reads run one 16-key step ahead of their MFMAs; the PV MFMAs start
+      // with the four row-sum MFMAs (no LDS operand) behind the first V
+      // reads, and each later pair of V reads is issued two MFMA pairs
+      // ahead of its use.  (Measured at N = 64 rollouts: partial 55.5 ->
+      // 53.4 us; reads four steps ahead, or V reads further ahead, were no
+      // better.)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);       // K reads, steps 0 and 1
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
         }
+        if (t < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // K reads, step t + 2
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // the first two V read pairs
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);       // row-sum MFMAs
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // PV MFMA pair
+        if (u < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the V read pair two ahead
       }
       __builtin_amdgcn_s_setprio(0);
     }
