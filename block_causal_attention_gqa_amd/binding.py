@@ -24,6 +24,7 @@ BC_ERR_ORDER = -4
 BC_ERR_WORKSPACE = -5
 BC_ERR_HIP = -6
 BC_ERR_SCRATCH = -7
+BC_ERR_CALLBACK = -8
 BC_STATIC_SCRATCH_BYTES = 32 << 20
 
 BC_F32 = 0
@@ -42,7 +43,7 @@ EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmas
             "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
             "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide",
             "bc_pipeline_create", "bc_pipeline_destroy", "bc_pipeline_next", "bc_pipeline_report",
-            "bc_attn_step_static")
+            "bc_attn_step_static", "bc_pipeline_decode")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -57,6 +58,24 @@ class BcActive(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("blk_off", _c_i32p), ("n_blk", ctypes.c_int32), ("n_seq", ctypes.c_int32),
                 ("n_rows", ctypes.c_int32), ("n_q_heads", ctypes.c_int32)]
+
+
+class BcStepInputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("blk_k", ctypes.c_void_p * BC_MAX_BLOCKS),
+                ("blk_v", ctypes.c_void_p * BC_MAX_BLOCKS)]
+
+
+# bc_step_inputs_fn and bc_after_attn_fn
+STEP_INPUTS_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _c_i32p, _c_i32p,
+                                  ctypes.POINTER(BcStepInputs))
+AFTER_ATTN_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _c_i32p, _c_i32p,
+                                 ctypes.c_int32, ctypes.c_void_p)
+
+
+def pipe_trace_ints(window):
+    """BC_PIPE_TRACE_INTS(window): int32 entries per step of the native trace."""
+    return 2 + 4 * int(window)
 
 
 class BcError(RuntimeError):
@@ -114,6 +133,9 @@ def lib():
     L.bc_pipeline_next.restype = ctypes.c_int
     L.bc_pipeline_report.argtypes = [vp, _c_i32p, _c_i32p]
     L.bc_pipeline_report.restype = ctypes.c_int
+    L.bc_pipeline_decode.argtypes = [vp, cp, _c_i32p, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                                     vp, sz, vp, sz, STEP_INPUTS_FN, AFTER_ATTN_FN, vp, _c_i32p, i32, _c_i32p, vp]
+    L.bc_pipeline_decode.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -456,6 +478,66 @@ class Pipeline:
         if k < 0:
             raise BcError(k, "bc_pipeline_report")
         return self._done[:k].tolist()
+
+    def decode(self, cache, length, n_q_heads, vocab, scale, threshold, masked, tokens, out, ws_attn, ws_unmask,
+               inputs, after_attn=None, max_steps=4096, stream=None):
+        """bc_pipeline_decode: the whole step loop in the library.
+
+        inputs(step, active, local_steps) returns the step's BcStepInputs
+        (device pointers kept alive by the caller); after_attn(step, active,
+        local_steps, cache_len, out_ptr) is optional.  ``length`` is the host
+        int32 cache length [1], advanced in place.  Returns (n_steps, trace)
+        with the trace as a list of dicts (active, modes, n_commit,
+        committed), like a step-by-step decode records it."""
+        if not (isinstance(length, np.ndarray) and length.dtype == np.int32 and length.flags.c_contiguous):
+            raise ValueError("length must be a contiguous int32 NumPy array")
+        if cache.n_seq != 1 or len(length) != 1:
+            raise ValueError("the pipelined decode runs one sequence")
+        w = self.window
+        stride = pipe_trace_ints(w)
+        trace = np.full((int(max_steps), stride), -1, np.int32)
+        n_steps = np.zeros(1, np.int32)
+        errors = []
+
+        def _inputs(user, step, n, active, local, dst):
+            try:
+                src = inputs(int(step), [active[j] for j in range(n)], [local[j] for j in range(n)])
+                ctypes.memmove(dst, ctypes.addressof(src), ctypes.sizeof(BcStepInputs))
+                return 0
+            except BaseException as e:   # noqa: BLE001 -- re-raised after the call
+                errors.append(e)
+                return 1
+
+        def _after(user, step, n, active, local, cache_len, outp):
+            try:
+                after_attn(int(step), [active[j] for j in range(n)], [local[j] for j in range(n)], int(cache_len),
+                           outp)
+                return 0
+            except BaseException as e:   # noqa: BLE001
+                errors.append(e)
+                return 1
+
+        fi = STEP_INPUTS_FN(_inputs)
+        fa = AFTER_ATTN_FN(_after) if after_attn is not None else AFTER_ATTN_FN()
+        cs = cache.struct()
+        st = lib().bc_pipeline_decode(
+            self._h, ctypes.byref(cs), length.ctypes.data_as(_c_i32p), int(n_q_heads), int(vocab), float(scale),
+            float(threshold), _dev(masked, "masked", torch.uint8), _dev(tokens, "tokens", torch.int32),
+            _dev(out, "out"), _dev(ws_attn, "ws_attn"), ws_attn.numel() * ws_attn.element_size(),
+            _dev(ws_unmask, "ws_unmask"), ws_unmask.numel() * ws_unmask.element_size(), fi, fa, None,
+            trace.ctypes.data_as(_c_i32p), int(max_steps), n_steps.ctypes.data_as(_c_i32p), _stream(stream))
+        if errors:
+            raise errors[0]
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_decode")
+        k = int(n_steps[0])
+        rows = trace[:k].tolist()
+        recs = []
+        for r in rows:
+            n, nd = r[0], r[1]
+            recs.append(dict(active=r[2:2 + n], modes=["full" if m == BC_UNMASK_FULL else "semi" for m in r[2 + w:2 + w + n]],
+                             n_commit=r[2 + 2 * w:2 + 2 * w + n], committed=r[2 + 3 * w:2 + 3 * w + nd]))
+        return k, recs
 
     def close(self):
         h = getattr(self, "_h", None)

@@ -199,6 +199,7 @@ const char* bc_status_str(int status) {
     case BC_ERR_HIP: return "BC_ERR_HIP: the HIP runtime rejected a launch";
     case BC_ERR_SCRATCH:
       return "BC_ERR_SCRATCH: the call needs more than the static scratch (BC_STATIC_SCRATCH_BYTES) holds";
+    case BC_ERR_CALLBACK: return "BC_ERR_CALLBACK: a caller callback returned nonzero";
     default: return "unknown bc_status";
   }
 }

@@ -18,13 +18,7 @@
 #include <vector>
 
 #include "bc.h"
-
-struct bc_pipeline {
-  std::vector<int> size, revealed, local, state;
-  int committed = 0, window = 1, n_div = 1;
-  double add = 0.0, act = 0.0;
-  std::vector<int> plan;   // the planned step's blocks (empty: no plan)
-};
+#include "pipeline_state.h"
 
 namespace {
 

@@ -670,6 +670,7 @@ class PipelinedDecode:
         self.keep_inputs = False
         self._resident = {}
         self._calls = {}
+        self._native = {}
         # the commit counts come back through pinned host memory
         self.n_commit_host = torch.zeros(self.window, dtype=torch.int32).pin_memory()
 
@@ -714,6 +715,58 @@ class PipelinedDecode:
             return self._run(None, after_attn)
         with torch.cuda.stream(stream):
             return self._run(stream, after_attn)
+
+    def run_native(self, stream=None, after_attn=None):
+        """The same decode with the step loop inside the library
+        (``bc_pipeline_decode``): the schedule, the calls, the commits and
+        the read-back of each step's commit counts (polled in mapped host
+        memory, no stream synchronisation) run natively; Python only hands
+        over each step's model outputs through a callback.  Same arguments
+        and results as ``run``."""
+        if stream is None:
+            return self._run_native(None, after_attn)
+        with torch.cuda.stream(stream):
+            return self._run_native(stream, after_attn)
+
+    def _native_inputs(self, active, steps):
+        key = (tuple(active), tuple(steps))
+        hit = self._native.get(key)
+        if hit is not None:
+            return hit
+        q, k, v, lg, blk_kv = self._step_inputs(active, steps)
+        st = B.BcStepInputs()
+        st.q, st.k, st.v, st.logits = q.data_ptr(), k.data_ptr(), v.data_ptr(), lg.data_ptr()
+        for j, (bk, bv) in enumerate(blk_kv):
+            st.blk_k[j], st.blk_v[j] = bk.data_ptr(), bv.data_ptr()
+        hit = (st, (q, k, v, lg, blk_kv))
+        if self.keep_inputs:
+            self._native[key] = hit
+        return hit
+
+    def _run_native(self, stream, after_attn):
+        sched = B.Pipeline(self.blocks, self.window, self.add, self.act, self.n_div)
+        self.length[0] = self.prefix
+        self.masked.fill_(1)
+        self.tokens.fill_(-1)
+        live = []   # without resident inputs: the last steps' tensors stay referenced
+
+        def inputs(step, active, steps):
+            st, tensors = self._native_inputs(active, steps)
+            live.append(tensors)
+            del live[:-2]
+            return st
+
+        hook = None
+        if after_attn is not None:
+            def hook(step, active, steps, length, _out):
+                after_attn(step, active, steps, length, self.out[:, :sum(self.blocks[b] for b in active)])
+        try:
+            n, self.trace = sched.decode(self.cache, self.length, self.Hq, self.V, self.scale, self.tau, self.masked,
+                                         self.tokens, self.out, self.ws_attn, self.ws_unmask, inputs, hook,
+                                         max_steps=sum(self.blocks) + len(self.blocks), stream=stream)
+        finally:
+            sched.close()
+        return n
 
     def _run(self, stream, after_attn):
         sched = B.Pipeline(self.blocks, self.window, self.add, self.act, self.n_div)

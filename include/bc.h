@@ -55,7 +55,8 @@ typedef enum {
   BC_ERR_ORDER = -4,        /* a commit that does not start at the current length */
   BC_ERR_WORKSPACE = -5,    /* workspace missing or smaller than the query says */
   BC_ERR_HIP = -6,          /* the HIP runtime rejected a launch */
-  BC_ERR_SCRATCH = -7       /* the call needs more than the static scratch holds */
+  BC_ERR_SCRATCH = -7,      /* the call needs more than the static scratch holds */
+  BC_ERR_CALLBACK = -8      /* a caller callback returned nonzero */
 } bc_status;
 
 typedef enum { BC_F32 = 0, BC_BF16 = 1 } bc_dtype;
@@ -331,6 +332,66 @@ void bc_pipeline_destroy(bc_pipeline *p);
 int bc_pipeline_next(bc_pipeline *p, int32_t *active, int32_t *local_step, int32_t *mode,
                      int32_t *n_div, int32_t *blk_off, int32_t *row0);
 int bc_pipeline_report(bc_pipeline *p, const int32_t *n_commit, int32_t *done);
+
+/* ---- Pipelined parallel decoding, the whole step loop natively ----------
+ * The same schedule (Fast-dVLA reading notes, key design 4 and its complete
+ * example) with the per-step loop inside the library: plan, the model's
+ * outputs for the step (from the caller's callback), bc_attn_step over the
+ * active blocks' rows (BC_MASK_BLOCK_BIDIR), bc_unmask_select with the
+ * planned modes and n_div, the report, and bc_kv_commit of the blocks it
+ * returns, in order, each with the K/V of the step that completed it.  The
+ * unmask writes each step's commit counts into host memory that the library
+ * maps for the device (hipHostMalloc, mapped and coherent: one small buffer
+ * per device, allocated on first use and held until the process ends), and
+ * the host polls it instead of copying and synchronising the stream.
+ * Decodes on one device take turns on that buffer (a lock), so overlapping
+ * calls serialise.
+ *
+ * bc_step_inputs, filled by `inputs` for the planned step (device pointers,
+ * rows = the active blocks' rows concatenated, oldest block first):
+ *   q [1][rows][n_q_heads][head_dim]; k, v [1][n_kv_heads][rows][head_dim]
+ *   (the cache's dtype); logits [rows][vocab] float32; blk_k[j], blk_v[j]
+ *   [n_kv_heads][block rows][head_dim]: active block j's own K/V, appended to
+ *   the cache if the block completes at this step.  They must stay valid
+ *   until the step's work has run (the next callback, or the return).
+ * inputs(user, step, n, active[n], local_step[n], in): returns 0, or nonzero
+ *   to stop the decode (then BC_ERR_CALLBACK).
+ * after_attn(user, step, n, active[n], local_step[n], cache_len, out): NULL,
+ *   or called once the step's attention call is enqueued on `stream` (it may
+ *   synchronise it to read `out`); nonzero stops the decode as above.
+ *
+ *   p        a schedule from bc_pipeline_create; the loop runs from its
+ *            current state until every block is committed.
+ *   cache    n_seq == 1; cache_len HOST [1], in/out, advanced by the commits.
+ *   masked, tokens  device [sum of block sizes] uint8 / int32, in/out (all
+ *            blocks' rows concatenated, as bc_pipeline_next's row0 counts).
+ *   out      device [widest step's rows][n_q_heads][head_dim], cache dtype.
+ *   ws_attn / ws_unmask  workspaces for the widest step (bc_attn_workspace_bytes
+ *            and bc_unmask_workspace_bytes of that step's shapes).
+ *   trace    HOST [max_steps][BC_PIPE_TRACE_INTS(window)] or NULL: per step
+ *            n, n_done, active[window], mode[window], n_commit[window],
+ *            done[window] (entries past n or n_done are -1).
+ *   *n_steps the number of steps run.
+ * Errors: BC_ERR_ARG (pointers, cache->n_seq != 1, max_steps < 0);
+ * BC_ERR_CAPACITY when the decode needs more than max_steps steps (trace
+ * given); BC_ERR_CALLBACK; any error of the calls above, returned as is
+ * (the schedule and the buffers are then left where the failing step
+ * stopped). */
+#define BC_PIPE_TRACE_INTS(window) (2 + 4 * (window))
+typedef struct {
+  const void *q, *k, *v;
+  const float *logits;
+  const void *blk_k[BC_MAX_BLOCKS], *blk_v[BC_MAX_BLOCKS];
+} bc_step_inputs;
+typedef int (*bc_step_inputs_fn)(void *user, int32_t step, int32_t n_active, const int32_t *active,
+                                 const int32_t *local_step, bc_step_inputs *in);
+typedef int (*bc_after_attn_fn)(void *user, int32_t step, int32_t n_active, const int32_t *active,
+                                const int32_t *local_step, int32_t cache_len, void *out);
+int bc_pipeline_decode(bc_pipeline *p, const bc_kv_cache *cache, int32_t *cache_len, int32_t n_q_heads,
+                       int32_t vocab, float scale, float threshold, uint8_t *masked, int32_t *tokens,
+                       void *out, void *ws_attn, size_t ws_attn_bytes, void *ws_unmask, size_t ws_unmask_bytes,
+                       bc_step_inputs_fn inputs, bc_after_attn_fn after_attn, void *user,
+                       int32_t *trace, int32_t max_steps, int32_t *n_steps, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Attention without allocation or workspace, for callers that cannot

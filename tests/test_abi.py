@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert B.bc_status_str(st).startswith("BC_")
     assert B.bc_status_str(-99) == "unknown bc_status"
 
@@ -188,3 +188,35 @@ def test_partial_record_sizes_follow_the_row_count(L):
     for dtype, R, per_row in ((B.BC_BF16, 32, (512, 8)), (B.BC_BF16, 64, (256, 16)), (B.BC_F32, 64, (512, 8))):
         rows = R * 16
         assert nbytes(dtype, R) == rounded(3 * rows * per_row[0]) + rounded(3 * rows * per_row[1]), (dtype, R)
+
+
+def test_pipeline_decode_validation(L):
+    """bc_pipeline_decode checks its pointers, the one-sequence cache and the
+    step bound before it touches the device."""
+    h = ctypes.c_void_p()
+    sizes = (ctypes.c_int32 * 2)(4, 4)
+    assert L.bc_pipeline_create(sizes, 2, 2, 0.5, 0.9, 4, ctypes.byref(h)) == B.BC_OK
+    lens = _lens(0)
+    n = ctypes.c_int32(-5)
+    fi = B.STEP_INPUTS_FN(lambda *a: 0)
+    none_after = B.AFTER_ATTN_FN()
+
+    def call(p=h, cache=None, length=lens, inputs=fi, max_steps=16, masked=1, tokens=1, out=1, n_steps=True):
+        c = cache if cache is not None else _cache()
+        return L.bc_pipeline_decode(p, ctypes.byref(c), length, 16, 1024, 0.1, 0.9, masked, tokens, out, 1, 1 << 20,
+                                    1, 1 << 20, inputs, none_after, None, None, max_steps,
+                                    ctypes.byref(n) if n_steps else None, None)
+
+    try:
+        assert call(p=None) == B.BC_ERR_ARG
+        assert call(cache=_cache(S=2)) == B.BC_ERR_ARG
+        assert call(length=None) == B.BC_ERR_ARG
+        assert call(inputs=B.STEP_INPUTS_FN()) == B.BC_ERR_ARG
+        assert call(max_steps=-1) == B.BC_ERR_ARG
+        assert call(masked=None) == B.BC_ERR_ARG
+        assert call(tokens=None) == B.BC_ERR_ARG
+        assert call(out=None) == B.BC_ERR_ARG
+        assert call(n_steps=False) == B.BC_ERR_ARG
+        assert n.value == -5   # nothing written on a rejected call
+    finally:
+        L.bc_pipeline_destroy(h)

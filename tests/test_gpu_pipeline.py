@@ -34,16 +34,20 @@ def _qkv32(b, s):
     return q, k, v
 
 
+@pytest.mark.parametrize("native", [False, True], ids=["host-loop", "native-loop"])
 @pytest.mark.parametrize("add,act,tau,n_div,window", [
     (0.5, 0.9, 0.5, 4, 3),     # three blocks in flight, semi phase
     (0.25, 0.5, 0.5, 8, 3),    # early joins, slow full blocks
     (1.0, 1.0, 0.5, 4, 3),     # no overlap: plain block-by-block decoding
     (0.0, 0.0, 0.9, 2, 2),     # successor full once its predecessor reveals a row, window 2
 ])
-def test_pipelined_625_matches_oracle(add, act, tau, n_div, window):
+def test_pipelined_625_matches_oracle(add, act, tau, n_div, window, native):
+    """Both drivers: the step loop in Python over prepared calls, and the
+    library's own loop (bc_pipeline_decode)."""
     import torch
     from block_causal_attention_gqa_amd import decode
-    print("pipelined 625 add=%g act=%g tau=%g n=%d window=%d" % (add, act, tau, n_div, window), flush=True)
+    print("pipelined 625 add=%g act=%g tau=%g n=%d window=%d native=%d" % (add, act, tau, n_div, window, native),
+          flush=True)
     sizes = list(P["blocks"])
     want_tok, want_trace = OP.pipelined_decode(sizes, _logits_for, add, act, tau, n_div, window)
     n_steps = len(want_trace)
@@ -58,7 +62,7 @@ def test_pipelined_625_matches_oracle(add, act, tau, n_div, window):
             torch.cuda.synchronize()
             seen[k] = (active, steps, length, out.float().cpu().numpy())
 
-    assert pd.run(after_attn=after_attn) == n_steps
+    assert (pd.run_native if native else pd.run)(after_attn=after_attn) == n_steps
     torch.cuda.synchronize()
     for k, (got, want) in enumerate(zip(pd.trace, want_trace)):
         assert got == want, "step %d: %s != %s" % (k, got, want)
@@ -98,3 +102,34 @@ def test_pipelined_625_matches_oracle(add, act, tau, n_div, window):
         assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), b
         row += n
     assert np.array_equal(kc[:, :P["prefix"]], pk[0, :, :P["prefix"]])
+
+
+def test_native_loop_stops_on_a_callback_error_and_runs_again():
+    """An exception raised while providing a step's inputs stops the native
+    loop (BC_ERR_CALLBACK inside, the exception itself outside); the device's
+    count buffer is released, so a second decode runs to the oracle's end."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 native loop: callback error, then a full decode", flush=True)
+    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV)
+    real = pd._native_inputs
+    calls = []
+
+    def failing(active, steps):
+        calls.append(1)
+        if len(calls) == 4:
+            raise KeyError("no inputs for this step")
+        return real(active, steps)
+
+    pd._native_inputs = failing
+    with pytest.raises(KeyError):
+        pd.run_native()
+    torch.cuda.synchronize()
+    assert len(calls) == 4
+    pd._native_inputs = real
+    sizes = list(P["blocks"])
+    want_tok, want_trace = OP.pipelined_decode(sizes, _logits_for, pd.add, pd.act, pd.tau, pd.n_div, pd.window)
+    assert pd.run_native() == len(want_trace)
+    torch.cuda.synchronize()
+    assert pd.trace == want_trace
+    assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok))
