@@ -783,15 +783,19 @@ def legs(stream):
     # step's commit counts decide the next step's blocks, so the host reads
     # them back every step and a decode is timed whole on the wall clock,
     # inputs resident; "sequential" is the same decode without overlap.
-    # Two drivers: the library's own step loop (bc_pipeline_decode, the
-    # counts polled in mapped host memory; the headline figures) and the
-    # step loop in Python over prepared calls ("host_loop")
+    # Three drivers: the schedule on the device (bc_pipeline_dev_*: every
+    # step is the model stand-in's copy of its seeded outputs, the attention,
+    # the unmask and the schedule kernel, replayed as graphs of 8 steps; the
+    # headline figures), the library's host-side step loop
+    # (bc_pipeline_decode, the counts polled in mapped host memory:
+    # "native_loop"), and the step loop in Python over prepared calls
+    # ("host_loop", run first: its trace bounds the staged model outputs)
     pip = {}
     for name, kw in (("pipelined", dict(add=0.5, act=0.9)), ("sequential", dict(add=1.0, act=1.0))):
         pd = decode.PipelinedDecode(seed=0, device="cuda:0", tau=0.5, n_div=4, window=3, **kw)
         pd.keep_inputs = True
         res = {}
-        for driver, fn in (("native", pd.run_native), ("host_loop", pd.run)):
+        for driver, fn in (("host_loop", pd.run), ("native_loop", pd.run_native), ("device", pd.run_device)):
             fn(stream)
             torch.cuda.synchronize()
             reps = 5
@@ -802,8 +806,8 @@ def legs(stream):
             ms = (time.perf_counter() - t0) * 1e3 / reps
             res[driver] = {"steps": n, "ms": round(ms, 3), "step_us": round(ms * 1e3 / n, 2),
                            "tok_s": round(sum(pd.blocks) / ms * 1e3, 1)}
-        pip[name] = dict(res["native"], max_active=max(len(st["active"]) for st in pd.trace),
-                         host_loop=res["host_loop"])
+        pip[name] = dict(res["device"], max_active=max(len(st["active"]) for st in pd.trace),
+                         native_loop=res["native_loop"], host_loop=res["host_loop"])
         del pd
     out["pipelined_625"] = pip
     # latency floors: a one-element fill kernel, and an in-place add of 256

@@ -43,7 +43,10 @@ EXPORTED = ("bc_kv_commit", "bc_attn_workspace_bytes", "bc_attn_step", "bc_unmas
             "bc_unmask_select", "bc_verify_workspace_bytes", "bc_spec_verify", "bc_spec_verify_sampled",
             "bc_status_str", "bc_attn_partial", "bc_attn_combine", "bc_vocab_scan", "bc_unmask_decide",
             "bc_pipeline_create", "bc_pipeline_destroy", "bc_pipeline_next", "bc_pipeline_report",
-            "bc_attn_step_static", "bc_pipeline_decode")
+            "bc_attn_step_static", "bc_pipeline_decode", "bc_pipeline_dev_create", "bc_pipeline_dev_destroy",
+            "bc_pipeline_dev_rows", "bc_pipeline_dev_plan", "bc_pipeline_dev_reset", "bc_pipeline_dev_step",
+            "bc_pipeline_dev_replay", "bc_pipeline_dev_status", "bc_pipeline_dev_trace",
+            "bc_pipeline_dev_read_plan")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -64,6 +67,17 @@ class BcStepInputs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("logits", ctypes.c_void_p), ("blk_k", ctypes.c_void_p * BC_MAX_BLOCKS),
                 ("blk_v", ctypes.c_void_p * BC_MAX_BLOCKS)]
+
+
+class BcDevPlan(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("rows", ctypes.c_int32), ("row0", ctypes.c_int32), ("len", ctypes.c_int32),
+                ("n_blk", ctypes.c_int32), ("blk_off", ctypes.c_int32 * (BC_MAX_BLOCKS + 2)),
+                ("active", ctypes.c_int32 * BC_MAX_BLOCKS), ("local_step", ctypes.c_int32 * BC_MAX_BLOCKS),
+                ("mode", ctypes.c_int32 * BC_MAX_BLOCKS), ("n_div", ctypes.c_int32 * BC_MAX_BLOCKS)]
+
+
+class BcStepBlock(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("logits", ctypes.c_void_p)]
 
 
 # bc_step_inputs_fn and bc_after_attn_fn
@@ -136,6 +150,28 @@ def lib():
     L.bc_pipeline_decode.argtypes = [vp, cp, _c_i32p, i32, i32, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                                      vp, sz, vp, sz, STEP_INPUTS_FN, AFTER_ATTN_FN, vp, _c_i32p, i32, _c_i32p, vp]
     L.bc_pipeline_decode.restype = ctypes.c_int
+    L.bc_pipeline_dev_create.argtypes = [_c_i32p, i32, i32, ctypes.c_double, ctypes.c_double, i32, cp, i32, i32, i32,
+                                         ctypes.c_float, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, i32,
+                                         ctypes.POINTER(ctypes.c_void_p)]
+    L.bc_pipeline_dev_create.restype = ctypes.c_int
+    L.bc_pipeline_dev_destroy.argtypes = [vp]
+    L.bc_pipeline_dev_destroy.restype = None
+    L.bc_pipeline_dev_rows.argtypes = [vp]
+    L.bc_pipeline_dev_rows.restype = ctypes.c_int
+    L.bc_pipeline_dev_plan.argtypes = [vp]
+    L.bc_pipeline_dev_plan.restype = ctypes.c_void_p
+    L.bc_pipeline_dev_reset.argtypes = [vp, vp]
+    L.bc_pipeline_dev_reset.restype = ctypes.c_int
+    L.bc_pipeline_dev_step.argtypes = [vp, vp]
+    L.bc_pipeline_dev_step.restype = ctypes.c_int
+    L.bc_pipeline_dev_replay.argtypes = [vp, vp, i32, vp]
+    L.bc_pipeline_dev_replay.restype = ctypes.c_int
+    L.bc_pipeline_dev_status.argtypes = [vp, _c_i32p, _c_i32p, _c_i32p, _c_i32p]
+    L.bc_pipeline_dev_status.restype = ctypes.c_int
+    L.bc_pipeline_dev_trace.argtypes = [vp, _c_i32p, i32]
+    L.bc_pipeline_dev_trace.restype = ctypes.c_int
+    L.bc_pipeline_dev_read_plan.argtypes = [vp, ctypes.POINTER(BcDevPlan)]
+    L.bc_pipeline_dev_read_plan.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -543,6 +579,91 @@ class Pipeline:
         h = getattr(self, "_h", None)
         if h is not None and h.value and _lib is not None:
             _lib.bc_pipeline_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+class DevicePipeline:
+    """The pipelined decode with the schedule on the device
+    (bc_pipeline_dev_*): the library's device state, workspaces and trace;
+    the caller's step buffers (R rows, R = ``rows``), cache and
+    masked / tokens.  ``step`` enqueues one step and reads nothing back, so
+    steps can be captured in a graph; ``status`` reads the mapped state once
+    the stream has run."""
+
+    def __init__(self, block_sizes, window, add, act, n_div, cache, prefix_len, n_q_heads, vocab, scale, threshold,
+                 masked, tokens, q, k, v, logits, out, max_steps):
+        sizes = np.ascontiguousarray(np.asarray(block_sizes, dtype=np.int32))
+        h = ctypes.c_void_p()
+        cs = cache.struct()
+        st = lib().bc_pipeline_dev_create(
+            sizes.ctypes.data_as(_c_i32p), len(sizes), int(window), float(add), float(act), int(n_div),
+            ctypes.byref(cs), int(prefix_len), int(n_q_heads), int(vocab), float(scale), float(threshold),
+            _dev(masked, "masked", torch.uint8), _dev(tokens, "tokens", torch.int32), _dev(q, "q"), _dev(k, "k"),
+            _dev(v, "v"), _dev(logits, "logits", torch.float32), _dev(out, "out"), int(max_steps), ctypes.byref(h))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_dev_create")
+        self._h = h
+        self.window = int(window)
+        self.max_steps = int(max_steps)
+        self.rows = int(lib().bc_pipeline_dev_rows(h))
+        self._keep = (cache, masked, tokens, q, k, v, logits, out)
+
+    def plan_ptr(self):
+        return int(lib().bc_pipeline_dev_plan(self._h))
+
+    def read_plan(self):
+        """The next step's plan, copied to the host (synchronous)."""
+        p = BcDevPlan()
+        st = lib().bc_pipeline_dev_read_plan(self._h, ctypes.byref(p))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_dev_read_plan")
+        return p
+
+    def reset(self, stream=None):
+        st = lib().bc_pipeline_dev_reset(self._h, _stream(stream))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_dev_reset")
+
+    def step(self, stream=None):
+        st = lib().bc_pipeline_dev_step(self._h, _stream(stream))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_dev_step")
+
+    def replay(self, table, max_local, stream=None):
+        """``table``: a device uint8 tensor holding BcStepBlock entries
+        [n_blocks][max_local]."""
+        st = lib().bc_pipeline_dev_replay(self._h, _dev(table, "table", torch.uint8), int(max_local),
+                                          _stream(stream))
+        if st != BC_OK:
+            raise BcError(st, "bc_pipeline_dev_replay")
+
+    def status(self):
+        """(finished, steps, cache length, error) after the enqueued work has run."""
+        vals = [ctypes.c_int32() for _ in range(4)]
+        lib().bc_pipeline_dev_status(self._h, *[ctypes.byref(x) for x in vals])
+        return tuple(int(x.value) for x in vals)
+
+    def trace(self):
+        """The steps run, as bc_pipeline_decode's trace records (synchronous)."""
+        w = self.window
+        buf = np.full((self.max_steps, pipe_trace_ints(w)), -1, np.int32)
+        k = lib().bc_pipeline_dev_trace(self._h, buf.ctypes.data_as(_c_i32p), self.max_steps)
+        if k < 0:
+            raise BcError(k, "bc_pipeline_dev_trace")
+        recs = []
+        for r in buf[:k].tolist():
+            n, nd = r[0], r[1]
+            recs.append(dict(active=r[2:2 + n], modes=["full" if m == BC_UNMASK_FULL else "semi" for m in r[2 + w:2 + w + n]],
+                             n_commit=r[2 + 2 * w:2 + 2 * w + n], committed=r[2 + 3 * w:2 + 3 * w + nd]))
+        return recs
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.bc_pipeline_dev_destroy(h)
         self._h = None
 
     def __del__(self):

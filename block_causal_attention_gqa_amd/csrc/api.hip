@@ -415,6 +415,23 @@ void fill_unmask(const float* logits, int32_t n_rows, int32_t vocab, const int32
 
 }  // namespace
 
+namespace bc {
+int prepare_attn_args(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_active* a, float scale,
+                      void* out, void* ws, size_t ws_bytes, AttnArgs* args) {
+  return prepare_attn(prefix, prefix_len, nullptr, nullptr, a, BC_MASK_BLOCK_BIDIR, scale, 0, out, ws, ws_bytes, args);
+}
+int prepare_unmask_args(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                        const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
+                        int32_t* n_commit, void* ws, size_t ws_bytes, UnmaskArgs* args) {
+  const int st = validate_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens,
+                                 n_commit, ws, ws_bytes);
+  if (st) return st;
+  fill_unmask(logits, n_rows, vocab, blk_off, n_blk, mode, n_div, threshold, masked, tokens, nullptr, n_commit, ws,
+              args);
+  return BC_OK;
+}
+}  // namespace bc
+
 extern "C" {
 
 int bc_attn_partial(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_kv_cache* priv,

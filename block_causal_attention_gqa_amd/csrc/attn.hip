@@ -203,7 +203,10 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
       it.rows_in_group = a.R * a.group;
     }
     const int key_begin = it.slot * a.chunk[ps];
-    const int key_end = min(a.prefix_len[ps], key_begin + a.chunk[ps]);
+    // (plan fields are the same for every lane; readfirstlane says so to the
+    // compiler, which cannot tell through a generic pointer)
+    const int plen = a.dyn ? __builtin_amdgcn_readfirstlane(a.dyn->len) : a.prefix_len[ps];
+    const int key_end = min(plen, key_begin + a.chunk[ps]);
     const long long off = ps * a.p_seq_stride + it.g * a.p_head_stride + (long long)key_begin * a.D;
     it.k0 = static_cast<const T*>(a.pk) + off;
     it.v0 = static_cast<const T*>(a.pv) + off;
@@ -254,8 +257,16 @@ __device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0,
     int l = r + 1;
     if (!a.causal) {
       l = a.R;
-      for (int b = 0; b < a.n_blk; ++b)
-        if (r < a.blk_off[b + 1]) { l = a.blk_off[b + 1]; break; }
+      if (a.dyn) {
+        const int nb = __builtin_amdgcn_readfirstlane(a.dyn->n_blk);
+        for (int b = 0; b < nb; ++b) {
+          const int e = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b + 1]);
+          if (r < e) { l = e; break; }
+        }
+      } else {
+        for (int b = 0; b < a.n_blk; ++b)
+          if (r < a.blk_off[b + 1]) { l = a.blk_off[b + 1]; break; }
+      }
     }
     lim[c] = l;
   }
@@ -468,6 +479,7 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   const int n = lane & 15, jj = lane >> 4;
 
   preload_item_args(a);
+  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
   const int item = item_of_block(a);
   if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
   const Item<bf16_t> it = decode_item<bf16_t>(a, item);
@@ -843,6 +855,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, jj = lane >> 4;
 
+  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
   const int item = item_of_block(a);
   if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
   const Item<float> it = decode_item<float>(a, item);
@@ -959,6 +972,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   constexpr int B = 4;
   __shared__ float red_m[SW > 1 ? 256 : 1], red_l[SW > 1 ? 256 : 1];
   __shared__ f32x4 red_o[NV][SW > 1 ? 256 : 1];
+  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
   const int t = threadIdx.x;
   // the fields every lane needs, loaded in one burst (as in the partial kernel;
   // measured: section decode +1.4%)

@@ -33,6 +33,11 @@ __device__ inline int fast_div(int n, FastDiv f) {
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 constexpr int kCompactRows = 1024;        // bf16 calls with at least this many output rows use compact partials
 
+// The next step of a device-resident pipelined decode (bc_dev_plan, see
+// include/bc.h), written by the schedule kernel and read by the step's kernels.
+using DevPlan = bc_dev_plan;
+struct UnmaskArgs;
+
 struct AttnArgs {
   const void* q;       // [S][R][Hq][D]
   void* out;           // [S][R][Hq][D]
@@ -85,7 +90,21 @@ struct AttnArgs {
   int tile_rows, unit_tiles, n_units, units_per_xcd;
   int comb_wpr;        // combine workgroups per row tile (set at launch)
   FastDiv dv_slots, dv_unit_tiles, dv_comb;
+  // Device-resident plan (one sequence, no fork) or null: the prefix length
+  // and the blocks come from it instead of prefix_len[0] / n_blk / blk_off;
+  // R stays the widest step's row count; a step with no active block does
+  // nothing.
+  const DevPlan* dyn;
 };
+
+// Kernel arguments of a block-bidirectional attention call without a fork,
+// and of an unmask call, validated and filled as bc_attn_step and
+// bc_unmask_select fill them (api.hip); BC_OK or an error.
+int prepare_attn_args(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_active* a, float scale,
+                      void* out, void* ws, size_t ws_bytes, AttnArgs* args);
+int prepare_unmask_args(const float* logits, int32_t n_rows, int32_t vocab, const int32_t* blk_off, int32_t n_blk,
+                        const int32_t* mode, const int32_t* n_div, float threshold, uint8_t* masked, int32_t* tokens,
+                        int32_t* n_commit, void* ws, size_t ws_bytes, UnmaskArgs* args);
 
 hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream);
@@ -115,12 +134,15 @@ struct UnmaskArgs {
   int blk_off[BC_MAX_BLOCKS + 1];
   int mode[BC_MAX_BLOCKS];
   int n_div[BC_MAX_BLOCKS];
+  // Device-resident plan or null: the blocks, modes and n come from it, and
+  // masked / tokens / conf are offset by its row0.
+  const DevPlan* dyn;
 };
 
 // row_mask: scan rows with row_mask[r] != 0 (all rows when null);
 // with_sum: also the exp-sum (unmask) besides max / argmax.
 hipError_t launch_scan(const float* logits, int n_rows, int vocab, const uint8_t* row_mask, bool with_sum,
-                       ScanPartial* part, hipStream_t stream);
+                       ScanPartial* part, hipStream_t stream, const DevPlan* dyn = nullptr);
 hipError_t launch_unmask_decide(const UnmaskArgs& a, hipStream_t stream);
 
 struct VerifyArgs {

@@ -212,11 +212,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
                                                              const uint8_t* __restrict__ row_mask,
                                                              const int* __restrict__ first, int n_lrows,
                                                              int m, const float* __restrict__ noise = nullptr,
-                                                             float inv_t = 1.f) {
+                                                             float inv_t = 1.f,
+                                                             const DevPlan* __restrict__ dyn = nullptr) {
   __shared__ Acc red[kScanThreads / 64];
   const int chunk = blockIdx.x, row = blockIdx.y;
   if constexpr (kMode == 0) {
-    if (row_mask && !row_mask[row]) return;
+    if (dyn) {   // device-resident plan: its rows only, flags at its row0
+      if (row >= __builtin_amdgcn_readfirstlane(dyn->rows) ||
+          !row_mask[__builtin_amdgcn_readfirstlane(dyn->row0) + row])
+        return;
+    } else if (row_mask && !row_mask[row]) {
+      return;
+    }
   } else {
     const int s = row / n_lrows, i = row - s * n_lrows;
     const int f = min(max(first[s], 0), m);
@@ -395,7 +402,7 @@ __device__ inline double readlane_f64(double v, int lane) {
 // inside the threshold band or the cut is not certain; the caller then
 // takes the workgroup-wide path, which refines.
 __device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, double tau, int mode_b, int div_b,
-                                SelectSmem& sm) {
+                                uint8_t* masked, int* tokens, float* conf, SelectSmem& sm) {
   const int i = threadIdx.x;
   const bool inE = i < nb && (sm.st[i] & kInE);
   const double c = inE ? sm.cf[i] : -__builtin_huge_val();
@@ -430,10 +437,10 @@ __device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, doub
     const int r = r0 + i;
     const bool take = how == 1 || (how == 2 && c > tau) || (how == 3 && rk < k);
     if (take) {
-      a.tokens[r] = sm.tok[i];
-      a.masked[r] = 0;
+      tokens[r] = sm.tok[i];
+      masked[r] = 0;
     }
-    if (a.conf) a.conf[r] = (float)c;
+    if (conf) conf[r] = (float)c;
   }
   if (i == 0) a.n_commit[b] = k;
   return true;
@@ -445,8 +452,25 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   __shared__ SelectSmem sm;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int r0 = a.blk_off[b];
-  const int nb = a.blk_off[b + 1] - r0;
+  // the block's rows and rule: from the arguments, or from a device-resident
+  // plan, whose flags and tokens sit at its row0 (blocks past its count idle)
+  int r0, nb, mode_b, div_b, ro = 0;
+  if (a.dyn) {   // (uniform values: readfirstlane tells the compiler)
+    if (b >= __builtin_amdgcn_readfirstlane(a.dyn->n)) return;
+    r0 = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b]);
+    nb = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b + 1]) - r0;
+    mode_b = __builtin_amdgcn_readfirstlane(a.dyn->mode[b]);
+    div_b = __builtin_amdgcn_readfirstlane(a.dyn->n_div[b]);
+    ro = __builtin_amdgcn_readfirstlane(a.dyn->row0);
+  } else {
+    r0 = a.blk_off[b];
+    nb = a.blk_off[b + 1] - r0;
+    mode_b = a.mode[b];
+    div_b = a.n_div[b];
+  }
+  uint8_t* const masked = a.masked + ro;
+  int* const tokens = a.tokens + ro;
+  float* const conf = a.conf ? a.conf + ro : nullptr;
   const double tau = (double)a.threshold;
   // The argument fields the merge and the decisions need, loaded in one
   // burst at kernel start: left to itself the compiler loads each next to
@@ -455,14 +479,13 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   // latency overlaps the merge.
   asm volatile("" ::"s"(a.masked), "s"(a.part), "s"(a.n_chunks), "s"(a.tokens), "s"(a.conf), "s"(a.n_commit),
                "s"(a.threshold));
-  const int mode_b = a.mode[b], div_b = a.n_div[b];
 
   // The masked flags go to LDS, then every row's chunk partials are merged
   // (the flag stores wait for their loads first; holding the flags in
   // registers across the merge to share one round of loads measured slower).
   // Partials of revealed rows were not written by the scan and are dropped
   // below.
-  for (int i = tid; i < nb; i += kScanThreads) sm.st[i] = a.masked[r0 + i] != 0 ? kInE : 0;
+  for (int i = tid; i < nb; i += kScanThreads) sm.st[i] = masked[r0 + i] != 0 ? kInE : 0;
   merge_rows(a.part, a.n_chunks, r0, nb, [](int) { return true; },
              [&](int i, const Acc& t) {
                sm.cf[i] = 1.0 / (double)t.s;
@@ -472,7 +495,7 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   __syncthreads();
   if (nb <= 64) {
     if (tid < 64) {
-      const bool ok = decide_one_wave(a, b, r0, nb, tau, mode_b, div_b, sm);
+      const bool ok = decide_one_wave(a, b, r0, nb, tau, mode_b, div_b, masked, tokens, conf, sm);
       if (tid == 0) sm.done = ok;
     }
     __syncthreads();
@@ -566,10 +589,10 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
     else if (how == 2) take = sm.cf[i] > tau;
     else if (how == 3) take = sm.rank[i] < k;
     if (take) {
-      a.tokens[r] = sm.tok[i];
-      a.masked[r] = 0;
+      tokens[r] = sm.tok[i];
+      masked[r] = 0;
     }
-    if (a.conf) a.conf[r] = (float)sm.cf[i];
+    if (conf) conf[r] = (float)sm.cf[i];
   }
   if (tid == 0) a.n_commit[b] = k;
 }
@@ -603,22 +626,22 @@ __global__ __launch_bounds__(kScanThreads) void verify_decide_kernel(const Verif
 }  // namespace
 
 hipError_t launch_scan(const float* logits, int n_rows, int vocab, const uint8_t* row_mask, bool with_sum,
-                       ScanPartial* part, hipStream_t stream) {
+                       ScanPartial* part, hipStream_t stream, const DevPlan* dyn) {
   const dim3 grid(scan_chunks(vocab), n_rows);
   const int nc = scan_chunks(vocab);
   const bool vec = vocab % 4 == 0;
   if (with_sum && vec)
     hipLaunchKernelGGL((scan_kernel<0, true, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0);
+                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
   else if (with_sum)
     hipLaunchKernelGGL((scan_kernel<0, true, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0);
+                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
   else if (vec)
     hipLaunchKernelGGL((scan_kernel<0, false, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0);
+                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
   else
     hipLaunchKernelGGL((scan_kernel<0, false, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0);
+                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
   return hipGetLastError();
 }
 

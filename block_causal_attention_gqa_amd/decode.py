@@ -671,6 +671,9 @@ class PipelinedDecode:
         self._resident = {}
         self._calls = {}
         self._native = {}
+        self._dev = None
+        self._dev_graph = None
+        self._dev_max_local = 0
         # the commit counts come back through pinned host memory
         self.n_commit_host = torch.zeros(self.window, dtype=torch.int32).pin_memory()
 
@@ -766,6 +769,126 @@ class PipelinedDecode:
                                          max_steps=sum(self.blocks) + len(self.blocks), stream=stream)
         finally:
             sched.close()
+        return n
+
+    def run_device(self, stream=None, max_local=None, steps_per_graph=8, after_step=None):
+        """The same decode with the schedule on the device
+        (``bc_pipeline_dev_*``): each step is the model's stand-in (a copy of
+        the planned blocks' seeded outputs into fixed step buffers), the
+        attention, the unmask and the schedule kernel, and no step reads
+        anything back.  Runs of ``steps_per_graph`` steps are captured once
+        in a graph and replayed, one replay queued ahead, until the schedule
+        reports the end (steps after it do nothing).  ``max_local`` bounds the local steps whose
+        outputs are staged (default: from the previous ``run``'s trace, one
+        more than any block's); a step past it stops the decode with an
+        error.  With ``after_step(k, active, local_steps, length, out)`` the
+        steps run one by one, without graphs, and the hook sees each step's
+        attention output.  Same results as ``run``, except that the
+        attention follows the widest step's split plan."""
+        own = stream is None
+        if own:   # graphs are not captured on the legacy default stream
+            if getattr(self, "_dev_stream", None) is None:
+                self._dev_stream = torch.cuda.Stream(device=self.dev)
+            stream = self._dev_stream
+            stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            n = self._run_device(stream, max_local, steps_per_graph, after_step)
+        if own:
+            torch.cuda.current_stream().wait_stream(stream)
+        return n
+
+    def _device_setup(self, max_local):
+        if max_local is None:
+            if not self.trace:
+                raise ValueError("max_local: run() first, or pass the bound")
+            max_local = 1 + max(sum(1 for st in self.trace if b in st["active"]) for b in range(len(self.blocks)))
+        if self._dev is not None and self._dev_max_local >= max_local:
+            return
+        self._dev = None
+        self._dev_graph = None
+        R = max(sum(self.blocks[i:i + self.window]) for i in range(len(self.blocks)))
+        dt = synth.torch_dtype(self.dtype)
+        self.step_q = torch.zeros((1, R, self.Hq, self.D), dtype=dt, device=self.dev)
+        self.step_k = torch.zeros((1, self.Hkv, R, self.D), dtype=dt, device=self.dev)
+        self.step_v = torch.zeros((1, self.Hkv, R, self.D), dtype=dt, device=self.dev)
+        self.step_logits = torch.zeros((R, self.V), dtype=torch.float32, device=self.dev)
+        self.step_out = torch.zeros((1, R, self.Hq, self.D), dtype=dt, device=self.dev)
+        # the seeded model outputs of every (block, local step) below the bound
+        nb = len(self.blocks)
+        entries = (B.BcStepBlock * (nb * max_local))()
+        staged = []
+        for b in range(nb):
+            for st in range(max_local):
+                (q, _), (k, _), (v, _) = self.qkv_for(b, st)
+                x = (q.to(self.dev).contiguous(), k.to(self.dev).contiguous(), v.to(self.dev).contiguous(),
+                     torch.from_numpy(self.logits_for(b, st)).to(self.dev))
+                staged.append(x)
+                e = entries[b * max_local + st]
+                e.q, e.k, e.v, e.logits = (t.data_ptr() for t in x)
+        self._dev_staged = staged
+        self._dev_table = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8).to(self.dev)
+        self._dev = B.DevicePipeline(self.blocks, self.window, self.add, self.act, self.n_div, self.cache, self.prefix,
+                                     self.Hq, self.V, self.scale, self.tau, self.masked, self.tokens, self.step_q,
+                                     self.step_k, self.step_v, self.step_logits, self.step_out,
+                                     sum(self.blocks) + nb)
+        self._dev_max_local = max_local
+
+    def _run_device(self, stream, max_local, steps_per_graph, after_step):
+        self._device_setup(max_local)
+        dev = self._dev
+        s = torch.cuda.current_stream()
+        self.masked.fill_(1)
+        self.tokens.fill_(-1)
+        dev.reset(s)
+        if after_step is None:
+            if self._dev_graph is None or self._dev_graph[1] != steps_per_graph:
+                s.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(steps_per_graph):
+                        dev.replay(self._dev_table, self._dev_max_local, s)
+                        dev.step(s)
+                self._dev_graph = (g, steps_per_graph)
+                # capture enqueued nothing: start again
+                self.masked.fill_(1)
+                self.tokens.fill_(-1)
+                dev.reset(s)
+            # one replay always queued behind the one being waited on, so
+            # the GPU never idles on the host's check; at most that one runs
+            # past the end, as steps that do nothing
+            g = self._dev_graph[0]
+            pending = []
+            for _ in range(2):
+                g.replay()
+                pending.append(torch.cuda.Event())
+                pending[-1].record(s)
+            while True:
+                pending.pop(0).synchronize()
+                if dev.status()[0]:
+                    break
+                g.replay()
+                pending.append(torch.cuda.Event())
+                pending[-1].record(s)
+            s.synchronize()
+            finished, n, length, err = dev.status()
+        else:
+            k = 0
+            while True:
+                plan = dev.read_plan()   # synchronises
+                if plan.n == 0:
+                    break
+                dev.replay(self._dev_table, self._dev_max_local, s)
+                dev.step(s)
+                s.synchronize()
+                rows = plan.rows
+                after_step(k, list(plan.active[:plan.n]), list(plan.local_step[:plan.n]), plan.len,
+                           self.step_out[:, :rows])
+                k += 1
+            finished, n, length, err = dev.status()
+        if err:
+            raise RuntimeError("device pipelined decode stopped: error %d" % err)
+        self.trace = dev.trace()
+        self.length[0] = length
         return n
 
     def _run(self, stream, after_attn):

@@ -393,6 +393,83 @@ int bc_pipeline_decode(bc_pipeline *p, const bc_kv_cache *cache, int32_t *cache_
                        bc_step_inputs_fn inputs, bc_after_attn_fn after_attn, void *user,
                        int32_t *trace, int32_t max_steps, int32_t *n_steps, void *stream);
 
+/* ---- Pipelined parallel decoding with the schedule on the device --------
+ * The same schedule and step as bc_pipeline_decode (Fast-dVLA reading notes,
+ * key design 4), with the state machine run by a one-workgroup kernel after
+ * each step's unmask: it takes the step's commit counts, appends the blocks
+ * the step completed to the cache (in order, with the step's K/V rows), and
+ * writes the next step's plan into device memory, where the next step's
+ * kernels -- and the caller's model -- read it.  No step needs the host, so
+ * runs of steps can be captured in one HIP graph and replayed; once every
+ * block is committed, further steps do nothing.  Results (tokens, masks,
+ * cache, per-step trace) are those of bc_pipeline_decode on the same model
+ * outputs; attention is within the tolerance of a different split plan.
+ *
+ * Step buffers, the caller's device memory, hold R rows (R =
+ * bc_pipeline_dev_rows: the widest step, the largest sum of `window`
+ * consecutive block sizes); the step's rows come first, in plan order:
+ *   q [R][n_q_heads][head_dim], k / v [n_kv_heads][R][head_dim] (cache dtype),
+ *   logits [R][vocab] float32, out [R][n_q_heads][head_dim] (cache dtype).
+ * Before each bc_pipeline_dev_step the caller's model writes the step's rows
+ * of q, k, v and logits, as the plan (bc_pipeline_dev_plan) lays them out;
+ * rows past plan->rows are never read for a result.
+ *
+ * bc_pipeline_dev_create: the schedule's parameters as bc_pipeline_create;
+ *   cache with n_seq == 1 and prefix_len committed rows; masked / tokens
+ *   device [sum of block sizes] (all blocks' rows); max_steps >= 1 bounds
+ *   the trace.  The library allocates its device state, workspaces and trace
+ *   (hipMalloc) and a small mapped host status, and owns them until
+ *   bc_pipeline_dev_destroy.  Errors: BC_ERR_ARG, BC_ERR_UNSUPPORTED (as
+ *   bc_attn_step / bc_unmask_select for the widest step), BC_ERR_HIP.
+ * bc_pipeline_dev_reset: enqueues the start of a decode (initial state, the
+ *   first plan); masked and tokens are the caller's to initialise.
+ * bc_pipeline_dev_step: enqueues one step: attention over the planned rows,
+ *   the unmask, the schedule kernel.  Nothing is read on the host.
+ * bc_pipeline_dev_replay: a stand-in for the model, for tests and replays of
+ *   recorded outputs: enqueues a copy of the planned blocks' rows from
+ *   table[block * max_local + local_step] (device array of bc_step_block:
+ *   q [size][n_q_heads][head_dim], k / v [n_kv_heads][size][head_dim],
+ *   logits [size][vocab]) into the step buffers.  A missing entry (local
+ *   step >= max_local or a null pointer) stops the decode with error 3.
+ * bc_pipeline_dev_status: the state after the enqueued work has run (the
+ *   caller synchronises first): finished (1 once every block is committed,
+ *   or on an error), the steps run, the cache length, and error (0; 1 a
+ *   commit count out of range; 2 more steps than max_steps; 3 a missing
+ *   replay input).
+ * bc_pipeline_dev_trace: copies the per-step trace (the layout of
+ *   bc_pipeline_decode's) of the steps run to the host, returns their count;
+ *   synchronous.
+ * bc_pipeline_dev_read_plan: copies the next step's plan to the host once
+ *   the device is idle (synchronous). */
+typedef struct {
+  int32_t n;        /* active blocks; 0 once every block is committed */
+  int32_t rows;     /* their rows: the step's rows */
+  int32_t row0;     /* first row of the first active block in masked / tokens */
+  int32_t len;      /* committed cache length the step's attention sees */
+  int32_t n_blk;    /* blocks of the attention: the active ones, then rows [rows, R) if any */
+  int32_t blk_off[BC_MAX_BLOCKS + 2];
+  int32_t active[BC_MAX_BLOCKS], local_step[BC_MAX_BLOCKS], mode[BC_MAX_BLOCKS], n_div[BC_MAX_BLOCKS];
+} bc_dev_plan;
+typedef struct {
+  const void *q, *k, *v;
+  const float *logits;
+} bc_step_block;
+typedef struct bc_pipeline_dev bc_pipeline_dev;
+int bc_pipeline_dev_create(const int32_t *block_sizes, int32_t n_blocks, int32_t window, double add, double act,
+                           int32_t n_div, const bc_kv_cache *cache, int32_t prefix_len, int32_t n_q_heads,
+                           int32_t vocab, float scale, float threshold, uint8_t *masked, int32_t *tokens, void *q,
+                           void *k, void *v, float *logits, void *out, int32_t max_steps, bc_pipeline_dev **dev);
+void bc_pipeline_dev_destroy(bc_pipeline_dev *dev);
+int bc_pipeline_dev_rows(const bc_pipeline_dev *dev);
+const bc_dev_plan *bc_pipeline_dev_plan(const bc_pipeline_dev *dev);
+int bc_pipeline_dev_reset(bc_pipeline_dev *dev, void *stream);
+int bc_pipeline_dev_step(bc_pipeline_dev *dev, void *stream);
+int bc_pipeline_dev_replay(bc_pipeline_dev *dev, const bc_step_block *table, int32_t max_local, void *stream);
+int bc_pipeline_dev_status(const bc_pipeline_dev *dev, int32_t *finished, int32_t *n_steps, int32_t *cache_len,
+                           int32_t *error);
+int bc_pipeline_dev_trace(const bc_pipeline_dev *dev, int32_t *trace, int32_t max_steps);
+int bc_pipeline_dev_read_plan(const bc_pipeline_dev *dev, bc_dev_plan *plan);
+
 /* ------------------------------------------------------------------------ */
 /* Attention without allocation or workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops

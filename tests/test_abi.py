@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     with open(os.path.join(ROOT, "include", "bc.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(bc_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void|bc_\w+)\s*\*?\s*(bc_\w+)\s*\(", text,
+                                 re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -220,3 +221,35 @@ def test_pipeline_decode_validation(L):
         assert n.value == -5   # nothing written on a rejected call
     finally:
         L.bc_pipeline_destroy(h)
+
+
+def test_device_pipeline_validation(L):
+    """bc_pipeline_dev_create rejects malformed schedules, caches and
+    buffers on the host; the other bc_pipeline_dev_* calls reject a null
+    handle."""
+    sizes = (ctypes.c_int32 * 3)(32, 32, 17)
+    out = ctypes.c_void_p()
+
+    def create(n_blocks=3, window=2, n_div=4, cache=None, prefix=16, masked=1, q=1, max_steps=100, vocab=1024):
+        c = cache if cache is not None else _cache(cap=512)
+        return L.bc_pipeline_dev_create(sizes, n_blocks, window, 0.5, 0.9, n_div, ctypes.byref(c), prefix, 16, vocab,
+                                        0.1, 0.9, masked, 1, q, 1, 1, 1, 1, max_steps, ctypes.byref(out))
+
+    assert create(n_blocks=0) == B.BC_ERR_ARG
+    assert create(window=0) == B.BC_ERR_ARG
+    assert create(n_div=0) == B.BC_ERR_ARG
+    assert create(cache=_cache(S=2, cap=512)) == B.BC_ERR_ARG
+    assert create(prefix=512 - 80) == B.BC_ERR_ARG        # the blocks would not fit
+    assert create(masked=None) == B.BC_ERR_ARG
+    assert create(q=None) == B.BC_ERR_ARG
+    assert create(max_steps=0) == B.BC_ERR_ARG
+    assert create(vocab=0) == B.BC_ERR_ARG
+    assert out.value is None
+    for f in (L.bc_pipeline_dev_reset, L.bc_pipeline_dev_step):
+        assert f(None, None) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_replay(None, 1, 1, None) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_status(None, None, None, None, None) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_trace(None, None, 0) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_read_plan(None, None) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_rows(None) == B.BC_ERR_ARG
+    assert L.bc_pipeline_dev_plan(None) is None

@@ -34,36 +34,29 @@ def _qkv32(b, s):
     return q, k, v
 
 
-@pytest.mark.parametrize("native", [False, True], ids=["host-loop", "native-loop"])
-@pytest.mark.parametrize("add,act,tau,n_div,window", [
+SETTINGS = [
     (0.5, 0.9, 0.5, 4, 3),     # three blocks in flight, semi phase
     (0.25, 0.5, 0.5, 8, 3),    # early joins, slow full blocks
     (1.0, 1.0, 0.5, 4, 3),     # no overlap: plain block-by-block decoding
     (0.0, 0.0, 0.9, 2, 2),     # successor full once its predecessor reveals a row, window 2
-])
-def test_pipelined_625_matches_oracle(add, act, tau, n_div, window, native):
-    """Both drivers: the step loop in Python over prepared calls, and the
-    library's own loop (bc_pipeline_decode)."""
-    import torch
-    from block_causal_attention_gqa_amd import decode
-    print("pipelined 625 add=%g act=%g tau=%g n=%d window=%d native=%d" % (add, act, tau, n_div, window, native),
-          flush=True)
-    sizes = list(P["blocks"])
-    want_tok, want_trace = OP.pipelined_decode(sizes, _logits_for, add, act, tau, n_div, window)
+]
+
+
+def _oracle(add, act, tau, n_div, window):
+    return OP.pipelined_decode(list(P["blocks"]), _logits_for, add, act, tau, n_div, window)
+
+
+def _sample_steps(want_trace):
     n_steps = len(want_trace)
     widest = max(range(n_steps), key=lambda k: len(want_trace[k]["active"]))
-    sample = sorted({0, widest, n_steps // 2, n_steps - 1})
+    return sorted({0, widest, n_steps // 2, n_steps - 1})
 
-    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV, add=add, act=act, tau=tau, n_div=n_div, window=window)
-    seen = {}
 
-    def after_attn(k, active, steps, length, out):
-        if k in sample:
-            torch.cuda.synchronize()
-            seen[k] = (active, steps, length, out.float().cpu().numpy())
-
-    assert (pd.run_native if native else pd.run)(after_attn=after_attn) == n_steps
-    torch.cuda.synchronize()
+def _check(pd, want_tok, want_trace, seen):
+    """Trace, tokens, sampled steps' attention and the final cache against
+    the oracle's decode."""
+    sizes = list(P["blocks"])
+    assert len(pd.trace) == len(want_trace)
     for k, (got, want) in enumerate(zip(pd.trace, want_trace)):
         assert got == want, "step %d: %s != %s" % (k, got, want)
     assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok))
@@ -76,6 +69,7 @@ def test_pipelined_625_matches_oracle(add, act, tau, n_div, window, native):
             last[b] = sum(1 for x in want_trace[:k + 1] if b in x["active"]) - 1
     (_, _), (pk, pv) = synth.kv_cache(SEED, 1, P["n_kv_heads"], pd.cap, P["head_dim"], [P["prefix"]], P["dtype"])
     D = P["head_dim"]
+    assert seen
     for k, (active, steps, length, got) in seen.items():
         done = [b for st in want_trace[:k] for b in st["committed"]]
         assert length == P["prefix"] + sum(sizes[b] for b in done)
@@ -102,6 +96,77 @@ def test_pipelined_625_matches_oracle(add, act, tau, n_div, window, native):
         assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), b
         row += n
     assert np.array_equal(kc[:, :P["prefix"]], pk[0, :, :P["prefix"]])
+
+
+@pytest.mark.parametrize("native", [False, True], ids=["host-loop", "native-loop"])
+@pytest.mark.parametrize("add,act,tau,n_div,window", SETTINGS)
+def test_pipelined_625_matches_oracle(add, act, tau, n_div, window, native):
+    """Both host-side drivers: the step loop in Python over prepared calls,
+    and the library's own loop (bc_pipeline_decode)."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 add=%g act=%g tau=%g n=%d window=%d native=%d" % (add, act, tau, n_div, window, native),
+          flush=True)
+    want_tok, want_trace = _oracle(add, act, tau, n_div, window)
+    sample = _sample_steps(want_trace)
+    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV, add=add, act=act, tau=tau, n_div=n_div, window=window)
+    seen = {}
+
+    def after_attn(k, active, steps, length, out):
+        if k in sample:
+            torch.cuda.synchronize()
+            seen[k] = (active, steps, length, out.float().cpu().numpy())
+
+    assert (pd.run_native if native else pd.run)(after_attn=after_attn) == len(want_trace)
+    torch.cuda.synchronize()
+    _check(pd, want_tok, want_trace, seen)
+
+
+@pytest.mark.parametrize("add,act,tau,n_div,window", SETTINGS)
+def test_device_schedule_matches_oracle(add, act, tau, n_div, window):
+    """The schedule on the device (bc_pipeline_dev_*): the decode replayed
+    as graphs of 16 steps until the schedule kernel reports the end, then
+    again step by step with every sampled step's attention read back; both
+    against the oracle."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 device schedule add=%g act=%g tau=%g n=%d window=%d" % (add, act, tau, n_div, window),
+          flush=True)
+    want_tok, want_trace = _oracle(add, act, tau, n_div, window)
+    max_local = 1 + max(sum(1 for st in want_trace if b in st["active"]) for b in range(len(P["blocks"])))
+    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV, add=add, act=act, tau=tau, n_div=n_div, window=window)
+    for rep in range(2):   # the second replays the captured graph from a reset state
+        assert pd.run_device(max_local=max_local) == len(want_trace)
+        torch.cuda.synchronize()
+        assert pd.trace == want_trace, "graph replay %d: trace" % rep
+        assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok))
+    sample = _sample_steps(want_trace)
+    seen = {}
+
+    def after_step(k, active, steps, length, out):
+        if k in sample:
+            seen[k] = (active, steps, length, out.float().cpu().numpy())
+
+    # step by step, over a fresh copy of the prefix (the graph runs appended to the cache)
+    (pk, pv), _ = synth.kv_cache(SEED, 1, P["n_kv_heads"], pd.cap, P["head_dim"], [P["prefix"]], P["dtype"])
+    pd.cache.k.copy_(pk.to(G.DEV))
+    pd.cache.v.copy_(pv.to(G.DEV))
+    assert pd.run_device(max_local=max_local, after_step=after_step) == len(want_trace)
+    torch.cuda.synchronize()
+    _check(pd, want_tok, want_trace, seen)
+
+
+def test_device_schedule_stops_at_a_missing_input():
+    """Model outputs staged for too few local steps: the replay marks the
+    decode stopped (error 3) instead of reading past its table, and the run
+    raises."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 device schedule: staged inputs too short", flush=True)
+    pd = decode.PipelinedDecode(seed=SEED, device=G.DEV)
+    with pytest.raises(RuntimeError, match="error 3"):
+        pd.run_device(max_local=1)
+    torch.cuda.synchronize()
 
 
 def test_native_loop_stops_on_a_callback_error_and_runs_again():
