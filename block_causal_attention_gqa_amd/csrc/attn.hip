@@ -183,7 +183,7 @@ struct Item {
   bool masked0;
 };
 
-template <typename T>
+template <typename T, bool kDyn>
 __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
   Item<T> it;
   it.k1 = it.v1 = nullptr;
@@ -205,7 +205,7 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
     const int key_begin = it.slot * a.chunk[ps];
     // (plan fields are the same for every lane; readfirstlane says so to the
     // compiler, which cannot tell through a generic pointer)
-    const int plen = a.dyn ? __builtin_amdgcn_readfirstlane(a.dyn->len) : a.prefix_len[ps];
+    const int plen = kDyn ? __builtin_amdgcn_readfirstlane(a.dyn->len) : a.prefix_len[ps];
     const int key_end = min(plen, key_begin + a.chunk[ps]);
     const long long off = ps * a.p_seq_stride + it.g * a.p_head_stride + (long long)key_begin * a.D;
     it.k0 = static_cast<const T*>(a.pk) + off;
@@ -243,7 +243,7 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
 
 // this lane's two query columns: validity, output row, and the end of the
 // active keys it may see
-template <int CT, typename T>
+template <int CT, bool kDyn, typename T>
 __device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0, int n, bool (&valid)[CT],
                                  int (&orow)[CT], int (&lim)[CT]) {
 #pragma unroll
@@ -257,7 +257,7 @@ __device__ inline void lane_rows(const AttnArgs& a, const Item<T>& it, int row0,
     int l = r + 1;
     if (!a.causal) {
       l = a.R;
-      if (a.dyn) {
+      if constexpr (kDyn) {
         const int nb = __builtin_amdgcn_readfirstlane(a.dyn->n_blk);
         for (int b = 0; b < nb; ++b) {
           const int e = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b + 1]);
@@ -459,7 +459,7 @@ __device__ inline void tile_barrier() {
 //   4. accumulates O^T += V(j)^T P(j)^T;
 //   5. waits for its loads and meets the other waves at one barrier.
 // Every load has a whole iteration to land.
-template <int D, int NW, int CT>
+template <int D, int NW, int CT, bool kDyn>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_partial_bf16_kernel(const AttnArgs a) {
   constexpr int KT = kAttnKeyTile;
@@ -479,13 +479,15 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   const int n = lane & 15, jj = lane >> 4;
 
   preload_item_args(a);
-  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
+  if constexpr (kDyn) {   // device-resident plan: nothing to do once the decode has finished
+    if (__builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;
+  }
   const int item = item_of_block(a);
   if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
-  const Item<bf16_t> it = decode_item<bf16_t>(a, item);
+  const Item<bf16_t> it = decode_item<bf16_t, kDyn>(a, item);
   bool valid[CT];
   int orow[CT], lim[CT];
-  lane_rows<CT>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
+  lane_rows<CT, kDyn>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
 
   // ---- Q^T operand, resident for the whole item.  The two-column-tile
   // form loads it into registers here; the one-column-tile form stages it
@@ -841,7 +843,7 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 // current tile is computed and written to LDS one iteration later.  Loads
 // past a segment's end are clamped to its last key: finite data that the
 // softmax gives probability 0.
-template <int D, int NW>
+template <int D, int NW, bool kDyn>
 __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KT = kAttnKeyTile;
@@ -855,13 +857,15 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_f32_kernel(const AttnArg
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, jj = lane >> 4;
 
-  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
+  if constexpr (kDyn) {   // device-resident plan: nothing to do once the decode has finished
+    if (__builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;
+  }
   const int item = item_of_block(a);
   if (item < 0) return;   // padding workgroup of the XCD-aligned mapping (uniform)
-  const Item<float> it = decode_item<float>(a, item);
+  const Item<float> it = decode_item<float, kDyn>(a, item);
   bool valid[2];
   int orow[2], lim[2];
-  lane_rows<2>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
+  lane_rows<2, kDyn>(a, it, it.mt * kTileRows + wave * kWaveRows, n, valid, orow, lim);
 
   const float* q = static_cast<const float*>(a.q);
   constexpr int QK = D / 4;
@@ -972,7 +976,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   constexpr int B = 4;
   __shared__ float red_m[SW > 1 ? 256 : 1], red_l[SW > 1 ? 256 : 1];
   __shared__ f32x4 red_o[NV][SW > 1 ? 256 : 1];
-  if (a.dyn && __builtin_amdgcn_readfirstlane(a.dyn->n) == 0) return;   // device-resident plan: the decode has finished
   const int t = threadIdx.x;
   // the fields every lane needs, loaded in one burst (as in the partial kernel;
   // measured: section decode +1.4%)
@@ -1101,22 +1104,31 @@ inline int partial_grid(const AttnArgs& a) {
   return a.xmap ? 8 * a.units_per_xcd * a.unit_tiles * a.n_slots : a.n_items;
 }
 
-template <int D>
+// kDyn: the device-resident plan's instantiations (a.dyn set); the ordinary
+// ones never look at it
+template <int D, bool kDyn>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.cols == 1)
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1, kDyn>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 2>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 2, kDyn>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool kDyn>
 hipError_t launch_partial_f32(const AttnArgs& a, hipStream_t stream) {
   if (a.waves == 2)
-    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 2>), dim3(partial_grid(a)), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 2, kDyn>), dim3(partial_grid(a)), dim3(128), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 4>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_f32_kernel<D, 4, kDyn>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool kDyn>
+hipError_t launch_partial(const AttnArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == BC_BF16)
+    return a.D == 128 ? launch_partial_bf16<128, kDyn>(a, stream) : launch_partial_bf16<64, kDyn>(a, stream);
+  return a.D == 128 ? launch_partial_f32<128, kDyn>(a, stream) : launch_partial_f32<64, kDyn>(a, stream);
 }
 
 template <typename T, int D, int SW, bool kCompact>
@@ -1161,8 +1173,7 @@ hipError_t launch_combine_typed(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream) {
-  if (dtype == BC_BF16) return a.D == 128 ? launch_partial_bf16<128>(a, stream) : launch_partial_bf16<64>(a, stream);
-  return a.D == 128 ? launch_partial_f32<128>(a, stream) : launch_partial_f32<64>(a, stream);
+  return a.dyn ? launch_partial<true>(a, dtype, stream) : launch_partial<false>(a, dtype, stream);
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream) {

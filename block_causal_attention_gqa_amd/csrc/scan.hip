@@ -206,7 +206,7 @@ __device__ void scan_chunk(const float* __restrict__ rowp, int vocab, int chunk,
 
 // mode 0: rows with row_mask[row] != 0 (all rows when row_mask is null);
 // mode 1: verify, row (s, i) with first[s] <= i <= min(m, n_lrows - 1).
-template <int kMode, bool kSum, bool kVec, bool kNoise = false>
+template <int kMode, bool kSum, bool kVec, bool kNoise = false, bool kDyn = false>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restrict__ logits, int vocab,
                                                              int n_chunks, ScanPartial* __restrict__ part,
                                                              const uint8_t* __restrict__ row_mask,
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float* __restr
   __shared__ Acc red[kScanThreads / 64];
   const int chunk = blockIdx.x, row = blockIdx.y;
   if constexpr (kMode == 0) {
-    if (dyn) {   // device-resident plan: its rows only, flags at its row0
+    if constexpr (kDyn) {   // device-resident plan: its rows only, flags at its row0
       if (row >= __builtin_amdgcn_readfirstlane(dyn->rows) ||
           !row_mask[__builtin_amdgcn_readfirstlane(dyn->row0) + row])
         return;
@@ -448,6 +448,7 @@ __device__ bool decide_one_wave(const UnmaskArgs& a, int b, int r0, int nb, doub
 
 // Decisions of block b, one workgroup.  Thread t owns rows t, t + 256, ...
 // after the merge, so only the few workgroup reductions need barriers.
+template <bool kDyn>
 __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const UnmaskArgs a) {
   __shared__ SelectSmem sm;
   const int tid = threadIdx.x;
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   // the block's rows and rule: from the arguments, or from a device-resident
   // plan, whose flags and tokens sit at its row0 (blocks past its count idle)
   int r0, nb, mode_b, div_b, ro = 0;
-  if (a.dyn) {   // (uniform values: readfirstlane tells the compiler)
+  if constexpr (kDyn) {   // (uniform values: readfirstlane tells the compiler)
     if (b >= __builtin_amdgcn_readfirstlane(a.dyn->n)) return;
     r0 = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b]);
     nb = __builtin_amdgcn_readfirstlane(a.dyn->blk_off[b + 1]) - r0;
@@ -465,12 +466,10 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   } else {
     r0 = a.blk_off[b];
     nb = a.blk_off[b + 1] - r0;
-    mode_b = a.mode[b];
-    div_b = a.n_div[b];
   }
-  uint8_t* const masked = a.masked + ro;
-  int* const tokens = a.tokens + ro;
-  float* const conf = a.conf ? a.conf + ro : nullptr;
+  uint8_t* const masked = kDyn ? a.masked + ro : a.masked;
+  int* const tokens = kDyn ? a.tokens + ro : a.tokens;
+  float* const conf = kDyn && a.conf ? a.conf + ro : a.conf;
   const double tau = (double)a.threshold;
   // The argument fields the merge and the decisions need, loaded in one
   // burst at kernel start: left to itself the compiler loads each next to
@@ -479,6 +478,10 @@ __global__ __launch_bounds__(kScanThreads) void unmask_decide_kernel(const Unmas
   // latency overlaps the merge.
   asm volatile("" ::"s"(a.masked), "s"(a.part), "s"(a.n_chunks), "s"(a.tokens), "s"(a.conf), "s"(a.n_commit),
                "s"(a.threshold));
+  if constexpr (!kDyn) {
+    mode_b = a.mode[b];
+    div_b = a.n_div[b];
+  }
 
   // The masked flags go to LDS, then every row's chunk partials are merged
   // (the flag stores wait for their loads first; holding the flags in
@@ -630,23 +633,35 @@ hipError_t launch_scan(const float* logits, int n_rows, int vocab, const uint8_t
   const dim3 grid(scan_chunks(vocab), n_rows);
   const int nc = scan_chunks(vocab);
   const bool vec = vocab % 4 == 0;
+  if (dyn) {   // the device-resident plan's instantiations (the unmask's scan)
+    if (vec)
+      hipLaunchKernelGGL((scan_kernel<0, true, true, false, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab,
+                         nc, part, row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+    else
+      hipLaunchKernelGGL((scan_kernel<0, true, false, false, true>), grid, dim3(kScanThreads), 0, stream, logits,
+                         vocab, nc, part, row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+    return hipGetLastError();
+  }
   if (with_sum && vec)
     hipLaunchKernelGGL((scan_kernel<0, true, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+                       row_mask, nullptr, 0, 0);
   else if (with_sum)
     hipLaunchKernelGGL((scan_kernel<0, true, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+                       row_mask, nullptr, 0, 0);
   else if (vec)
     hipLaunchKernelGGL((scan_kernel<0, false, true>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+                       row_mask, nullptr, 0, 0);
   else
     hipLaunchKernelGGL((scan_kernel<0, false, false>), grid, dim3(kScanThreads), 0, stream, logits, vocab, nc, part,
-                       row_mask, nullptr, 0, 0, nullptr, 1.f, dyn);
+                       row_mask, nullptr, 0, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_unmask_decide(const UnmaskArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(unmask_decide_kernel, dim3(a.n_blk), dim3(kScanThreads), 0, stream, a);
+  if (a.dyn)   // the device-resident plan's instantiation
+    hipLaunchKernelGGL(unmask_decide_kernel<true>, dim3(a.n_blk), dim3(kScanThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(unmask_decide_kernel<false>, dim3(a.n_blk), dim3(kScanThreads), 0, stream, a);
   return hipGetLastError();
 }
 
