@@ -461,17 +461,26 @@ def bc_spec_verify_sampled(logits, noise, inv_temperature, draft, fixed, first, 
     return st
 
 
-def bc_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=None, check=True):
+def _verify_args(logits, draft, fixed, first, accept_len, bonus, ws, stream):
     S, L, V = (int(x) for x in logits.shape)
     m = int(draft.shape[1])
-    st = lib().bc_spec_verify(
-        _dev(logits, "logits", torch.float32, S * L * V), S, L, V, _dev(draft, "draft", torch.int32, S * m), m,
-        _dev(fixed, "fixed", torch.uint8, S * m, allow_none=True), _dev(first, "first", torch.int32, S),
-        _dev(accept_len, "accept_len", torch.int32, S), _dev(bonus, "bonus", torch.int32, S),
-        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+    return (_dev(logits, "logits", torch.float32, S * L * V), S, L, V, _dev(draft, "draft", torch.int32, S * m), m,
+            _dev(fixed, "fixed", torch.uint8, S * m, allow_none=True), _dev(first, "first", torch.int32, S),
+            _dev(accept_len, "accept_len", torch.int32, S), _dev(bonus, "bonus", torch.int32, S),
+            _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream))
+
+
+def bc_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=None, check=True):
+    st = lib().bc_spec_verify(*_verify_args(logits, draft, fixed, first, accept_len, bonus, ws, stream))
     if check and st != BC_OK:
         raise BcError(st, "bc_spec_verify")
     return st
+
+
+def prepare_spec_verify(logits, draft, fixed, first, accept_len, bonus, ws, stream=None):
+    """bc_spec_verify as a Prepared call."""
+    return Prepared("bc_spec_verify", _verify_args(logits, draft, fixed, first, accept_len, bonus, ws, stream),
+                    (logits, draft, fixed, first, accept_len, bonus, ws))
 
 
 class Pipeline:

@@ -446,8 +446,15 @@ class ForkTrajectory:
         self.trace, self.rounds = [], []
         self.result = None
         # the synthetic model's per-round draws, kept once drawn (a decode
-        # repeated with the same agreement rate reads them from here)
+        # repeated with the same agreement rate reads them from here); the
+        # planted positions are kept on the device
         self._targets, self._plant_idx = {}, {}
+        # the round's library calls, marshalled once per (block, active
+        # rollouts, pool entry) and reissued; the private lengths are read
+        # from this host array at each call
+        self._calls = {}
+        self._pl = np.zeros(N, np.int32)
+        self._prefix_len = np.array([self.prefix], np.int32)
 
     def targets(self, b, r, s):
         """(verify argmax targets, drafts) [R_b] of rollout s in round r."""
@@ -487,20 +494,40 @@ class ForkTrajectory:
                 for j, s in enumerate(active):
                     t, d = self.targets(b, r, s)
                     x[j * R:(j + 1) * R] = (j * R + np.arange(R)) * V + (t if kind == "verify" else d)
-                flat_idx[kind] = torch.from_numpy(x)
+                flat_idx[kind] = torch.from_numpy(x).to(self.dev, non_blocking=False)
             self._plant_idx[key] = flat_idx
+        self._planted = flat_idx
         for kind in ("draft", "verify"):
-            h = self.h_idx[kind]
-            h[: n * R] = flat_idx[kind]
-            idx = self.d_idx[kind][: n * R]
-            idx.copy_(h[: n * R], non_blocking=True)
+            idx = flat_idx[kind]
             flat = self.base[kind]
             torch.index_select(flat, 0, idx, out=self.saved[kind][: n * R])
             flat.index_fill_(0, idx, float(self.peak))
 
     def _restore(self, n_rows):
         for kind in ("draft", "verify"):
-            self.base[kind].index_copy_(0, self.d_idx[kind][:n_rows], self.saved[kind][:n_rows])
+            self.base[kind].index_copy_(0, self._planted[kind], self.saved[kind][:n_rows])
+
+    def _round_calls(self, b, n, r, priv, masked, tokens, first_d, out):
+        """The round's four library calls for n active rollouts of block b,
+        marshalled on first use and kept."""
+        key = (b, n, r % self.pool)
+        hit = self._calls.get(key)
+        if hit is None:
+            R, V = self.blocks[b], self.V
+            qkv = [self.qkv[(b, r % self.pool, pass_id)] for pass_id in (0, 1)]
+            pl = self._pl[:n]
+            off = list(range(0, n * R + 1, R))
+            draft, verify = (B.prepare_attn_step(self.shared, self._prefix_len, priv, pl, *(x[:n] for x in qkv[i]),
+                                                 [0, R], mask, self.scale, out, self.ws_attn)
+                             for i, mask in ((0, B.BC_MASK_BLOCK_BIDIR), (1, B.BC_MASK_BLOCK_CAUSAL)))
+            dlg = self.base["draft"][: n * R * V].view(n * R, V)
+            argmax = B.prepare_unmask_select(dlg, off, [B.BC_UNMASK_SEMI] * n, [1] * n, 0.0, masked, tokens, None,
+                                             self.n_commit[:n], self.ws_unmask)
+            vlg = self.base["verify"][: n * R * V].view(n, R, V)
+            spec = B.prepare_spec_verify(vlg, tokens.view(n, R), None, first_d, self.accept_len[:n], self.bonus[:n],
+                                         self.ws_verify)
+            hit = self._calls[key] = (draft, argmax, verify, spec, qkv)
+        return hit
 
     def run(self, stream=None, after_pass=None):
         """Decode the whole section for every rollout.  Returns the decoded
@@ -541,35 +568,29 @@ class ForkTrajectory:
                     compacted = active
                     priv = B.KVCache(self.sub.k[:n], self.sub.v[:n])
                 # the round's state: verified rows unmasked with their tokens
+                fa = first[active]
                 hm, ht = self.h_masked[: n * R].numpy(), self.h_tokens[: n * R].numpy()
-                for j, s in enumerate(active):
-                    hm[j * R:(j + 1) * R] = np.arange(R) >= first[s]
-                    ht[j * R:(j + 1) * R] = verified[s]
-                self.h_first[:n] = torch.from_numpy(first[active].astype(np.int32))
+                hm[:] = (np.arange(R)[None, :] >= fa[:, None]).ravel()
+                ht[:] = verified[active].ravel()
+                self.h_first[:n].numpy()[:] = fa
                 masked, tokens, first_d = self.masked[: n * R], self.tokens[: n * R], self.first[:n]
                 masked.copy_(self.h_masked[: n * R], non_blocking=True)
                 tokens.copy_(self.h_tokens[: n * R], non_blocking=True)
                 first_d.copy_(self.h_first[:n], non_blocking=True)
                 self._plant(b, r, active)
                 out = self.out[: n * R * Hq * D].view(n, R, Hq, D)
-                qkv = [self.qkv[(b, r % self.pool, pass_id)] for pass_id in (0, 1)]
-                q, k, v = (x[:n] for x in qkv[0])
-                B.bc_attn_step(self.shared, [self.prefix], priv, [pl] * n, q, k, v, [0, R], B.BC_MASK_BLOCK_BIDIR,
-                               self.scale, out, self.ws_attn, stream=stream)
+                self._pl[:n] = pl
+                draft, argmax, verify, spec, qkv = self._round_calls(b, n, r, priv, masked, tokens, first_d, out)
+                draft()
                 if after_pass is not None:
                     after_pass(b, r, 0, list(active), out)
-                dlg = self.base["draft"][: n * R * V].view(n * R, V)
-                B.bc_unmask_select(dlg, list(range(0, n * R + 1, R)), [B.BC_UNMASK_SEMI] * n, [1] * n, 0.0, masked,
-                                   tokens, None, self.n_commit[:n], self.ws_unmask, stream=stream)
-                q, k, v = (x[:n] for x in qkv[1])
-                B.bc_attn_step(self.shared, [self.prefix], priv, [pl] * n, q, k, v, [0, R], B.BC_MASK_BLOCK_CAUSAL,
-                               self.scale, out, self.ws_attn, stream=stream)
+                argmax()
+                verify()
                 if after_pass is not None:
                     after_pass(b, r, 1, list(active), out)
-                vlg = self.base["verify"][: n * R * V].view(n, R, V)
-                B.bc_spec_verify(vlg, tokens.view(n, R), None, first_d, self.accept_len[:n], self.bonus[:n],
-                                 self.ws_verify, stream=stream)
+                spec()
                 self._restore(n * R)
+                k, v = qkv[1][1][:n], qkv[1][2][:n]
                 self.h_acc[:n].copy_(self.accept_len[:n], non_blocking=True)
                 self.h_bonus[:n].copy_(self.bonus[:n], non_blocking=True)
                 self.h_drafts[: n * R].copy_(tokens, non_blocking=True)
@@ -578,18 +599,20 @@ class ForkTrajectory:
                 drafts = self.h_drafts[: n * R].numpy().reshape(n, R)
                 self.trace.append(dict(block=b, round=r, active=list(active),
                                        first=[int(first[s]) for s in active], accept=acc, bonus=bon))
-                still, done_slot, done_seq = [], [], []
-                for j, s in enumerate(active):
-                    f, a = int(first[s]), acc[j]
-                    verified[s, f:f + a] = drafts[j, f:f + a]
-                    if bon[j] >= 0:
-                        verified[s, f + a] = bon[j]
-                    first[s] = f + a + (1 if bon[j] >= 0 else 0)
-                    if first[s] < R:
-                        still.append(s)
-                    else:
-                        done_slot.append(j)
-                        done_seq.append(s)
+                # accepted drafts, then the bonus at the first mismatch
+                A, Bo, act_arr = np.asarray(acc), np.asarray(bon), np.asarray(active)
+                cols = np.arange(R)[None, :]
+                take = (cols >= fa[:, None]) & (cols < (fa + A)[:, None])
+                vs = verified[act_arr]
+                vs[take] = drafts[take]
+                hasb = Bo >= 0
+                vs[np.nonzero(hasb)[0], (fa + A)[hasb]] = Bo[hasb]
+                verified[act_arr] = vs
+                nf = fa + A + hasb
+                first[act_arr] = nf
+                fin = nf >= R
+                still = act_arr[~fin].tolist()
+                done_slot, done_seq = np.nonzero(fin)[0].tolist(), act_arr[fin].tolist()
                 if done_seq:
                     # the K/V of this (their last) verify pass are what they commit
                     js = torch.tensor(done_slot, dtype=torch.int64, device=self.dev)
