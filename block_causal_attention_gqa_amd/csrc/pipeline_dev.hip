@@ -352,17 +352,19 @@ int bc_pipeline_dev_create(const int32_t* block_sizes, int32_t n_blocks, int32_t
   }
   if (prefix_len < 0 || prefix_len + total > cache->capacity) return BC_ERR_ARG;
   // R: the widest step, the largest sum of `window` consecutive blocks
-  int R = 0;
+  int R = 0, widest = 0;
   for (int b = 0; b < n_blocks; ++b) {
     int r = 0;
     for (int j = b; j < n_blocks && j < b + window; ++j) r += block_sizes[j];
-    R = std::max(R, r);
+    if (r > R) R = r, widest = b;
   }
-  // the widest step's arguments: R rows as `window` equal-sized blocks are
-  // not needed -- any valid offsets do, the plan replaces them on the device
-  std::vector<int32_t> off = {0, R};
-  std::vector<int32_t> mode = {BC_UNMASK_FULL}, div = {1};
-  const bc_active a{q, k, v, off.data(), 1, 1, R, n_q_heads};
+  // the widest step's arguments, validated with that step's blocks (the
+  // plan replaces the offsets, modes and n on the device)
+  std::vector<int32_t> off = {0};
+  for (int j = widest; j < n_blocks && j < widest + window; ++j) off.push_back(off.back() + block_sizes[j]);
+  const int n_w = (int)off.size() - 1;
+  std::vector<int32_t> mode(n_w, BC_UNMASK_FULL), div(n_w, 1);
+  const bc_active a{q, k, v, off.data(), n_w, 1, R, n_q_heads};
   const size_t ws_attn = bc_attn_workspace_bytes(cache, nullptr, &a, 0);
   const size_t ws_unmask = bc_unmask_workspace_bytes(R, vocab);
   if (ws_attn == 0 || ws_unmask == 0) return BC_ERR_UNSUPPORTED;
@@ -427,7 +429,7 @@ int bc_pipeline_dev_create(const int32_t* block_sizes, int32_t n_blocks, int32_t
   const int32_t len_max = cache->capacity;
   int st = prepare_attn_args(cache, &len_max, &a, scale, out, wa, ws_attn, &d->attn);
   if (st == BC_OK)
-    st = prepare_unmask_args(logits, R, vocab, off.data(), 1, mode.data(), div.data(), threshold, masked, tokens,
+    st = prepare_unmask_args(logits, R, vocab, off.data(), n_w, mode.data(), div.data(), threshold, masked, tokens,
                              counts, wu, ws_unmask, &d->unmask);
   if (st != BC_OK) {
     bc_pipeline_dev_destroy(d);

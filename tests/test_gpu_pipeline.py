@@ -198,3 +198,40 @@ def test_native_loop_stops_on_a_callback_error_and_runs_again():
     torch.cuda.synchronize()
     assert pd.trace == want_trace
     assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok))
+
+
+@pytest.mark.parametrize("add,act,n_div,window", [(0.3, 0.6, 2, 3), (0.0, 0.5, 3, 2)])
+def test_irregular_blocks_all_drivers(add, act, n_div, window):
+    """Blocks of 7, 1, 9, 4, 2 and 13 rows over a 100-key prefix (vocabulary
+    1024): the widest step is not a multiple of any block size and a one-row
+    block joins and commits; every driver against the oracle's trace and
+    tokens, and the cache holding each block's K/V of its last step."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined irregular blocks add=%g act=%g n=%d window=%d" % (add, act, n_div, window), flush=True)
+    preset = dict(P, blocks=[7, 1, 9, 4, 2, 13], prefix=100, vocab=1024)
+    sizes = preset["blocks"]
+    pd = decode.PipelinedDecode(preset, seed=SEED, device=G.DEV, add=add, act=act, tau=0.5, n_div=n_div,
+                                window=window)
+    want_tok, want_trace = OP.pipelined_decode(sizes, pd.logits_for, add, act, 0.5, n_div, window)
+    last = {}
+    for k, st in enumerate(want_trace):
+        for b in st["active"]:
+            last[b] = sum(1 for x in want_trace[:k + 1] if b in x["active"]) - 1
+    max_local = 1 + max(last.values())
+    runs = (("host", lambda: pd.run()), ("native", lambda: pd.run_native()),
+            ("device", lambda: pd.run_device(max_local=max_local)))
+    for name, fn in runs:
+        assert fn() == len(want_trace), name
+        torch.cuda.synchronize()
+        assert pd.trace == want_trace, name
+        assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok)), name
+        assert not pd.masked.cpu().numpy().any(), name
+        kc = pd.cache.k.float().cpu().numpy()[0]
+        vc = pd.cache.v.float().cpu().numpy()[0]
+        assert int(pd.length[0]) == preset["prefix"] + sum(sizes), name
+        row = preset["prefix"]
+        for b, n in enumerate(sizes):
+            _, (_, kb), (_, vb) = pd.qkv_for(b, last[b])
+            assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), (name, b)
+            row += n
