@@ -546,7 +546,8 @@ int bc_pipeline_dev_status(const bc_pipeline_dev* d, int32_t* finished, int32_t*
 
 int bc_pipeline_dev_trace(const bc_pipeline_dev* d, int32_t* trace, int32_t max_steps) {
   if (!d || !trace || max_steps < 0) return BC_ERR_ARG;
-  const int n = std::min(max_steps, (int)d->status_host[1]);
+  if (hipDeviceSynchronize() != hipSuccess) return BC_ERR_HIP;   // the status and trace are final
+  const int n = std::min(max_steps, (int)static_cast<const volatile int32_t*>(d->status_host)[1]);
   if (n <= 0) return 0;
   if (hipMemcpy(trace, d->sched.trace, sizeof(int32_t) * n * (2 + 4 * d->window), hipMemcpyDeviceToHost) !=
       hipSuccess)

@@ -436,9 +436,9 @@ int bc_pipeline_decode(bc_pipeline *p, const bc_kv_cache *cache, int32_t *cache_
  *   or on an error), the steps run, the cache length, and error (0; 1 a
  *   commit count out of range; 2 more steps than max_steps; 3 a missing
  *   replay input).
- * bc_pipeline_dev_trace: copies the per-step trace (the layout of
- *   bc_pipeline_decode's) of the steps run to the host, returns their count;
- *   synchronous.
+ * bc_pipeline_dev_trace: waits for the device, then copies the per-step
+ *   trace (the layout of bc_pipeline_decode's) of the steps run to the host
+ *   and returns their count.
  * bc_pipeline_dev_read_plan: copies the next step's plan to the host once
  *   the device is idle (synchronous). */
 typedef struct {
