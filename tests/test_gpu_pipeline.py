@@ -235,3 +235,65 @@ def test_irregular_blocks_all_drivers(add, act, n_div, window):
             _, (_, kb), (_, vb) = pd.qkv_for(b, last[b])
             assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), (name, b)
             row += n
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("f32", 128), ("f32", 64), ("bf16", 64)])
+def test_device_plan_cases_of_other_dtypes_and_head_dims(dtype, head_dim):
+    """The device-plan cases of the float32 partial kernel and of head_dim 64
+    (8q/2kv heads, blocks of 5, 12, 3 and 9 rows over a 40-key prefix,
+    vocabulary 512): trace, tokens and committed cache of every driver
+    against the oracle, and one sampled step's attention within the
+    tolerance of its dtype (1e-5 for float32, 1e-2 for bf16)."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined %s D=%d: all drivers" % (dtype, head_dim), flush=True)
+    preset = dict(P, dtype=dtype, head_dim=head_dim, n_q_heads=8, n_kv_heads=2, blocks=[5, 12, 3, 9], prefix=40,
+                  vocab=512)
+    sizes = preset["blocks"]
+    add, act, tau, n_div, window = 0.2, 0.6, 0.5, 3, 3
+    pd = decode.PipelinedDecode(preset, seed=SEED, device=G.DEV, add=add, act=act, tau=tau, n_div=n_div,
+                                window=window)
+    want_tok, want_trace = OP.pipelined_decode(sizes, pd.logits_for, add, act, tau, n_div, window)
+    last = {}
+    for k, st in enumerate(want_trace):
+        for b in st["active"]:
+            last[b] = sum(1 for x in want_trace[:k + 1] if b in x["active"]) - 1
+    max_local = 1 + max(last.values())
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    sample = len(want_trace) // 2
+    seen = {}
+
+    def after_step(k, active, steps, length, out):
+        if k == sample:
+            seen[k] = (active, steps, length, out.float().cpu().numpy())
+
+    runs = (("host", lambda: pd.run()), ("native", lambda: pd.run_native()),
+            ("device", lambda: pd.run_device(max_local=max_local)),
+            ("device-steps", lambda: pd.run_device(max_local=max_local, after_step=after_step)))
+    for name, fn in runs:
+        assert fn() == len(want_trace), name
+        torch.cuda.synchronize()
+        assert pd.trace == want_trace, name
+        assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok)), name
+        kc = pd.cache.k.float().cpu().numpy()[0]
+        vc = pd.cache.v.float().cpu().numpy()[0]
+        row = preset["prefix"]
+        for b, n in enumerate(sizes):
+            _, (_, kb), (_, vb) = pd.qkv_for(b, last[b])
+            assert np.array_equal(kc[:, row:row + n], kb[0]) and np.array_equal(vc[:, row:row + n], vb[0]), (name, b)
+            row += n
+    # the sampled step against the oracle's attention over the cache it saw
+    active, steps, length, got = seen[sample]
+    done = [b for st in want_trace[:sample] for b in st["committed"]]
+    assert length == preset["prefix"] + sum(sizes[b] for b in done)
+    (_, _), (pk, pv) = synth.kv_cache(SEED, 1, preset["n_kv_heads"], pd.cap, head_dim, [preset["prefix"]], dtype)
+    ck = np.concatenate([pk[0, :, :preset["prefix"]]] + [pd.qkv_for(b, last[b])[1][1][0] for b in done], axis=1)
+    cv = np.concatenate([pv[0, :, :preset["prefix"]]] + [pd.qkv_for(b, last[b])[2][1][0] for b in done], axis=1)
+    h = [pd.qkv_for(b, s) for b, s in zip(active, steps)]
+    q = np.concatenate([x[0][1] for x in h], axis=1)
+    ka = np.concatenate([x[1][1] for x in h], axis=2)
+    va = np.concatenate([x[2][1] for x in h], axis=2)
+    off = np.concatenate([[0], np.cumsum([sizes[b] for b in active])])
+    want = OA.attention_step(q, ck[None], cv[None], [length], ka, va, off, OA.MASK_BIDIR, scale=head_dim ** -0.5)
+    err = np.abs(got[:, :off[-1]] - want).max()
+    assert err <= tol, "sampled step %d attention max-abs %.3g" % (sample, err)
