@@ -351,6 +351,7 @@ int bc_pipeline_dev_create(const int32_t* block_sizes, int32_t n_blocks, int32_t
     total += block_sizes[b];
   }
   if (prefix_len < 0 || prefix_len + total > cache->capacity) return BC_ERR_ARG;
+  if (vocab % 4 != 0) return BC_ERR_UNSUPPORTED;   // the replay copies logit rows in 16-byte units
   // R: the widest step, the largest sum of `window` consecutive blocks
   int R = 0, widest = 0;
   for (int b = 0; b < n_blocks; ++b) {
@@ -478,10 +479,6 @@ int bc_pipeline_dev_create(const int32_t* block_sizes, int32_t n_blocks, int32_t
   r.kv_row_bytes = cache->head_dim * elem_size(cache->dtype);
   r.Hkv = cache->n_kv_heads;
   r.logit_row_bytes = vocab * (int)sizeof(float);
-  if (r.logit_row_bytes % 16 != 0) {   // the replay copies 16-byte units
-    bc_pipeline_dev_destroy(d);
-    return BC_ERR_UNSUPPORTED;
-  }
   *dev = d;
   return BC_OK;
 }

@@ -420,7 +420,8 @@ int bc_pipeline_decode(bc_pipeline *p, const bc_kv_cache *cache, int32_t *cache_
  *   the trace.  The library allocates its device state, workspaces and trace
  *   (hipMalloc) and a small mapped host status, and owns them until
  *   bc_pipeline_dev_destroy.  Errors: BC_ERR_ARG, BC_ERR_UNSUPPORTED (as
- *   bc_attn_step / bc_unmask_select for the widest step), BC_ERR_HIP.
+ *   bc_attn_step / bc_unmask_select for the widest step, or a vocabulary
+ *   that is not a multiple of 4), BC_ERR_HIP.
  * bc_pipeline_dev_reset: enqueues the start of a decode (initial state, the
  *   first plan); masked and tokens are the caller's to initialise.
  * bc_pipeline_dev_step: enqueues one step: attention over the planned rows,

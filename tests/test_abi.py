@@ -244,6 +244,7 @@ def test_device_pipeline_validation(L):
     assert create(q=None) == B.BC_ERR_ARG
     assert create(max_steps=0) == B.BC_ERR_ARG
     assert create(vocab=0) == B.BC_ERR_ARG
+    assert create(vocab=1022) == B.BC_ERR_UNSUPPORTED   # logit rows not whole 16-byte units
     assert out.value is None
     for f in (L.bc_pipeline_dev_reset, L.bc_pipeline_dev_step):
         assert f(None, None) == B.BC_ERR_ARG
