@@ -149,3 +149,57 @@ def test_block_size_one_is_causal_decoding():
     got = a[0].float().numpy().reshape(n, Hq, D)
     err = np.abs(got - full[L0:]).max()
     assert err <= 1e-2, "B = 1 decode vs full causal recompute: max-abs %.3g" % err
+
+
+def test_bench_configuration_sampled_sequences_match_oracle():
+    """The large-block decode as the bench times it: batch 16, B = 32,
+    vocabulary 151936, 4 distinct logits and Q/K/V sets cycled over the
+    steps, seed 0.  Two of the 16 sequences (the first and the twelfth; the
+    oracle's float64 decode of a sequence at this vocabulary takes several
+    seconds) are decoded by the oracle on the same pool entries: tokens and
+    committed cache bit for bit, and the attention of the step the bench
+    times alone (the middle block's first step) within 1e-2."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("large-block decode B=32 batch 16 vocab 151936 (bench configuration)", flush=True)
+    S, seed, pool = 16, 0, 4
+    p = synth.large_block_preset(32, n_seq=S)
+    blocks, steps, V = list(p["blocks"]), p["steps"], p["vocab"]
+    Hq, Hkv, D = p["n_q_heads"], p["n_kv_heads"], p["head_dim"]
+    dec = decode.SectionDecode(p, seed=seed, n_seq=S, device=G.DEV, logits_pool=pool, qkv_pool=pool)
+    keep = {(len(blocks) // 2, 0)}
+    seen = {}
+
+    def after_attn(b, st, out):
+        if (b, st) in keep:
+            torch.cuda.synchronize()
+            seen[(b, st)] = out.float().cpu().numpy()
+
+    dec.after_attn = after_attn
+    dec.run()
+    torch.cuda.synchronize()
+    tokens = dec.tokens.cpu().numpy()
+    kc = dec.cache.k.float().cpu().numpy()
+    vc = dec.cache.v.float().cpu().numpy()
+    assert not dec.masked.cpu().numpy().any()
+    # the pools as the decoder draws them (the same seeded generators)
+    lg_pool = [synth.logits(seed, S * 32, V, p["sigma"], 1000 + i) for i in range(pool)]
+    qkv_pool = [synth.active_qkv(seed, S, 32, Hq, Hkv, D, p["dtype"], 2000 + 32, i) for i in range(pool)]
+    _, (pk, pv) = synth.kv_cache(seed, S, Hkv, p["prefix"] + sum(blocks), D, [p["prefix"]] * S, p["dtype"])
+    row0 = np.concatenate([[0], np.cumsum(blocks)])
+    for s in (0, 11):
+        def inp(b, st):
+            i = (b * steps + st) % pool
+            (_, q), (_, k), (_, v) = qkv_pool[i]
+            return q[s:s + 1], k[s:s + 1], v[s:s + 1], lg_pool[i][s * 32:(s + 1) * 32]
+
+        n = sum(blocks)
+        want = OS.section_decode(pk[s], pv[s], p["prefix"], [[b] for b in range(len(blocks))], blocks, inp, steps,
+                                 p["threshold"], np.ones(n, np.uint8), np.full(n, -1, np.int32), scale=D ** -0.5,
+                                 keep=keep, attend_all=False)
+        got = np.concatenate([tokens[S * row0[b] + s * bs: S * row0[b] + (s + 1) * bs] for b, bs in enumerate(blocks)])
+        assert np.array_equal(got, want["tokens"]), "sequence %d: tokens" % s
+        assert np.array_equal(kc[s], want["cache_k"]) and np.array_equal(vc[s], want["cache_v"]), "sequence %d: cache" % s
+        for key in keep:
+            err = np.abs(seen[key][s] - want["attention"][key][0]).max()
+            assert err <= 1e-2, "sequence %d: attention max-abs %.3g" % (s, err)
