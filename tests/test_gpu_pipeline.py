@@ -297,3 +297,22 @@ def test_device_plan_cases_of_other_dtypes_and_head_dims(dtype, head_dim):
     want = OA.attention_step(q, ck[None], cv[None], [length], ka, va, off, OA.MASK_BIDIR, scale=head_dim ** -0.5)
     err = np.abs(got[:, :off[-1]] - want).max()
     assert err <= tol, "sampled step %d attention max-abs %.3g" % (sample, err)
+
+
+@pytest.mark.parametrize("add,act", [(0.5, 0.9), (1.0, 1.0)])
+def test_bench_configurations_all_drivers(add, act):
+    """The 625-token decode exactly as the bench times it (seed 0, tau 0.5,
+    n = 4, window 3; with overlap and without): every driver's trace, tokens
+    and final cache length against the oracle."""
+    import torch
+    from block_causal_attention_gqa_amd import decode
+    print("pipelined 625 bench configuration add=%g act=%g" % (add, act), flush=True)
+    pd = decode.PipelinedDecode(seed=0, device=G.DEV, tau=0.5, n_div=4, window=3, add=add, act=act)
+    want_tok, want_trace = OP.pipelined_decode(list(P["blocks"]), pd.logits_for, add, act, 0.5, 4, 3)
+    pd.keep_inputs = True
+    for name, fn in (("host", pd.run), ("native", pd.run_native), ("device", pd.run_device)):
+        assert fn() == len(want_trace), name
+        torch.cuda.synchronize()
+        assert pd.trace == want_trace, name
+        assert np.array_equal(pd.tokens.cpu().numpy(), np.concatenate(want_tok)), name
+        assert int(pd.length[0]) == pd.cap, name
