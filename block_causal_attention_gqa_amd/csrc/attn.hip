@@ -18,7 +18,9 @@
 //     a fork the tile runs over the rows of ALL rollouts, so the shared prefix
 //     is streamed once per tile instead of once per rollout;
 //   * active items: slot P covers the rollout's private keys plus the active
-//     keys, where the block predicate applies.  The predicate is never stored:
+//     keys, where the block predicate applies (without a fork the active
+//     keys may instead ride in the last prefix chunk's items: "fold", no
+//     slot P).  The predicate is never stored:
 //     active key j is visible to active row r iff j < lim(r), with lim(r) the
 //     end of r's block (BIDIR) or r + 1 (CAUSAL).
 // A second kernel merges the slots with log-sum-exp weights.
@@ -211,6 +213,23 @@ __device__ inline Item<T> decode_item(const AttnArgs& a, int item) {
     it.k0 = static_cast<const T*>(a.pk) + off;
     it.v0 = static_cast<const T*>(a.pv) + off;
     it.n0 = max(0, key_end - key_begin);
+    if (a.fold && it.slot == a.n_splits - 1) {
+      // the sequence's active keys ride in its last prefix chunk (no fork:
+      // the item's rows are exactly the rows of that sequence and KV head)
+      const long long act_off = (long long)(it.s_item * a.Hkv + it.g) * a.R * a.D;
+      const T* ak = static_cast<const T*>(a.ak) + act_off;
+      const T* av = static_cast<const T*>(a.av) + act_off;
+      if (it.n0 > 0) {
+        it.k1 = ak;
+        it.v1 = av;
+        it.n1 = a.R;
+      } else {
+        it.k0 = ak;
+        it.v0 = av;
+        it.n0 = a.R;
+        it.masked0 = true;
+      }
+    }
   } else {
     const int i2 = item - a.n_prefix_items;
     const int rest = fast_div(i2, a.dv_mt_active);

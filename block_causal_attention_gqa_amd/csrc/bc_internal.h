@@ -64,7 +64,8 @@ struct AttnArgs {
   int fork;            // 1: one shared prefix for all S rollouts + private caches
   int causal;          // bc_mask
   int n_splits;        // prefix chunks P; slot P holds private + active keys
-  int n_slots;         // P + 1
+  int n_slots;         // P + 1, or P under fold
+  int fold;            // 1 (no fork): the active keys ride in the last prefix chunk's items, no slot P
   int n_mt_prefix;     // row tiles per prefix group
   int n_mt_active;     // row tiles per (seq, kv head) for the active items
   int n_prefix_items;

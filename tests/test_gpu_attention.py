@@ -107,8 +107,8 @@ def test_fork_sixteen_rollouts_ragged_rows():
     _check(60, 16, 23, 16, 2, 128, "bf16", [3282], [0, 23], CAUSAL, fork=True, priv_len=priv, priv_cap=48)
 
 
-# ---- many rows per KV-head group (>= 2048): the eight-wave kernel whose two
-# wave groups alternate matrix and vector halves
+# ---- many rows per KV-head group (>= 2048 rows): 128-row tiles with two
+# 16-row column tiles per wave, long items
 
 
 @pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
@@ -232,6 +232,30 @@ def test_automatic_splits_shrink_to_the_workspace():
                        D ** -0.5, out, ws)
         got = out.float().cpu().numpy()
         assert np.abs(got - want).max() <= TOL["bf16"]
+
+
+# ---- fold: without a fork, when the prefix items fill the co-resident
+# workgroups but the active items would not fit beside them, the last prefix
+# chunk of each row tile also takes its active keys.  16 sequences x 8 KV
+# heads x 32 rows x 4 query heads: 256 row tiles of 64 rows, so two chunks
+# give 512 prefix items and 256 active items (folded); one chunk gives 256 +
+# 256 (resident together) and three give 768 prefix items (more than one
+# round anyway): both keep the active items apart.  The lengths put the last
+# chunk's prefix keys at zero (the active keys become the item's only
+# segment), at partial tiles, and at whole tiles.
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_fold_active_keys_into_the_last_chunk(mode, splits):
+    lens = [0, 1, 40, 63, 64, 65, 127, 300, 511, 512, 700, 1000, 1023, 1024, 1100, 1200]
+    _check(120 + splits, 16, 32, 32, 8, 128, "bf16", lens, [0, 7, 19, 32], mode, cap=1200, n_splits=splits)
+
+
+def test_fold_head_dim_64_automatic_splits():
+    lens = [int(x) for x in np.random.default_rng(124).integers(0, 2049, 16)]
+    _check(124, 16, 32, 32, 8, 64, "bf16", lens, [0, 32], BIDIR, cap=2048, n_splits=2)
+    _check(125, 16, 32, 32, 8, 64, "bf16", lens, [0, 32], BIDIR, cap=2048)
 
 
 # ---- the call limits: BC_MAX_BLOCKS active blocks, BC_MAX_SEQ sequences
