@@ -144,7 +144,12 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   // large-block batch 16 38.7 -> 36.8 us and batch 8 27.0 -> 25.1 us (256
   // items with 128-row tiles); fork N = 16 29.4 -> 26.1 us (240); fork
   // N = 32 / 48 / 64 (480 / 432 / 384 items) are faster with 128 rows.
-  bool small = groups * ((rows_group + 127) / 128) < 32;
+  // Groups of at most 64 rows also take 64-row tiles: a 128-row tile would
+  // be at least half padding, whose MFMAs and operand reads every wave still
+  // issues (measured, large-block batch 16 over a 2176-key prefix, block
+  // sizes 1 / 4 / 8 / 16: call 28.9 / 31.1 / 31.4 / 33.5 -> 26.4 / 28.4 /
+  // 28.9 / 30.3 us back to back).
+  bool small = groups * ((rows_group + 127) / 128) < 32 || rows_group <= 64;
   int P = n_splits;
   if (!small && prefix->dtype == BC_BF16) {
     const int mt2 = (rows_group + 127) / 128;
