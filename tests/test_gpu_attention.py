@@ -130,6 +130,35 @@ def test_many_rows_empty_prefix():
     _check(75, 1, 1024, 4, 1, 128, "bf16", [0], [0, 512, 1024], CAUSAL)
 
 
+# ---- many sequences, each with its own prefix of very different length
+
+
+@pytest.mark.parametrize("splits", [0, 2, 3])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_batch_ragged_prefixes(mode, splits):
+    # 8 sequences x 4 KV heads: 32 groups of 32 rows x 4 heads (128 rows);
+    # prefixes from empty to 2047 keys, so a call's items run from 0 to 16
+    # key tiles; blocks of 7 / 13 / 12
+    lens = [2047, 64, 0, 300, 517, 1000, 1999, 130]
+    _check(80 + splits, 8, 32, 16, 4, 128, "bf16", lens, [0, 7, 20, 32], mode, cap=2048, n_splits=splits)
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_batch16_ragged_prefixes_with_short_ones(mode):
+    # 16 sequences x 8 KV heads of 2 query heads: 128 row tiles of 64 rows
+    # (32 rows x 2 heads); prefixes from empty to 2047 keys, several shorter
+    # than one key tile or one split
+    lens = [0, 5, 64, 100, 130, 300, 2047, 1999, 1500, 1024, 777, 65, 2000, 1234, 640, 191]
+    _check(86, 16, 32, 16, 8, 128, "bf16", lens, [0, 7, 20, 32], mode, cap=2048)
+
+
+def test_batch16_ragged_prefixes_folded():
+    # the large-block batch-16 shape (32q/8kv, 32-row block) with ragged
+    # prefixes: 512 prefix items, the active keys folded into the last chunk
+    lens = [2176 - 37 * s for s in range(16)]
+    _check(85, 16, 32, 32, 8, 128, "bf16", lens, [0, 32], BIDIR, cap=2176)
+
+
 def test_block_size_one_equals_causal():
     # WAM-Diff2 sec. 2.1: B = 1 is causal decoding -- bitwise equal on the GPU
     a, _ = G.attn_case(70, 1, 16, 8, 2, 128, "bf16", [300], list(range(17)), BIDIR)
