@@ -449,6 +449,11 @@ __device__ inline u32x4 raw_buffer(const void* base, int bytes) {
   return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)bytes, (uint32_t)kRawBufferWord3};
 }
 
+__device__ inline uint32_t lds_addr(const BC_LDS uint8_t* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
+// LDS given at launch (the fork's direct form)
+extern __shared__ __attribute__((aligned(16))) uint8_t bc_dyn_lds[];
+
 __device__ inline uint32_t lds_offset(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((BC_LDS const uint8_t*)p);
 }
@@ -857,6 +862,409 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   else write_partial_f32<D, CT, false>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
+// ====================================================== fork, direct form
+// Shared-prefix fork with every row tile on one CU (N rollouts, 2 N Hkv row
+// tiles >= the CUs): row tile (kv head g, rollout s, half h) holds half of
+// rollout s's R x group query rows of kv head g (at most 96), and its
+// workgroup covers ALL the keys those rows see, in two key halves:
+//   kh = 0: the shared prefix's keys [0, X), then the rollout's private keys;
+//   kh = 1: the shared prefix's keys [X, L), then the active keys (the only
+//           segment the block predicate applies to),
+// with X cut so that both halves run the same number of 64-key tiles (the
+// shorter runs one empty tile at most).  Wave 6 kh + rg holds row group rg
+// (16 rows, one column tile) of key half kh: 12 waves, three per SIMD, which
+// hide each other's latencies.  Each half streams its keys through a
+// two-stage K/V ring of its own, loaded by its first four waves.  At the end
+// half 1 hands (o, m, l) to half 0 through LDS, which merges them and writes
+// the normalised output: no split partials, no combine, every CU the same
+// work.  The price is one K and one V operand read per 16 rows instead of
+// per 32 (two column tiles per wave leave 6 waves, which sit unevenly on the
+// 4 SIMDs: measured slower, 67.7 against 61.5 us).
+// LDS (given at launch): per half K(0), K(1), V(0), V(1) (64 KB), then the
+// Q tile of the 96 rows (24 KB).
+constexpr unsigned kForkLdsBytes = 2u * 4 * kAttnKeyTile * 128 * 2 + kForkTileRows * 128 * 2;
+constexpr int kForkWaves = 2 * kForkTileRows / 16;   // 12: three per SIMD
+
+template <int D>
+__global__ __launch_bounds__(kForkWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_fork_direct_kernel(const AttnArgs a) {
+  constexpr int CT = 1;                // one 16-row column tile per wave
+  constexpr int KT = kAttnKeyTile;
+  constexpr int RB = D * 2;            // bytes per key row
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int TB = KT * RB;          // bytes per tile and tensor
+  constexpr int RPL = 1024 / RB;       // key rows per wave-wide 16-byte load
+  constexpr int RG = kForkTileRows / (16 * CT);   // row groups (waves) per key half
+  constexpr int WR = 16 * CT;          // rows per wave
+  constexpr int LW = 4;                // loading waves per half
+  static_assert(TB % (LW * 1024) == 0 && LW <= RG, "a tile must split evenly over the loading waves");
+  constexpr int LPW = TB / (LW * 1024);
+  constexpr int QLPW = WR * RB / 1024;  // Q loads per wave (its rows)
+  constexpr int QK = D / 32;
+  constexpr int kHalfBytes = 4 * TB;
+  constexpr uint32_t kQOff = 2 * kHalfBytes;
+  using lds_t = const BC_LDS uint8_t*;
+  const lds_t lds = (lds_t)bc_dyn_lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = w / RG, rg = w - kh * RG;
+  const int n = lane & 15, jj = lane >> 4;
+
+  // row tile: consecutive tiles (one kv head's) share an XCD and its L2.
+  // (Integer division runs on the vector unit; readfirstlane keeps these
+  // workgroup-uniform values, and the pointers made from them, in SGPRs.)
+  const int n_tiles = a.S * a.Hkv * 2;
+  const int tile = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, n_tiles));
+  const int g = __builtin_amdgcn_readfirstlane(tile / (a.S * 2));
+  const int s = (tile - g * a.S * 2) >> 1, hf = tile & 1;
+  const int rows_r = a.R * a.group;
+  const int half = (rows_r + 1) >> 1;
+  const int rows_here = hf == 0 ? half : rows_r - half;
+  // output row of row ml of the tile (clamped to the tile's last row)
+  auto out_row = [&](int ml, int& r) __attribute__((always_inline)) {
+    const int mr = hf * half + min(ml, rows_here - 1);
+    r = mr / a.group;
+    return (s * a.R + r) * a.Hq + g * a.group + (mr - r * a.group);
+  };
+
+  // this lane's query columns
+  bool valid[CT];
+  int orow[CT], lim[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int ml = rg * WR + c * 16 + n;
+    valid[c] = ml < rows_here;
+    int r;
+    orow[c] = out_row(ml, r);
+    int l = r + 1;
+    if (!a.causal) {
+      l = a.R;
+      for (int b = 0; b < a.n_blk; ++b)
+        if (r < a.blk_off[b + 1]) { l = a.blk_off[b + 1]; break; }
+    }
+    lim[c] = l;
+  }
+
+  // the two halves' key segments; both run nt tiles
+  const int L = a.prefix_len[0], lv = a.priv_len[s];
+  const int TL = (L + KT - 1) / KT, tv = (lv + KT - 1) / KT, tr = (a.R + KT - 1) / KT;
+  const int cut = __builtin_amdgcn_readfirstlane(max(0, min(TL, (TL + tr - tv) / 2)));
+  const int X = min(cut * KT, L);
+  const int nt = __builtin_amdgcn_readfirstlane(max(cut + tv, TL - cut + tr));
+  const bf16_t* pk = static_cast<const bf16_t*>(a.pk) + g * a.p_head_stride;
+  const bf16_t* pv = static_cast<const bf16_t*>(a.pv) + g * a.p_head_stride;
+  const bf16_t *ka, *va, *kb_, *vb_;
+  int na, nb;
+  if (kh == 0) {
+    ka = pk;
+    va = pv;
+    na = X;
+    const long long po = s * a.v_seq_stride + g * a.v_head_stride;
+    kb_ = static_cast<const bf16_t*>(a.vk) + po;
+    vb_ = static_cast<const bf16_t*>(a.vv) + po;
+    nb = lv;
+  } else {
+    ka = pk + (long long)X * D;
+    va = pv + (long long)X * D;
+    na = L - X;
+    const long long ao = (long long)(s * a.Hkv + g) * a.R * D;
+    kb_ = static_cast<const bf16_t*>(a.ak) + ao;
+    vb_ = static_cast<const bf16_t*>(a.av) + ao;
+    nb = a.R;
+  }
+  const int nta = (na + KT - 1) / KT, ntb = (nb + KT - 1) / KT;
+  const bool mskb = kh == 1;
+
+  // tile j of this half: its segment, first key, key count and whether the
+  // block predicate applies; past both segments an empty tile (no keys)
+  auto tile_src = [&](int j, const bf16_t*& kp, const bf16_t*& vp, int& nk, int& kb, bool& msk)
+                      __attribute__((always_inline)) {
+    if (j < nta) { kp = ka; vp = va; nk = na; kb = j * KT; msk = false; }
+    else if (j < nta + ntb) { kp = kb_; vp = vb_; nk = nb; kb = (j - nta) * KT; msk = mskb; }
+    else { kp = ka; vp = va; nk = 0; kb = 0; msk = false; }
+  };
+
+  // LDS addresses: this half's stages at hb; operand addresses include hb
+  const uint32_t hb = kh * kHalfBytes;
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (rg * LPW + i) * RPL + lane / CPR, pos = lane % CPR;
+    koff[i] = row * RB + (pos ^ swz_k<D>(row)) * 16;
+    voff[i] = row * RB + (pos ^ swz_v<D>(row)) * 16;
+  }
+  uint32_t kaddr[QK], vaddr[D / 16];
+  {
+    const int kr = 8 * (n >> 2) + (n & 3);
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) kaddr[kk] = hb + kr * RB + ((4 * kk + jj) ^ swz_k<D>(kr)) * 16;
+    const int vr = 8 * jj + (n >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      vaddr[dt] = hb + vr * RB + ((2 * dt + ((n & 3) >> 1)) ^ swz_v<D>(vr)) * 16 + (n & 1) * 8;
+  }
+  // loads of tile j's K or V into stage p of this half (K at p TB, V at
+  // (2 + p) TB), by the half's first LW waves; rows past the tile's keys
+  // arrive as zeros
+  auto load = [&](int j, bool is_v, int p) __attribute__((always_inline)) {
+    if (rg >= LW) return;   // wave-uniform
+    const bf16_t *kp, *vp;
+    int nk, kb;
+    bool msk;
+    tile_src(j, kp, vp, nk, kb, msk);
+    // (the clamp compiles to a vector med3: readfirstlane keeps the
+    // descriptor in SGPRs, as the buffer load needs)
+    const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(nk - kb, KT)) * RB);
+    const u32x4 rs = raw_buffer((is_v ? vp : kp) + (long long)kb * D, nrec);
+    const uint32_t dst = lds_addr(lds) + hb + (is_v ? 2 + p : p) * TB + rg * LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rs, dst + i * 1024, is_v ? voff[i] : koff[i]);
+  };
+
+  bf16x8 qop[CT][QK];
+  float m_run[CT];
+  f32x4 o[CT][D / 16], osum[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    m_run[c] = kNegInf;
+    osum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto scores = [&](int p, f32x4 (&st)[CT][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int trow = 32 * (t >> 1) + 4 * (t & 1);
+      bf16x8 kop[QK];
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) kop[kk] = *(const BC_LDS bf16x8*)(lds + kaddr[kk] + p * TB + trow * RB);
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+          st[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qop[c][kk], st[c][t], 0, 0, 0);
+    }
+  };
+  auto mask = [&](int j, f32x4 (&st)[CT][4]) __attribute__((always_inline)) {
+    const bf16_t *kp, *vp;
+    int nk, kb;
+    bool msk;
+    tile_src(j, kp, vp, nk, kb, msk);
+    if (msk || kb + KT > nk) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int thr = (msk ? min(nk, lim[c]) : nk) - kb - key_group_off<true>(jj);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!(key_const_off<true>(t, i) < thr)) st[c][t][i] = kNegInf;
+      }
+    }
+  };
+  auto accumulate = [&](int p, const bf16x8 (&pb)[CT][2]) __attribute__((always_inline)) {
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) osum[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][s2], osum[c], 0, 0, 0);
+#pragma unroll
+    for (int dt0 = 0; dt0 < D / 16; dt0 += 4) {
+      bf16x8 vop[4][2];
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const lds_t base = lds + vaddr[dt0 + d4] + (2 + p) * TB + 32 * s2 * RB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BC_LDS i16x4*)base);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BC_LDS i16x4*)(base + 4 * RB));
+          vop[d4][s2] = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int c = 0; c < CT; ++c)
+            o[c][dt0 + d4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[d4][s2], pb[c][s2], o[c][dt0 + d4], 0, 0, 0);
+    }
+  };
+  // iteration j: as the partial kernel's (maxima and rare rescale of tile j,
+  // score MFMAs of tile j + 1 beside the exponentials of tile j, PV MFMAs
+  // of tile j, one barrier).  The MFMA block runs at raised wave priority,
+  // so that of the three waves sharing a SIMD the one issuing MFMAs is
+  // preferred (measured: 61.5 -> 59.5 us per N = 64 draft pass).
+  auto step = [&](auto par, auto last, int j, f32x4 (&s_cur)[CT][4], f32x4 (&s_nxt)[CT][4])
+                  __attribute__((always_inline)) {
+    constexpr int p = decltype(par)::value;
+    constexpr bool kLast = decltype(last)::value;
+    if constexpr (!kLast) {
+      if (j + 2 < nt) load(j + 2, false, p);
+      if (j + 1 < nt) load(j + 1, true, 1 - p);
+    }
+    mask(j, s_cur);
+    const float sl2 = a.scale_log2;
+    float alpha[CT], muse[CT];
+    bool moved = false;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s_cur[c][t][i]);
+      tmax = group4_max(tmax);
+      const float tm = tmax * sl2;
+      const bool move = tm > m_run[c] + kRescaleSlack;
+      const float mnew = move ? tm : m_run[c];
+      muse[c] = mnew == kNegInf ? 0.f : mnew;
+      alpha[c] = move ? __builtin_amdgcn_exp2f(m_run[c] - muse[c]) : 1.f;
+      m_run[c] = mnew;
+      moved |= move;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[c][dt] *= alpha[c];
+        osum[c] *= alpha[c];
+      }
+    }
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!kLast) scores(1 - p, s_nxt);
+    bf16x8 pb[CT][2];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      float pr[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[c][t][i], sl2, -muse[c]));
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[c][s2][e] = (__bf16)pr[2 * s2][e];
+          pb[c][s2][e + 4] = (__bf16)pr[2 * s2 + 1][e];
+        }
+    }
+    accumulate(p, pb);
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!kLast) tile_barrier();
+  };
+
+  // ---- prologue: K(0), (half 0) the Q tile, V(0), K(1)
+  load(0, false, 0);
+  if (kh == 0) {
+    // this wave's WR Q rows, row t of the wave at t RB with chunk c at
+    // position c ^ (t mod CPR); rows past the tile's rows load its last row
+    const bf16_t* q = static_cast<const bf16_t*>(a.q);
+    int r0;
+    const int base = __builtin_amdgcn_readfirstlane(out_row(rg * WR, r0));
+    const u32x4 rs = raw_buffer(q + (long long)base * D, 0x7ffffff0);
+    const uint32_t dst = lds_addr(lds) + kQOff + rg * WR * RB;
+#pragma unroll
+    for (int i = 0; i < QLPW; ++i) {
+      const int t = i * RPL + lane / CPR, pos = lane % CPR;   // row within the wave
+      int rt;
+      const int ro = out_row(rg * WR + t, rt);
+      buffer_load_lds16(rs, dst + i * 1024, (uint32_t)((ro - base) * RB + (pos ^ (t % CPR)) * 16));
+    }
+  }
+  load(0, true, 0);
+  if (nt > 1) load(1, false, 1);
+  // K(0) and Q have landed once no more than V(0) and K(1) are outstanding
+  if (rg < LW) {
+    if (nt > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int t = rg * WR + c * 16 + n;
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk)
+      qop[c][kk] = *(const BC_LDS bf16x8*)(lds + kQOff + t * RB + ((4 * kk + jj) ^ (t % CPR)) * 16);
+  }
+  f32x4 sa[CT][4], sb[CT][4];
+  scores(0, sa);
+  tile_barrier();
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using More = std::false_type;
+  using Last = std::true_type;
+  int j = 0;
+  for (; j + 2 < nt; j += 2) {
+    step(S0{}, More{}, j, sa, sb);
+    step(S1{}, More{}, j + 1, sb, sa);
+  }
+  if (j + 1 < nt) {
+    step(S0{}, More{}, j, sa, sb);
+    step(S1{}, Last{}, j + 1, sb, sa);
+  } else {
+    step(S0{}, Last{}, j, sa, sb);
+  }
+
+  // ---- half 1 hands (o, m, l) to half 0 through its own (now idle) stages
+  constexpr int kPub = CT * ((D / 16) * 1024 + 2 * 256);
+  static_assert(RG * kPub <= kHalfBytes, "published partials fit in half 1's stages");
+  float l_run[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) l_run[c] = osum[c][0];
+  lds_barrier();
+  BC_LDS uint8_t* const pub = (BC_LDS uint8_t*)(lds + kHalfBytes + rg * kPub);
+  if (kh == 1) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      BC_LDS uint8_t* pc = pub + c * ((D / 16) * 1024 + 512);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *(BC_LDS f32x4*)(pc + dt * 1024 + lane * 16) = o[c][dt];
+      *(BC_LDS float*)(pc + (D / 16) * 1024 + lane * 4) = m_run[c];
+      *(BC_LDS float*)(pc + (D / 16) * 1024 + 256 + lane * 4) = l_run[c];
+    }
+  }
+  lds_barrier();
+  if (kh == 1) return;
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    if (!valid[c]) continue;
+    const BC_LDS uint8_t* pc = pub + c * ((D / 16) * 1024 + 512);
+    const float m1 = *(const BC_LDS float*)(pc + (D / 16) * 1024 + lane * 4);
+    const float l1 = *(const BC_LDS float*)(pc + (D / 16) * 1024 + 256 + lane * 4);
+    const float m = fmaxf(m_run[c], m1);
+    float l = l_run[c];
+    if (m != kNegInf) {
+      const float a0 = __builtin_amdgcn_exp2f(m_run[c] - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = o[c][dt] * a0 + *(const BC_LDS f32x4*)(pc + dt * 1024 + lane * 16) * a1;
+      l = l * a0 + l1 * a1;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 x = o[c][dt] * inv;
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)x[e]);
+      *reinterpret_cast<u32x2*>(out + (long long)orow[c] * D + 16 * dt + 4 * jj) =
+          u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+    }
+  }
+}
+
 // ============================================================ fp32 partial
 // Register-staged: the next tile's global loads are issued before the
 // current tile is computed and written to LDS one iteration later.  Loads
@@ -1127,6 +1535,13 @@ inline int partial_grid(const AttnArgs& a) {
 // ones never look at it
 template <int D, bool kDyn>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
+  if constexpr (D == 128 && !kDyn) {
+    if (a.fork_direct) {
+      hipLaunchKernelGGL((attn_fork_direct_kernel<128>), dim3(a.S * a.Hkv * 2), dim3(kForkWaves * 64), kForkLdsBytes,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.cols == 1)
     hipLaunchKernelGGL((attn_partial_bf16_kernel<D, 4, 1, kDyn>), dim3(partial_grid(a)), dim3(256), 0, stream, a);
   else
@@ -1196,6 +1611,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream)
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream) {
+  if (a.fork_direct) return hipSuccess;   // the partial pass wrote the output
   if (dtype == BC_BF16)
     return a.D == 128 ? launch_combine_typed<bf16_t, 128>(a, stream) : launch_combine_typed<bf16_t, 64>(a, stream);
   return a.D == 128 ? launch_combine_typed<float, 128>(a, stream) : launch_combine_typed<float, 64>(a, stream);

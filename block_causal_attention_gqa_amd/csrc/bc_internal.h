@@ -32,6 +32,7 @@ __device__ inline int fast_div(int n, FastDiv f) {
 // ---------------------------------------------------------------- attention
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 constexpr int kCompactRows = 1024;        // bf16 calls with at least this many output rows use compact partials
+constexpr int kForkTileRows = 96;         // rows per row tile of the fork's direct form (half a rollout's rows)
 
 // The next step of a device-resident pipelined decode (bc_dev_plan, see
 // include/bc.h), written by the schedule kernel and read by the step's kernels.
@@ -96,6 +97,10 @@ struct AttnArgs {
   // R stays the widest step's row count; a step with no active block does
   // nothing.
   const DevPlan* dyn;
+  // 1: shared-prefix fork in the direct form (one 12-wave workgroup per row
+  // tile of half a rollout's rows over all their keys, output written by the
+  // partial pass; the combine does nothing)
+  int fork_direct;
 };
 
 // Kernel arguments of a block-bidirectional attention call without a fork,

@@ -263,7 +263,10 @@ int bc_spec_verify_sampled(const float *logits, const float *noise, float inv_te
  *   (float32; for bf16 inputs with n_seq * n_rows * n_q_heads >= 1024, int16
  *   against a power of two per row and split, within 2^-14 of the row's
  *   largest element); the combine pass merges them with log-sum-exp weights
- *   into `out`.
+ *   into `out`.  A shared-prefix fork call with n_prefix_splits = 0, bf16,
+ *   head_dim 128, n_rows * (n_q_heads / n_kv_heads) <= 192 and
+ *   2 * n_seq * n_kv_heads >= 256 has no split partials: its partial pass
+ *   writes `out` itself and its combine pass does nothing.
  *
  * bc_unmask_select(args) == bc_vocab_scan(logits, n_rows, vocab, masked, 1,
  *   ws, ws_bytes, stream); bc_unmask_decide(args).

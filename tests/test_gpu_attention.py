@@ -241,6 +241,55 @@ def test_partial_then_combine_equals_step():
     assert torch.equal(a, b)
 
 
+# ---- the fork at N >= 64 rollouts: one workgroup per half of a rollout's
+# rows over all their keys (shared prefix, private keys, active keys), in two
+# key halves merged in LDS, the output written without a combine
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("prefix", [0, 70, 1000])
+def test_fork_sixtyfour_short_prefixes_odd_rows(mode, prefix):
+    # 23-row blocks (184 rows per rollout and KV head: half tiles of 92),
+    # shared prefixes from empty to 1000 keys, private lengths 0 .. 47, two
+    # blocks inside the active rows
+    priv = [(13 * s) % 48 for s in range(64)]
+    _check(95, 64, 23, 16, 2, 128, "bf16", [prefix], [0, 9, 23], mode, fork=True, priv_len=priv, priv_cap=48,
+           cap=max(prefix, 1))
+
+
+def test_fork_sixtyfour_partial_then_combine_equals_step():
+    # the partial pass writes the output itself; the combine then does nothing
+    import torch
+    from block_causal_attention_gqa_amd import synth
+    seed, N, R, Hq, Hkv, D = 96, 64, 24, 16, 2, 128
+    (pk, pv), _ = synth.kv_cache(seed, 1, Hkv, 3282, D, [3282], "bf16")
+    priv_len = [(5 * s) % 48 for s in range(N)]
+    (vk, vv), _ = synth.kv_cache(seed, N, Hkv, 48, D, priv_len, "bf16", purpose=("priv_k", "priv_v"))
+    (q, _), (k, _), (v, _) = synth.active_qkv(seed, N, R, Hq, Hkv, D, "bf16", 0)
+    prefix, priv = B.KVCache(pk.to(G.DEV), pv.to(G.DEV)), B.KVCache(vk.to(G.DEV), vv.to(G.DEV))
+    q, k, v = q.to(G.DEV), k.to(G.DEV), v.to(G.DEV)
+    ws = torch.empty(B.bc_attn_workspace_bytes(prefix, priv, (N, R, Hq, D), [0, R]), dtype=torch.uint8,
+                     device=G.DEV)
+    a = torch.empty((N, R, Hq, D), dtype=torch.bfloat16, device=G.DEV)
+    b = torch.full_like(a, 7.0)
+    args = (prefix, [3282], priv, priv_len, q, k, v, [0, R], BIDIR, D ** -0.5)
+    B.bc_attn_step(*args, a, ws)
+    B.bc_attn_partial(*args, b, ws)
+    B.bc_attn_combine(*args, b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_fork_sixtyfour_forced_splits_agree_with_direct_form():
+    # an explicit split count takes the split plan (partials and combine);
+    # both forms match the oracle and each other within the bf16 tolerance
+    priv = [(11 * s) % 48 for s in range(64)]
+    d = _check(97, 64, 24, 16, 2, 128, "bf16", [3282], [0, 24], CAUSAL, fork=True, priv_len=priv, priv_cap=48)
+    f = _check(97, 64, 24, 16, 2, 128, "bf16", [3282], [0, 24], CAUSAL, fork=True, priv_len=priv, priv_cap=48,
+               n_splits=2)
+    assert np.abs(d - f).max() <= 2 * TOL["bf16"]
+
+
 def test_automatic_splits_shrink_to_the_workspace():
     # a workspace that holds fewer slots than the automatic choice wants:
     # the call uses fewer splits and the result still matches the oracle
