@@ -39,7 +39,7 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 
 // ------------------------------------------------------------ attention plan
 struct Plan {
-  int waves, cols, fork_direct, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  int waves, cols, direct, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
   int xmap, tile_rows, unit_tiles, n_units, units_per_xcd;
   bool compact;        // compact split partials (bf16 inputs, many rows)
   bool fold;           // active keys in the last prefix chunk's items (no slot P)
@@ -207,13 +207,19 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   p->o_bytes = align256((size_t)(P + 1) * p->rows_total * D * (compact ? 2 : 4));
   p->ml_bytes = align256((size_t)(P + 1) * p->rows_total * (compact ? 16 : 8));
   p->total_bytes = p->o_bytes + p->ml_bytes;
-  // Fork, direct form: when half a rollout's rows fit one 96-row tile (bf16,
-  // head_dim 128) and the 2 N Hkv row tiles give every CU at least one, each
-  // tile's workgroup covers all the keys its rows see and writes the output
-  // (no split partials, no combine).  The workspace size stays the split
-  // plan's, which a workspace sized for these shapes holds anyway.
-  p->fork_direct = fork && prefix->dtype == BC_BF16 && D == 128 && n_splits == 0 &&
-                   R * group <= 2 * kForkTileRows && (long long)S * Hkv * 2 >= 256;
+  // Direct form (shared-prefix fork): when half of a rollout's rows per KV
+  // head fill more than half of one 96-row tile (bf16, head_dim 128) and the
+  // 2 N Hkv row tiles give every CU at least one, each tile's workgroup
+  // covers all the keys its rows see and writes the output (no split
+  // partials, no combine).  Emptier tiles would pay a full tile's MFMAs for
+  // a few rows.  The workspace size stays the split plan's, which a
+  // workspace sized for these shapes holds anyway.  (Without a fork the same
+  // form, 64-row tiles of half a sequence's rows, measured no better on the
+  // large-block batch 16 call: 33.4 -> 32.7 us back to back, 39.8 -> 41.9 us
+  // after a clean flush.)
+  const int half_rows = (R * group + 1) / 2;
+  p->direct = fork && prefix->dtype == BC_BF16 && D == 128 && n_splits == 0 && (long long)S * Hkv * 2 >= 256 &&
+              half_rows <= kForkTileRows && 2 * half_rows > kForkTileRows;
 }
 
 }  // namespace
@@ -345,7 +351,7 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   args->D = D;
   args->waves = p.waves;
   args->cols = p.cols;
-  args->fork_direct = p.fork_direct;
+  args->direct = p.direct;
   args->fork = priv ? 1 : 0;
   args->causal = mask == BC_MASK_BLOCK_CAUSAL;
   args->n_splits = p.P;

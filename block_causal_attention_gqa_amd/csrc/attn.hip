@@ -864,9 +864,10 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 
 // ====================================================== fork, direct form
 // Shared-prefix fork with every row tile on one CU (N rollouts, 2 N Hkv row
-// tiles >= the CUs): row tile (kv head g, rollout s, half h) holds half of
-// rollout s's R x group query rows of kv head g (at most 96), and its
-// workgroup covers ALL the keys those rows see, in two key halves:
+// tiles >= the CUs), over all the keys its rows see, with no split partials
+// and no combine.  Row tile (kv head g, rollout s, half h) holds half of
+// rollout s's R x group query rows of kv head g: at most 96.  The
+// workgroup covers the rows' keys in two halves:
 //   kh = 0: the shared prefix's keys [0, X), then the rollout's private keys;
 //   kh = 1: the shared prefix's keys [X, L), then the active keys (the only
 //           segment the block predicate applies to),
@@ -876,26 +877,26 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 // hide each other's latencies.  Each half streams its keys through a
 // two-stage K/V ring of its own, loaded by its first four waves.  At the end
 // half 1 hands (o, m, l) to half 0 through LDS, which merges them and writes
-// the normalised output: no split partials, no combine, every CU the same
-// work.  The price is one K and one V operand read per 16 rows instead of
-// per 32 (two column tiles per wave leave 6 waves, which sit unevenly on the
-// 4 SIMDs: measured slower, 67.7 against 61.5 us).
+// the normalised output: every CU the same work.  The price is one K and one
+// V operand read per 16 rows instead of per 32 (two column tiles per wave
+// leave 6 waves, which sit unevenly on the 4 SIMDs: measured slower, 67.7
+// against 61.5 us).
 // LDS (given at launch): per half K(0), K(1), V(0), V(1) (64 KB), then the
 // Q tile of the 96 rows (24 KB).
+constexpr int kForkRG = kForkTileRows / 16;   // 6 row groups per key half
 constexpr unsigned kForkLdsBytes = 2u * 4 * kAttnKeyTile * 128 * 2 + kForkTileRows * 128 * 2;
-constexpr int kForkWaves = 2 * kForkTileRows / 16;   // 12: three per SIMD
 
 template <int D>
-__global__ __launch_bounds__(kForkWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(2 * kForkRG * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_fork_direct_kernel(const AttnArgs a) {
+  constexpr int RG = kForkRG;
   constexpr int CT = 1;                // one 16-row column tile per wave
   constexpr int KT = kAttnKeyTile;
   constexpr int RB = D * 2;            // bytes per key row
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int TB = KT * RB;          // bytes per tile and tensor
   constexpr int RPL = 1024 / RB;       // key rows per wave-wide 16-byte load
-  constexpr int RG = kForkTileRows / (16 * CT);   // row groups (waves) per key half
-  constexpr int WR = 16 * CT;          // rows per wave
+  constexpr int WR = 16;               // rows per wave
   constexpr int LW = 4;                // loading waves per half
   static_assert(TB % (LW * 1024) == 0 && LW <= RG, "a tile must split evenly over the loading waves");
   constexpr int LPW = TB / (LW * 1024);
@@ -1536,8 +1537,8 @@ inline int partial_grid(const AttnArgs& a) {
 template <int D, bool kDyn>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
   if constexpr (D == 128 && !kDyn) {
-    if (a.fork_direct) {
-      hipLaunchKernelGGL((attn_fork_direct_kernel<128>), dim3(a.S * a.Hkv * 2), dim3(kForkWaves * 64), kForkLdsBytes,
+    if (a.direct) {
+      hipLaunchKernelGGL((attn_fork_direct_kernel<128>), dim3(a.S * a.Hkv * 2), dim3(2 * kForkRG * 64), kForkLdsBytes,
                          stream, a);
       return hipGetLastError();
     }
@@ -1611,7 +1612,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, int dtype, hipStream_t stream)
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, int dtype, hipStream_t stream) {
-  if (a.fork_direct) return hipSuccess;   // the partial pass wrote the output
+  if (a.direct) return hipSuccess;   // the partial pass wrote the output
   if (dtype == BC_BF16)
     return a.D == 128 ? launch_combine_typed<bf16_t, 128>(a, stream) : launch_combine_typed<bf16_t, 64>(a, stream);
   return a.D == 128 ? launch_combine_typed<float, 128>(a, stream) : launch_combine_typed<float, 64>(a, stream);

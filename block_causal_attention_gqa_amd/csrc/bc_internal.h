@@ -97,10 +97,10 @@ struct AttnArgs {
   // R stays the widest step's row count; a step with no active block does
   // nothing.
   const DevPlan* dyn;
-  // 1: shared-prefix fork in the direct form (one 12-wave workgroup per row
-  // tile of half a rollout's rows over all their keys, output written by the
-  // partial pass; the combine does nothing)
-  int fork_direct;
+  // 1: the fork's direct form (one workgroup per half of a rollout's rows
+  // over all their keys, output written by the partial pass; the combine
+  // does nothing)
+  int direct;
 };
 
 // Kernel arguments of a block-bidirectional attention call without a fork,
