@@ -39,11 +39,12 @@ int check_blk_off(const int32_t* off, int n_blk, int n_rows, int max_rows_per_bl
 
 // ------------------------------------------------------------ attention plan
 struct Plan {
-  int waves, cols, direct, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
+  int waves, cols, fork_rows, direct, P, n_mt_prefix, n_mt_active, n_prefix_items, n_items, rows_total, n_slots;
   int xmap, tile_rows, unit_tiles, n_units, units_per_xcd;
   bool compact;        // compact split partials (bf16 inputs, many rows)
   bool fold;           // active keys in the last prefix chunk's items (no slot P)
-  size_t o_bytes, ml_bytes, total_bytes;
+  size_t o_bytes, ml_bytes, total_bytes;   // what this call's plan writes
+  size_t reserve_bytes;   // what bc_attn_workspace_bytes reports: at least total_bytes
 };
 
 int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_active* a,
@@ -207,19 +208,45 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   p->o_bytes = align256((size_t)(P + 1) * p->rows_total * D * (compact ? 2 : 4));
   p->ml_bytes = align256((size_t)(P + 1) * p->rows_total * (compact ? 16 : 8));
   p->total_bytes = p->o_bytes + p->ml_bytes;
-  // Direct form (shared-prefix fork): when half of a rollout's rows per KV
-  // head fill more than half of one 96-row tile (bf16, head_dim 128) and the
-  // 2 N Hkv row tiles give every CU at least one, each tile's workgroup
-  // covers all the keys its rows see and writes the output (no split
-  // partials, no combine).  Emptier tiles would pay a full tile's MFMAs for
-  // a few rows.  The workspace size stays the split plan's, which a
-  // workspace sized for these shapes holds anyway.  (Without a fork the same
-  // form, 64-row tiles of half a sequence's rows, measured no better on the
-  // large-block batch 16 call: 33.4 -> 32.7 us back to back, 39.8 -> 41.9 us
-  // after a clean flush.)
+  p->reserve_bytes = p->total_bytes;
+  p->fork_rows = 0;
+  p->direct = 0;
+  // Fork, row-tile form: when half of a rollout's rows per KV head fill more
+  // than half of one 96-row tile (bf16, head_dim 128), each (KV head,
+  // rollout, half) row tile takes P_r key splits, as many as give every CU
+  // one workgroup (2 N Hkv P_r >= 256) while each split keeps at least 12
+  // key tiles; a workgroup covers its split's prefix chunk -- the last also the
+  // rollout's private keys and the active keys, so there is no slot for
+  // them -- in two key halves merged in LDS (attn_fork_rows_kernel).  With
+  // P_r = 1 (N >= 128 / Hkv) it writes the output itself and the combine
+  // does nothing.  Emptier tiles would pay a full tile's MFMAs for a few
+  // rows; fewer workgroups than CUs, or shorter splits (small N), keep the
+  // split plan (measured at N = 4: 16 splits of 3 tiles, 14.8 -> 16.2 us;
+  // N = 16, 4 splits of 13 tiles: 26.2 -> 25.2 us; N = 64, one split: 63 ->
+  // 58 us, draft passes over a 3282-key prefix).  The
+  // workspace size reported is the larger of the two plans', so that a
+  // workspace sized at capacity serves every call with these shapes.
+  // (Without a fork the same form, 64-row tiles of half a sequence's rows,
+  // measured no better on the large-block batch 16 call: 33.4 -> 32.7 us
+  // back to back, 39.8 -> 41.9 us after a clean flush.)
   const int half_rows = (R * group + 1) / 2;
-  p->direct = fork && prefix->dtype == BC_BF16 && D == 128 && n_splits == 0 && (long long)S * Hkv * 2 >= 256 &&
-              half_rows <= kForkTileRows && 2 * half_rows > kForkTileRows;
+  if (fork && prefix->dtype == BC_BF16 && D == 128 && n_splits == 0 && half_rows <= kForkTileRows &&
+      2 * half_rows > kForkTileRows) {
+    const int tiles = S * Hkv * 2;
+    const int Pr = std::max(1, std::min(256 / tiles, maxlen / (12 * kAttnKeyTile)));
+    if ((long long)tiles * Pr >= 256) {
+      p->fork_rows = 1;
+      p->direct = Pr == 1;
+      p->P = Pr;
+      p->n_slots = Pr;
+      const int per = (maxlen + Pr - 1) / Pr;
+      chunk[0] = std::max(kAttnKeyTile, (per + kAttnKeyTile - 1) / kAttnKeyTile * kAttnKeyTile);
+      p->o_bytes = align256((size_t)Pr * p->rows_total * D * (compact ? 2 : 4));
+      p->ml_bytes = align256((size_t)Pr * p->rows_total * (compact ? 16 : 8));
+      p->total_bytes = p->o_bytes + p->ml_bytes;
+      p->reserve_bytes = std::max(p->reserve_bytes, p->total_bytes);
+    }
+  }
 }
 
 }  // namespace
@@ -277,7 +304,7 @@ size_t bc_attn_workspace_bytes(const bc_kv_cache* prefix, const bc_kv_cache* pri
   Plan p;
   int chunk[BC_MAX_SEQ];
   make_plan(prefix, priv, a, caps, n_prefix_splits, &p, chunk);
-  return p.total_bytes;
+  return p.reserve_bytes;
 }
 
 }  // extern "C"
@@ -351,6 +378,7 @@ int prepare_attn(const bc_kv_cache* prefix, const int32_t* prefix_len, const bc_
   args->D = D;
   args->waves = p.waves;
   args->cols = p.cols;
+  args->fork_rows = p.fork_rows;
   args->direct = p.direct;
   args->fork = priv ? 1 : 0;
   args->causal = mask == BC_MASK_BLOCK_CAUSAL;

@@ -451,7 +451,7 @@ __device__ inline u32x4 raw_buffer(const void* base, int bytes) {
 
 __device__ inline uint32_t lds_addr(const BC_LDS uint8_t* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
 
-// LDS given at launch (the fork's direct form)
+// LDS given at launch (the fork's row-tile form)
 extern __shared__ __attribute__((aligned(16))) uint8_t bc_dyn_lds[];
 
 __device__ inline uint32_t lds_offset(const void* p) {
@@ -862,25 +862,27 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
   else write_partial_f32<D, CT, false>(a, it.slot, valid, orow, m_run, l_run, o, jj);
 }
 
-// ====================================================== fork, direct form
-// Shared-prefix fork with every row tile on one CU (N rollouts, 2 N Hkv row
-// tiles >= the CUs), over all the keys its rows see, with no split partials
-// and no combine.  Row tile (kv head g, rollout s, half h) holds half of
-// rollout s's R x group query rows of kv head g: at most 96.  The
-// workgroup covers the rows' keys in two halves:
-//   kh = 0: the shared prefix's keys [0, X), then the rollout's private keys;
-//   kh = 1: the shared prefix's keys [X, L), then the active keys (the only
-//           segment the block predicate applies to),
-// with X cut so that both halves run the same number of 64-key tiles (the
-// shorter runs one empty tile at most).  Wave 6 kh + rg holds row group rg
-// (16 rows, one column tile) of key half kh: 12 waves, three per SIMD, which
-// hide each other's latencies.  Each half streams its keys through a
-// two-stage K/V ring of its own, loaded by its first four waves.  At the end
-// half 1 hands (o, m, l) to half 0 through LDS, which merges them and writes
-// the normalised output: every CU the same work.  The price is one K and one
-// V operand read per 16 rows instead of per 32 (two column tiles per wave
-// leave 6 waves, which sit unevenly on the 4 SIMDs: measured slower, 67.7
-// against 61.5 us).
+// ==================================================== fork, row-tile form
+// Shared-prefix fork with every CU the same work: row tile (kv head g,
+// rollout s, half h) holds half of rollout s's R x group query rows of kv
+// head g (at most 96), and P key splits of it make the workgroups (2 N Hkv
+// P >= the CUs; P = 1 at N = 64, 4 at N = 16).  Split q covers the shared
+// prefix's chunk [q C, (q + 1) C); the last split also the rollout's private
+// keys and the active keys.  The workgroup covers its split's keys in two
+// halves:
+//   kh = 0: the first part of the chunk, then (last split) the private keys;
+//   kh = 1: the rest of the chunk, then (last split) the active keys (the
+//           only segment the block predicate applies to),
+// cut so that both halves run the same number of 64-key tiles (the shorter
+// runs one empty tile at most).  Wave 6 kh + rg holds row group rg (16 rows,
+// one column tile) of key half kh: 12 waves, three per SIMD, which hide each
+// other's latencies.  Each half streams its keys through a two-stage K/V ring
+// of its own, loaded by its first four waves.  At the end half 1 hands (o,
+// m, l) to half 0 through LDS, which merges them and writes, with one split,
+// the normalised output (no split partials, no combine) and otherwise the
+// split's record for the combine.  The price is one K and one V operand read
+// per 16 rows instead of per 32 (two column tiles per wave leave 6 waves,
+// which sit unevenly on the 4 SIMDs: measured slower, 67.7 against 61.5 us).
 // LDS (given at launch): per half K(0), K(1), V(0), V(1) (64 KB), then the
 // Q tile of the 96 rows (24 KB).
 constexpr int kForkRG = kForkTileRows / 16;   // 6 row groups per key half
@@ -888,7 +890,7 @@ constexpr unsigned kForkLdsBytes = 2u * 4 * kAttnKeyTile * 128 * 2 + kForkTileRo
 
 template <int D>
 __global__ __launch_bounds__(2 * kForkRG * 64) __attribute__((amdgpu_waves_per_eu(3)))
-void attn_fork_direct_kernel(const AttnArgs a) {
+void attn_fork_rows_kernel(const AttnArgs a) {
   constexpr int RG = kForkRG;
   constexpr int CT = 1;                // one 16-row column tile per wave
   constexpr int KT = kAttnKeyTile;
@@ -916,10 +918,15 @@ void attn_fork_direct_kernel(const AttnArgs a) {
   // row tile: consecutive tiles (one kv head's) share an XCD and its L2.
   // (Integer division runs on the vector unit; readfirstlane keeps these
   // workgroup-uniform values, and the pointers made from them, in SGPRs.)
-  const int n_tiles = a.S * a.Hkv * 2;
-  const int tile = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, n_tiles));
-  const int g = __builtin_amdgcn_readfirstlane(tile / (a.S * 2));
-  const int s = (tile - g * a.S * 2) >> 1, hf = tile & 1;
+  // workgroup: (kv head g, key split q, rollout s, half hf), in that order
+  // of significance, so that consecutive ones -- the row tiles streaming one
+  // prefix chunk -- share an XCD and its L2
+  const int per_g = a.n_splits * a.S * 2;
+  const int id = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.Hkv * per_g));
+  const int g = __builtin_amdgcn_readfirstlane(id / per_g);
+  const int q = __builtin_amdgcn_readfirstlane((id - g * per_g) / (a.S * 2));
+  const int tile = id - g * per_g - q * a.S * 2;
+  const int s = tile >> 1, hf = tile & 1;
   const int rows_r = a.R * a.group;
   const int half = (rows_r + 1) >> 1;
   const int rows_here = hf == 0 ? half : rows_r - half;
@@ -948,14 +955,20 @@ void attn_fork_direct_kernel(const AttnArgs a) {
     lim[c] = l;
   }
 
-  // the two halves' key segments; both run nt tiles
-  const int L = a.prefix_len[0], lv = a.priv_len[s];
-  const int TL = (L + KT - 1) / KT, tv = (lv + KT - 1) / KT, tr = (a.R + KT - 1) / KT;
+  // split q's keys: the prefix chunk [q C, min(L, (q + 1) C)), and in the
+  // last split also the rollout's private keys and the active keys; the two
+  // halves' segments, both run nt tiles
+  const int L = a.prefix_len[0], C = a.chunk[0];
+  const int k0 = min(L, q * C);
+  const int nc = min(L, k0 + C) - k0;
+  const bool last = q == a.n_splits - 1;
+  const int lv = last ? a.priv_len[s] : 0, ra = last ? a.R : 0;
+  const int TL = (nc + KT - 1) / KT, tv = (lv + KT - 1) / KT, tr = (ra + KT - 1) / KT;
   const int cut = __builtin_amdgcn_readfirstlane(max(0, min(TL, (TL + tr - tv) / 2)));
-  const int X = min(cut * KT, L);
+  const int X = min(cut * KT, nc);
   const int nt = __builtin_amdgcn_readfirstlane(max(cut + tv, TL - cut + tr));
-  const bf16_t* pk = static_cast<const bf16_t*>(a.pk) + g * a.p_head_stride;
-  const bf16_t* pv = static_cast<const bf16_t*>(a.pv) + g * a.p_head_stride;
+  const bf16_t* pk = static_cast<const bf16_t*>(a.pk) + g * a.p_head_stride + (long long)k0 * D;
+  const bf16_t* pv = static_cast<const bf16_t*>(a.pv) + g * a.p_head_stride + (long long)k0 * D;
   const bf16_t *ka, *va, *kb_, *vb_;
   int na, nb;
   if (kh == 0) {
@@ -969,11 +982,11 @@ void attn_fork_direct_kernel(const AttnArgs a) {
   } else {
     ka = pk + (long long)X * D;
     va = pv + (long long)X * D;
-    na = L - X;
+    na = nc - X;
     const long long ao = (long long)(s * a.Hkv + g) * a.R * D;
     kb_ = static_cast<const bf16_t*>(a.ak) + ao;
     vb_ = static_cast<const bf16_t*>(a.av) + ao;
-    nb = a.R;
+    nb = ra;
   }
   const int nta = (na + KT - 1) / KT, ntb = (nb + KT - 1) / KT;
   const bool mskb = kh == 1;
@@ -1238,22 +1251,33 @@ void attn_fork_direct_kernel(const AttnArgs a) {
   }
   lds_barrier();
   if (kh == 1) return;
-  bf16_t* out = static_cast<bf16_t*>(a.out);
+  // merge half 1's (o, m, l) into half 0's
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    if (!valid[c]) continue;
     const BC_LDS uint8_t* pc = pub + c * ((D / 16) * 1024 + 512);
     const float m1 = *(const BC_LDS float*)(pc + (D / 16) * 1024 + lane * 4);
     const float l1 = *(const BC_LDS float*)(pc + (D / 16) * 1024 + 256 + lane * 4);
     const float m = fmaxf(m_run[c], m1);
-    float l = l_run[c];
     if (m != kNegInf) {
       const float a0 = __builtin_amdgcn_exp2f(m_run[c] - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[c][dt] = o[c][dt] * a0 + *(const BC_LDS f32x4*)(pc + dt * 1024 + lane * 16) * a1;
-      l = l * a0 + l1 * a1;
+      l_run[c] = l_run[c] * a0 + l1 * a1;
+      m_run[c] = m;
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  }
+  if (!a.direct) {
+    // one of several key splits: the split record for the combine
+    if (a.compact) write_partial_q16<D, CT>(a, q, valid, orow, m_run, l_run, o, jj);
+    else write_partial_f32<D, CT, false>(a, q, valid, orow, m_run, l_run, o, jj);
+    return;
+  }
+  // the only split: the normalised output
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    if (!valid[c]) continue;
+    const float inv = l_run[c] > 0.f ? 1.f / l_run[c] : 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const f32x4 x = o[c][dt] * inv;
@@ -1537,9 +1561,9 @@ inline int partial_grid(const AttnArgs& a) {
 template <int D, bool kDyn>
 hipError_t launch_partial_bf16(const AttnArgs& a, hipStream_t stream) {
   if constexpr (D == 128 && !kDyn) {
-    if (a.direct) {
-      hipLaunchKernelGGL((attn_fork_direct_kernel<128>), dim3(a.S * a.Hkv * 2), dim3(2 * kForkRG * 64), kForkLdsBytes,
-                         stream, a);
+    if (a.fork_rows) {
+      hipLaunchKernelGGL((attn_fork_rows_kernel<128>), dim3(a.S * a.Hkv * 2 * a.n_splits), dim3(2 * kForkRG * 64),
+                         kForkLdsBytes, stream, a);
       return hipGetLastError();
     }
   }

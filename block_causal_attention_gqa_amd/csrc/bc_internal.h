@@ -32,7 +32,7 @@ __device__ inline int fast_div(int n, FastDiv f) {
 // ---------------------------------------------------------------- attention
 constexpr int kAttnKeyTile = 64;          // keys staged through LDS per iteration
 constexpr int kCompactRows = 1024;        // bf16 calls with at least this many output rows use compact partials
-constexpr int kForkTileRows = 96;         // rows per row tile of the fork's direct form (half a rollout's rows)
+constexpr int kForkTileRows = 96;         // rows per row tile of the fork's row-tile form (half a rollout's rows)
 
 // The next step of a device-resident pipelined decode (bc_dev_plan, see
 // include/bc.h), written by the schedule kernel and read by the step's kernels.
@@ -97,9 +97,11 @@ struct AttnArgs {
   // R stays the widest step's row count; a step with no active block does
   // nothing.
   const DevPlan* dyn;
-  // 1: the fork's direct form (one workgroup per half of a rollout's rows
-  // over all their keys, output written by the partial pass; the combine
-  // does nothing)
+  // 1: the fork's row-tile form (one workgroup per half of a rollout's rows
+  // and key split, attn_fork_rows_kernel)
+  int fork_rows;
+  // 1: the partial pass writes the output itself (a row-tile form with one
+  // key split); the combine does nothing
   int direct;
 };
 

@@ -263,11 +263,12 @@ int bc_spec_verify_sampled(const float *logits, const float *noise, float inv_te
  *   (float32; for bf16 inputs with n_seq * n_rows * n_q_heads >= 1024, int16
  *   against a power of two per row and split, within 2^-14 of the row's
  *   largest element); the combine pass merges them with log-sum-exp weights
- *   into `out`.  Shared-prefix fork calls in the direct form have no split
- *   partials: their partial pass writes `out` itself and their combine pass
- *   does nothing.  Those are the bf16, head_dim 128 fork calls with
- *   n_prefix_splits = 0, 2 * n_seq * n_kv_heads >= 256 and 97 to 192 rows
- *   per rollout and KV head (n_rows * n_q_heads / n_kv_heads).
+ *   into `out`.  Shared-prefix fork calls with a single key split in the
+ *   row-tile form have no split partials: their partial pass writes `out`
+ *   itself and their combine pass does nothing.  Those are the bf16,
+ *   head_dim 128 fork calls with n_prefix_splits = 0,
+ *   2 * n_seq * n_kv_heads >= 256 and 97 to 192 rows per rollout and KV
+ *   head (n_rows * n_q_heads / n_kv_heads).
  *
  * bc_unmask_select(args) == bc_vocab_scan(logits, n_rows, vocab, masked, 1,
  *   ws, ws_bytes, stream); bc_unmask_decide(args).

@@ -257,11 +257,22 @@ def test_fork_sixtyfour_short_prefixes_odd_rows(mode, prefix):
            cap=max(prefix, 1))
 
 
-def test_fork_sixtyfour_partial_then_combine_equals_step():
-    # the partial pass writes the output itself; the combine then does nothing
+@pytest.mark.parametrize("N,mode", [(16, BIDIR), (32, CAUSAL)])
+def test_fork_row_tiles_with_key_splits(N, mode):
+    # N = 16 / 32 rollouts over the full 3282-key prefix: 4 / 2 key splits
+    # per row tile (one workgroup per CU), split records merged by the
+    # combine; two blocks inside the active rows, private lengths 0 .. 47
+    priv = [(7 * s + 3) % 48 for s in range(N)]
+    _check(98 + N, N, 24, 16, 2, 128, "bf16", [3282], [0, 10, 24], mode, fork=True, priv_len=priv, priv_cap=48)
+
+
+@pytest.mark.parametrize("N", [16, 64])
+def test_fork_row_tiles_partial_then_combine_equals_step(N):
+    # N = 64: the partial pass writes the output itself and the combine does
+    # nothing; N = 16: split records, merged by the combine
     import torch
     from block_causal_attention_gqa_amd import synth
-    seed, N, R, Hq, Hkv, D = 96, 64, 24, 16, 2, 128
+    seed, R, Hq, Hkv, D = 96, 24, 16, 2, 128
     (pk, pv), _ = synth.kv_cache(seed, 1, Hkv, 3282, D, [3282], "bf16")
     priv_len = [(5 * s) % 48 for s in range(N)]
     (vk, vv), _ = synth.kv_cache(seed, N, Hkv, 48, D, priv_len, "bf16", purpose=("priv_k", "priv_v"))
