@@ -191,12 +191,12 @@ def test_partial_record_sizes_follow_the_row_count(L):
         assert nbytes(dtype, R) == rounded(3 * rows * per_row[0]) + rounded(3 * rows * per_row[1]), (dtype, R)
 
 
-def test_fork_direct_form_keeps_the_split_plans_workspace(L):
+def test_fork_row_tile_form_keeps_the_split_plans_workspace(L):
     # N = 64 rollouts over a 3282-key shared prefix (24 rows x 16 heads per
-    # rollout, 2 KV heads): the automatic plan is the direct form, which
-    # writes no split partials, yet reports the split plan's size (P = 2
-    # prefix splits + the active slot, compact records), so that a workspace
-    # sized for the shapes also serves calls that split
+    # rollout, 2 KV heads): the automatic plan is the row-tile form with one
+    # key split, which writes no split partials, yet reports the split
+    # plan's size (P = 2 prefix splits + the active slot, compact records),
+    # so that a workspace sized for the shapes also serves calls that split
     act, keep = _active(S=64, R=24, Hq=16, off=(0, 24))
     shared, priv = _cache(S=1, cap=3282), _cache(S=64, cap=48)
     auto = L.bc_attn_workspace_bytes(ctypes.byref(shared), ctypes.byref(priv), ctypes.byref(act), 0)
