@@ -915,12 +915,11 @@ void attn_fork_rows_kernel(const AttnArgs a) {
   const int kh = w / RG, rg = w - kh * RG;
   const int n = lane & 15, jj = lane >> 4;
 
-  // row tile: consecutive tiles (one kv head's) share an XCD and its L2.
-  // (Integer division runs on the vector unit; readfirstlane keeps these
-  // workgroup-uniform values, and the pointers made from them, in SGPRs.)
   // workgroup: (kv head g, key split q, rollout s, half hf), in that order
   // of significance, so that consecutive ones -- the row tiles streaming one
-  // prefix chunk -- share an XCD and its L2
+  // prefix chunk -- share an XCD and its L2.  (Integer division runs on the
+  // vector unit; readfirstlane keeps these workgroup-uniform values, and the
+  // pointers made from them, in SGPRs.)
   const int per_g = a.n_splits * a.S * 2;
   const int id = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, a.Hkv * per_g));
   const int g = __builtin_amdgcn_readfirstlane(id / per_g);
