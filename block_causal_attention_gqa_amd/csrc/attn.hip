@@ -877,7 +877,7 @@ void attn_partial_bf16_kernel(const AttnArgs a) {
 // runs one empty tile at most).  Wave 6 kh + rg holds row group rg (16 rows,
 // one column tile) of key half kh: 12 waves, three per SIMD, which hide each
 // other's latencies.  Each half streams its keys through a two-stage K/V ring
-// of its own, loaded by its first four waves.  At the end half 1 hands (o,
+// of its own, loaded by its first two waves.  At the end half 1 hands (o,
 // m, l) to half 0 through LDS, which merges them and writes, with one split,
 // the normalised output (no split partials, no combine) and otherwise the
 // split's record for the combine.  The price is one K and one V operand read
@@ -899,7 +899,10 @@ void attn_fork_rows_kernel(const AttnArgs a) {
   constexpr int TB = KT * RB;          // bytes per tile and tensor
   constexpr int RPL = 1024 / RB;       // key rows per wave-wide 16-byte load
   constexpr int WR = 16;               // rows per wave
-  constexpr int LW = 4;                // loading waves per half
+  // loading waves per half: two, one per SIMD across both halves (measured
+  // at N = 64, draft / verify pass: four 59.5 / 57.3 us, two 57.0 / 54.4 us,
+  // one 64.1 / 60.0 us)
+  constexpr int LW = 2;
   static_assert(TB % (LW * 1024) == 0 && LW <= RG, "a tile must split evenly over the loading waves");
   constexpr int LPW = TB / (LW * 1024);
   constexpr int QLPW = WR * RB / 1024;  // Q loads per wave (its rows)
