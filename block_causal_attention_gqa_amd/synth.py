@@ -22,7 +22,7 @@ _TAGS = {
     "prefix_k": 1, "prefix_v": 2, "q": 3, "k": 4, "v": 5, "logits": 6,
     "priv_k": 7, "priv_v": 8, "draft": 9, "peak": 10, "ratio": 11,
     "subset": 12, "commit_k": 13, "commit_v": 14, "misc": 15, "gumbel": 16,
-    "layout": 17, "scaffold": 18,
+    "layout": 17, "scaffold": 18, "score_dir": 19,
 }
 
 

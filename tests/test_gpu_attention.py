@@ -442,3 +442,91 @@ def test_fork_head_dim_64(mode):
     # 24 rows x 8 heads per KV head
     priv = [(13 * s) % 48 for s in range(16)]
     _check(114, 16, 24, 16, 2, 64, "bf16", [1500], [0, 24], mode, fork=True, priv_len=priv, priv_cap=48)
+
+
+# ---- a running maximum that jumps: the online softmax's rescale.  With N(0,1)
+# inputs a row's scaled scores stay within a few units, so after the first key
+# tile no tile raises the running maximum by more than the rescale slack (8 in
+# log2 units, 8 ln 2 = 5.5 in natural units) and the rescale of a non-empty
+# accumulator never runs.  Here chosen key ranges get raised scores
+# (G.biased_keys), so that a row's maximum climbs by 8-20 units several times:
+# inside a chunk, across split chunks (the combine), across the fork's key
+# halves (the merge in LDS), and between prefix, private and active keys.
+
+SLACK_NAT = 8 * np.log(2.0)
+
+
+def _steps(levels, width):
+    lv = np.asarray(levels, np.float64)
+    return lambda j: lv[np.minimum(np.asarray(j) // width, len(lv) - 1)]
+
+
+def _const(c):
+    return lambda j: np.full(len(j), float(c))
+
+
+PREFIX_JUMPS = _steps([0, 4, 12, 20, 8, 16], 512)
+
+
+def _check_biased(seed, S, R, Hq, Hkv, D, dtype, prefix_len, blk_off, mode, bias, **kw):
+    print("attn biased case seed=%d S=%d R=%d Hq=%d Hkv=%d D=%d %s prefix=%s blk=%s mode=%d %s"
+          % (seed, S, R, Hq, Hkv, D, dtype, list(prefix_len)[:4], list(blk_off)[:6], mode, kw), flush=True)
+    got, h = G.attn_case(seed, S, R, Hq, Hkv, D, dtype, prefix_len, blk_off, mode, key_bias=bias, **kw)
+    fork = kw.get("fork", False)
+    want = OA.attention_step(h["q"], h["pk"], h["pv"], prefix_len, h["k"], h["v"], blk_off, mode,
+                             scale=h["scale"], priv_k=h["vk"] if fork else None,
+                             priv_v=h["vv"] if fork else None,
+                             priv_len=kw.get("priv_len") if fork else None)
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], "max-abs %.3g > %.3g" % (err, TOL[dtype])
+    # the inputs do what they are for: over the first sequence's prefix, the
+    # first row's running maximum (moved only past the slack, as the kernels
+    # move theirs) is raised by a 64-key tile at least twice
+    sc = h["pk"][0, 0, :prefix_len[0]].astype(np.float64) @ h["q"][0, 0, 0].astype(np.float64) * h["scale"]
+    tiles = [sc[i:i + 64].max() for i in range(0, len(sc), 64)]
+    m, moves = tiles[0], 0
+    for t in tiles[1:]:
+        if t > m + SLACK_NAT:
+            m, moves = t, moves + 1
+    assert moves >= 2, "the running maximum moved %d times" % moves
+
+
+@pytest.mark.parametrize("splits", [0, 1, 4])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_running_max_jumps_section_shape(mode, splits):
+    # bs1 section shape; splits 0: the automatic split (about 25 chunks of two
+    # tiles, float32 records); 1: one chunk over the whole prefix
+    bias = dict(prefix=PREFIX_JUMPS, active=_const(22.0))
+    _check_biased(90 + splits, 1, 32, 16, 2, 128, "bf16", [3072], [0, 12, 32], mode, bias, cap=3352,
+                  n_splits=splits)
+
+
+def test_running_max_jumps_many_rows_head_dim_64():
+    # 2048 rows per group: 128-row tiles of two column tiles, compact records
+    bias = dict(prefix=_steps([0, 9, 18], 320), active=lambda j: 14.0 + 0.02 * np.asarray(j))
+    _check_biased(98, 1, 512, 16, 4, 64, "bf16", [1000], [0, 100, 256, 300, 512], CAUSAL, bias)
+
+
+def test_running_max_jumps_batch16_folded():
+    # the large-block batch-16 shape: ragged prefixes, active keys folded into
+    # the last chunk, XCD-aligned mapping
+    lens = [2176 - 37 * s for s in range(16)]
+    bias = dict(prefix=_steps([0, 10, 2, 20], 512), active=_const(21.0))
+    _check_biased(99, 16, 32, 32, 8, 128, "bf16", lens, [0, 32], BIDIR, bias, cap=2176)
+
+
+@pytest.mark.parametrize("N", [4, 16, 64])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_running_max_jumps_fork(N, mode):
+    # N = 4: split plan; 16: row-tile form with key splits; 64: row-tile form,
+    # one split, the two key halves merged in LDS
+    priv = [(13 * s + 5) % 48 for s in range(N)]
+    bias = dict(prefix=PREFIX_JUMPS, priv=_const(21.0), active=_const(22.0))
+    _check_biased(100 + N, N, 24, 16, 2, 128, "bf16", [3282], [0, 9, 24], mode, bias, fork=True,
+                  priv_len=priv, priv_cap=48)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_running_max_jumps_fp32(splits):
+    bias = dict(prefix=_steps([0, 9, 1, 18], 64), active=_const(16.0))
+    _check_biased(110 + splits, 1, 8, 4, 1, 64, "f32", [256], [0, 8], BIDIR, bias, n_splits=splits)
