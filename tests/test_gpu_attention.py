@@ -530,3 +530,49 @@ def test_running_max_jumps_fork(N, mode):
 def test_running_max_jumps_fp32(splits):
     bias = dict(prefix=_steps([0, 9, 1, 18], 64), active=_const(16.0))
     _check_biased(110 + splits, 1, 8, 4, 1, 64, "f32", [256], [0, 8], BIDIR, bias, n_splits=splits)
+
+
+# ---- query heads per KV head that are not powers of two (12q/2kv, 28q/4kv
+# and the like): the kernels split row indices by the group size through a
+# multiply-high (tests/test_fastdiv.py checks its constants on the CPU)
+
+
+@pytest.mark.parametrize("group", [3, 5, 6, 7, 12, 16])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_odd_group_sizes(group, mode):
+    _check(120 + group, 1, 20, 2 * group, 2, 128, "bf16", [777], [0, 7, 20], mode, cap=800)
+
+
+@pytest.mark.parametrize("group", [3, 7])
+def test_odd_group_sizes_two_column_tiles(group):
+    # 300 rows x group 7 = 2100 rows per group: 128-row tiles, compact records
+    _check(130 + group, 1, 300, 4 * group, 4, 64, "bf16", [500], [0, 100, 300], CAUSAL)
+
+
+@pytest.mark.parametrize("group", [5, 6, 7])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_odd_group_sizes_fork_row_tiles(group, mode):
+    # 64 rollouts: half of a rollout's 24 x group rows (60 / 72 / 84) fills one
+    # 96-row tile of the row-tile form, one key split
+    priv = [(5 * s) % 40 for s in range(64)]
+    _check(140 + group, 64, 24, 2 * group, 2, 128, "bf16", [1500], [0, 10, 24], mode, fork=True,
+           priv_len=priv, priv_cap=40)
+
+
+@pytest.mark.parametrize("N,group", [(16, 6), (16, 3), (4, 7)])
+def test_odd_group_sizes_fork(N, group):
+    # N = 16, group 6: row-tile form with key splits; group 3 and N = 4: split plan
+    priv = [(7 * s + 3) % 48 for s in range(N)]
+    _check(150 + N + group, N, 24, 2 * group, 2, 128, "bf16", [3282], [0, 24], CAUSAL, fork=True,
+           priv_len=priv, priv_cap=48)
+
+
+def test_odd_group_sizes_batch():
+    # 12 sequences x 28q/4kv, ragged prefixes
+    lens = [900 - 61 * s for s in range(12)]
+    _check(160, 12, 16, 28, 4, 128, "bf16", lens, [0, 5, 16], BIDIR, cap=900)
+
+
+@pytest.mark.parametrize("group", [3, 6])
+def test_odd_group_sizes_fp32(group):
+    _check(170 + group, 1, 8, group, 1, 64, "f32", [256], [0, 3, 8], CAUSAL)
