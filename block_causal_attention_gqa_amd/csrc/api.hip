@@ -85,7 +85,8 @@ int validate_attn(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_a
 // partial workgroups resident at once: two per CU on 256 CUs
 constexpr int kSlotsResident = 512;
 
-int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, double slot_row_bytes, bool wide) {
+int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, double slot_row_bytes, bool wide,
+                int max_splits = 256) {
   constexpr int kCUs = 256;
   constexpr double kTileUs1 = 1.9, kTileUs2 = 2.5, kItemUs = 2.0, kBytesPerUs = 5.0e6;
   // Slot traffic of two-column-tile calls (many rows, long items) is priced
@@ -96,7 +97,7 @@ int auto_splits(int row_tiles, int maxlen, double kv_bytes, int rows_total, doub
   // P ~ 25 is the measured optimum.
   const double slot_us = (double)rows_total * slot_row_bytes * 2.0 / (wide ? 2.0e6 : kBytesPerUs);
   const double floor_us = kv_bytes / kBytesPerUs + kItemUs;
-  const int most = std::max(1, std::min(256, (maxlen + kAttnKeyTile - 1) / kAttnKeyTile));
+  const int most = std::max(1, std::min(max_splits, (maxlen + kAttnKeyTile - 1) / kAttnKeyTile));
   int best = 1;
   double best_us = 1e300;
   for (int P = 1; P <= most; ++P) {
@@ -162,7 +163,22 @@ void make_plan(const bc_kv_cache* prefix, const bc_kv_cache* priv, const bc_acti
   const int tile_rows = p->waves * p->cols * 16;
   p->n_mt_prefix = (rows_group + tile_rows - 1) / tile_rows;
   p->n_mt_active = (R * group + tile_rows - 1) / tile_rows;
-  if (P == 0) P = auto_splits(groups * p->n_mt_prefix, maxlen, kv, S * R * Hq, slot_row_bytes, p->cols == 2);
+  if (P == 0) {
+    // Without a fork and with at most 8 row tiles, the XCD-aligned mapping
+    // (below) puts each row tile's P + 1 items on an XCD of its own.  Past
+    // its 32 CUs they double up, and for these latency-bound one-column-tile
+    // items a second workgroup on a CU costs more than the longer items of
+    // fewer splits (measured, bs1 section decode: 12 rows over 3072 keys 10.1
+    // us with the model's 48 one-tile splits against 8.5 us at 24-30 two-tile
+    // splits; 6 rows over 3276 / 3346 keys 9.3 against 8.2-8.4 us; the decode
+    // 1567 -> 1538 us), so the split count keeps them on a CU each.  (With
+    // more row tiles per XCD the model's trade stays: capping those measured
+    // slower.)
+    int max_splits = 256;
+    const int row_tiles = groups * p->n_mt_prefix;
+    if (!fork && p->cols == 1 && row_tiles <= 8) max_splits = 31;
+    P = auto_splits(row_tiles, maxlen, kv, S * R * Hq, slot_row_bytes, p->cols == 2, max_splits);
+  }
   p->P = P;
   p->n_prefix_items = groups * P * p->n_mt_prefix;
   const int n_active_items = S * Hkv * p->n_mt_active;

@@ -268,3 +268,28 @@ def test_device_pipeline_validation(L):
     assert L.bc_pipeline_dev_read_plan(None, None) == B.BC_ERR_ARG
     assert L.bc_pipeline_dev_rows(None) == B.BC_ERR_ARG
     assert L.bc_pipeline_dev_plan(None) is None
+
+
+def test_one_column_tile_splits_fit_each_xcd(L):
+    # bf16 calls without a fork and with at most 8 row tiles, whose items run
+    # under the XCD-aligned mapping (a row tile's P + 1 items on an XCD of its
+    # own, 32 CUs): the automatic split count keeps those items on a CU each,
+    # P + 1 <= 32.  Over the bs1 section
+    # decode's prefixes (3072-3346 keys) that is the two-tile split count
+    # ceil(L / 128), where items of one tile would need 48-53 splits.  Read
+    # back from the workspace size, which holds (P + 1) float32 records of 520
+    # bytes per output row (fewer than 1024 rows here), each array rounded up
+    # to 256 bytes.
+    def auto_p(R, cap, S=1, Hq=16, Hkv=2, per_row=520):
+        act, keep = _active(S=S, R=R, Hq=Hq, off=(0, R))
+        n = L.bc_attn_workspace_bytes(ctypes.byref(_cache(S=S, Hkv=Hkv, cap=cap)), None, ctypes.byref(act), 0)
+        return n // (S * R * Hq * per_row) - 1
+    for R in (6, 12, 32):           # 2, 4 and 8 row tiles of 64 rows: one per XCD at most
+        for cap in (3072, 3276, 3346):
+            assert auto_p(R, cap) == -(-cap // 128), (R, cap)
+        assert auto_p(R, 1000) + 1 <= 32
+    # more row tiles than XCDs keep the model's count: batch 16, 32q/8kv,
+    # 32-row blocks (256 row tiles) take 2 splits; 1-row blocks (128 row
+    # tiles of 4 rows) more than one
+    assert auto_p(32, 2176, S=16, Hq=32, Hkv=8, per_row=272) == 2
+    assert auto_p(1, 2176, S=16, Hq=32, Hkv=8) > 1
