@@ -182,6 +182,14 @@ class SectionDecode:
         """One whole decode.  Returns nothing; tokens / masked hold the result."""
         S = self.S
         length = self.len0.copy()
+        # every output row starts masked (scaffold rows revealed with their
+        # template tokens): one launch for the whole decode, before its first
+        # block; a block's rows are not touched before the block runs
+        if self.masked0 is None:
+            self.masked.fill_(1)
+        else:
+            self.masked.copy_(self.masked0)
+            self.tokens.copy_(self.tokens0)
         for u, blks in enumerate(self.units):
             ur = self.unit_rows[u]
             out = self.out[ur]
@@ -189,11 +197,6 @@ class SectionDecode:
                 bs, off = self.blocks[b], self.row0[b]
                 rows = slice(S * off, S * (off + bs))
                 masked, tokens = self.masked[rows], self.tokens[rows]
-                if self.masked0 is None:
-                    masked.fill_(1)
-                else:
-                    masked.copy_(self.masked0[rows])
-                    tokens.copy_(self.tokens0[rows])
                 blk_rows = list(range(0, S * bs + 1, bs))
                 for st in range(self.steps):
                     q, k, v = self.qkv[b][st]
