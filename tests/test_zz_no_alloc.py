@@ -41,6 +41,8 @@ CASES = [
     # (seed, S, R, Hq, Hkv, D, prefix lengths, blk_off, fork, priv_len, mask)
     (4, 64, 24, 16, 2, 128, [3282], [0, 9, 24], True, [(11 * s) % 48 for s in range(64)],
      B.BC_MASK_BLOCK_BIDIR),                                                          # fork, output written directly
+    (5, 16, 32, 32, 8, 128, [2176 - 37 * s for s in range(16)], [0, 32], False, None,
+     B.BC_MASK_BLOCK_BIDIR),                                                          # batch 16, folded, compact
     (1, 16, 24, 16, 2, 128, [3282], [0, 24], True, [24] * 16, B.BC_MASK_BLOCK_CAUSAL),  # fork, compact partials
     (2, 1, 32, 16, 2, 128, [3084], [0, 32], False, None, B.BC_MASK_BLOCK_BIDIR),         # bs1 section step
     (3, 1, 7, 16, 2, 64, [300], [0, 3, 7], False, None, B.BC_MASK_BLOCK_BIDIR),          # smaller, two blocks
